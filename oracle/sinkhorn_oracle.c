@@ -1,0 +1,265 @@
+/*
+ * fp64 CPU oracle for log-domain Sinkhorn.  TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg load
+ * this file's library.  The product path (the HIP library) never calls it and
+ * shares no code with it.  It is plain and slow on purpose: every step is the
+ * textbook definition, written out, in double precision, from the fp32 inputs
+ * upcast to double.
+ *
+ * Sources (page titles as printed on gist.science):
+ *  - "FlashSinkhorn: IO-Aware Entropic Optimal Transport on GPU",
+ *    technical summary, "Problemstellung" (EOT between weighted point clouds
+ *    solved by Sinkhorn iterations), "Methodik" intro (squared Euclidean cost)
+ *    and "Methodik" section 1 (the stabilised log-domain update: a potential
+ *    is minus eps times a log-sum-exp over the other side of
+ *    (other potential - cost)/eps; the other update is symmetric).
+ *    Section 2 of the same page states the log-sum-exp reductions are exact.
+ *  - The Birkhoff projection pages ("Aceleración de la Proyección de Birkhoff
+ *    para Hiper-conexiones ...", section 2 and its French twin): projecting a
+ *    4x4 matrix onto the doubly-stochastic matrices is entropic OT with unit
+ *    marginals, iterated by Sinkhorn-Knopp; section 2.1 subtracts the maximum
+ *    before exponentiating; section 1 names 20 fixed iterations.
+ *
+ * Convention (the pages put log b inside the log-sum-exp; here eps*log a sits
+ * outside it, which gives the same plan with f' = f + eps log a and
+ * g' = g + eps log b):
+ *
+ *   C_ij = sum_k (x_ik - y_jk)^2                          (direct difference)
+ *   f_i  <- eps*log a_i - eps*LSE_j((g_j - C_ij)/eps)
+ *   g_j  <- eps*log b_j - eps*LSE_i((f_i - C_ij)/eps)    (with the new f)
+ *   LSE(v) = M + log(sum exp(v - M)),  M = max v          (two passes)
+ *   P_ij = exp((f_i + g_j - C_ij)/eps)                     (never stored)
+ *
+ * One iteration is one f half-step followed by one g half-step.  f and g are
+ * in/out: the first half-step reads g.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static double sq_dist(const double *p, const double *q, int d)
+{
+    double c = 0.0;
+    for (int k = 0; k < d; ++k) {
+        double t = p[k] - q[k];
+        c += t * t;
+    }
+    return c;
+}
+
+/*
+ * One half-step for the side whose points are P (np x d, weights w):
+ *   out_i = eps*log w_i - eps*LSE_j((other_j - C(P_i, Q_j))/eps)
+ * over all nq points Q_j with potentials other_j.  rows == NULL updates every
+ * i in [0, np) and writes out[i]; otherwise it updates rows[r] for
+ * r in [0, nrows) and writes out[r].
+ */
+void oracle_half_update(const double *P, const double *Q, const double *w,
+                        const double *other, int64_t np, int64_t nq, int d,
+                        double eps, const int64_t *rows, int64_t nrows,
+                        double *out)
+{
+    int64_t count = rows ? nrows : np;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < count; ++r) {
+        int64_t i = rows ? rows[r] : r;
+        const double *pi = P + i * (int64_t)d;
+        double mx = -INFINITY;
+        for (int64_t j = 0; j < nq; ++j) {
+            double v = (other[j] - sq_dist(pi, Q + j * (int64_t)d, d)) / eps;
+            if (v > mx)
+                mx = v;
+        }
+        double s = 0.0;
+        for (int64_t j = 0; j < nq; ++j) {
+            double v = (other[j] - sq_dist(pi, Q + j * (int64_t)d, d)) / eps;
+            s += exp(v - mx);
+        }
+        out[r] = eps * log(w[i]) - eps * (mx + log(s));
+    }
+}
+
+/*
+ * iters alternating iterations at one eps, in place on f (n) and g (m).
+ */
+void oracle_sinkhorn(const double *x, const double *y, const double *a,
+                     const double *b, int64_t n, int64_t m, int d, double eps,
+                     int iters, double *f, double *g)
+{
+    for (int k = 0; k < iters; ++k) {
+        oracle_half_update(x, y, a, g, n, m, d, eps, NULL, 0, f);
+        oracle_half_update(y, x, b, f, m, n, d, eps, NULL, 0, g);
+    }
+}
+
+/*
+ * Statistics of the plan P_ij = exp((f_i + g_j - C_ij)/eps), never stored:
+ *   cost     = sum_ij P_ij C_ij
+ *   rowsum_i = sum_j P_ij,  colsum_j = sum_i P_ij
+ *   marg[0]  = sum_i |rowsum_i - a_i|,  marg[1] = sum_j |colsum_j - b_j|
+ * rowsum / colsum may be NULL.  Per-row and per-column partials are added in
+ * index order.
+ */
+void oracle_plan_stats(const double *x, const double *y, const double *a,
+                       const double *b, const double *f, const double *g,
+                       int64_t n, int64_t m, int d, double eps, double *cost,
+                       double *marg, double *rowsum, double *colsum)
+{
+    double *rs = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    double *rc = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    double *cs = (double *)malloc(sizeof(double) * (size_t)(m > 0 ? m : 1));
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < n; ++i) {
+        double s = 0.0, c = 0.0;
+        for (int64_t j = 0; j < m; ++j) {
+            double cij = sq_dist(x + i * (int64_t)d, y + j * (int64_t)d, d);
+            double p = exp((f[i] + g[j] - cij) / eps);
+            s += p;
+            c += p * cij;
+        }
+        rs[i] = s;
+        rc[i] = c;
+    }
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t j = 0; j < m; ++j) {
+        double s = 0.0;
+        for (int64_t i = 0; i < n; ++i) {
+            double cij = sq_dist(x + i * (int64_t)d, y + j * (int64_t)d, d);
+            s += exp((f[i] + g[j] - cij) / eps);
+        }
+        cs[j] = s;
+    }
+    double tc = 0.0, mr = 0.0, mc = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        tc += rc[i];
+        mr += fabs(rs[i] - a[i]);
+        if (rowsum)
+            rowsum[i] = rs[i];
+    }
+    for (int64_t j = 0; j < m; ++j) {
+        mc += fabs(cs[j] - b[j]);
+        if (colsum)
+            colsum[j] = cs[j];
+    }
+    *cost = tc;
+    marg[0] = mr;
+    marg[1] = mc;
+    free(rs);
+    free(rc);
+    free(cs);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Batched 4x4 Birkhoff projection: EOT with a = b = 1 and cost = -L.       */
+/* ---------------------------------------------------------------------- */
+
+static double lse4(const double v[4])
+{
+    double mx = v[0];
+    for (int k = 1; k < 4; ++k)
+        if (v[k] > mx)
+            mx = v[k];
+    double s = 0.0;
+    for (int k = 0; k < 4; ++k)
+        s += exp(v[k] - mx);
+    return mx + log(s);
+}
+
+/* One iteration on one matrix: f from g, then g from the new f. */
+static void birk_iter(const double L[16], double eps, double f[4], double g[4])
+{
+    double v[4];
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 4; ++j)
+            v[j] = (g[j] + L[4 * i + j]) / eps;
+        f[i] = -eps * lse4(v);
+    }
+    for (int j = 0; j < 4; ++j) {
+        for (int i = 0; i < 4; ++i)
+            v[i] = (f[i] + L[4 * i + j]) / eps;
+        g[j] = -eps * lse4(v);
+    }
+}
+
+/* P_ij = exp((f_i + g_j + L_ij)/eps) and the larger of the worst row-sum and
+ * worst column-sum deviation from 1. */
+static double birk_plan(const double L[16], double eps, const double f[4],
+                        const double g[4], double P[16])
+{
+    double err = 0.0;
+    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j)
+            P[4 * i + j] = exp((f[i] + g[j] + L[4 * i + j]) / eps);
+    for (int i = 0; i < 4; ++i) {
+        double s = P[4 * i] + P[4 * i + 1] + P[4 * i + 2] + P[4 * i + 3];
+        if (fabs(s - 1.0) > err)
+            err = fabs(s - 1.0);
+    }
+    for (int j = 0; j < 4; ++j) {
+        double s = P[j] + P[4 + j] + P[8 + j] + P[12 + j];
+        if (fabs(s - 1.0) > err)
+            err = fabs(s - 1.0);
+    }
+    return err;
+}
+
+/*
+ * For each of the B matrices (L row-major, 16 doubles each): start from g = 0,
+ * iterate; with tol >= 0 stop after the first iteration k >= 1 whose plan has
+ * error <= tol, else after max_iters; with tol < 0 run exactly max_iters.
+ * Writes the plan to P and the iteration count reached to iters_out (nullable).
+ */
+void oracle_birkhoff4(const double *L, int64_t B, double eps, int max_iters,
+                      double tol, double *P, int32_t *iters_out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t bi = 0; bi < B; ++bi) {
+        const double *Lb = L + 16 * bi;
+        double f[4] = {0, 0, 0, 0}, g[4] = {0, 0, 0, 0};
+        int k = 0;
+        for (k = 1; k <= max_iters; ++k) {
+            birk_iter(Lb, eps, f, g);
+            if (tol >= 0.0) {
+                double tmp[16];
+                if (birk_plan(Lb, eps, f, g, tmp) <= tol)
+                    break;
+            }
+        }
+        if (k > max_iters)
+            k = max_iters;
+        birk_plan(Lb, eps, f, g, P + 16 * bi);
+        if (iters_out)
+            iters_out[bi] = k;
+    }
+}
+
+/* Exactly iters[b] iterations for matrix b (replay of a given count); also
+ * returns each plan's error in err (nullable). */
+void oracle_birkhoff4_replay(const double *L, int64_t B, double eps,
+                             const int32_t *iters, double *P, double *err)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t bi = 0; bi < B; ++bi) {
+        const double *Lb = L + 16 * bi;
+        double f[4] = {0, 0, 0, 0}, g[4] = {0, 0, 0, 0};
+        for (int k = 0; k < iters[bi]; ++k)
+            birk_iter(Lb, eps, f, g);
+        double e = birk_plan(Lb, eps, f, g, P + 16 * bi);
+        if (err)
+            err[bi] = e;
+    }
+}

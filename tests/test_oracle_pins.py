@@ -1,0 +1,427 @@
+"""Pins of the fp64 oracle against facts fixed outside it.
+
+Nothing here re-types the oracle's update. Each test checks the oracle against
+one of: a closed form, an invariant every iterate must satisfy, a library
+routine (scipy), a different algorithm reaching the same unique solution, or
+brute force on tiny inputs. The form of the update these pin is the
+log-domain Sinkhorn step of "FlashSinkhorn: IO-Aware Entropic Optimal
+Transport on GPU" (Methodik section 1) in the convention with eps*log a
+outside the log-sum-exp; the 4x4 case is the Birkhoff projection of the
+"Aceleración de la Proyección de Birkhoff ..." page (sections 1, 2, 4).
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.optimize import linear_sum_assignment, minimize
+from scipy.spatial.distance import cdist
+from scipy.special import logsumexp
+
+import oracle
+from workloads import make_logits, random_clouds
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def dense_cost(x, y):
+    return cdist(np.asarray(x, np.float64), np.asarray(y, np.float64), "sqeuclidean")
+
+
+def dense_plan(x, y, f, g, eps):
+    return np.exp((f[:, None] + g[None, :] - dense_cost(x, y)) / eps)
+
+
+# --------------------------------------------------------------------------- #
+# One half-step                                                                #
+# --------------------------------------------------------------------------- #
+
+@pytest.mark.parametrize("eps", [1.0, 0.1, 0.003])
+def test_half_step_matches_scipy_logsumexp(eps):
+    c = random_clouds(37, 53, 3, seed=1)
+    rng = np.random.default_rng(7)
+    g = rng.normal(0, 0.3, size=53)
+    f = oracle.half_update(c["x"], c["y"], c["a"], g, eps)
+    C = dense_cost(c["x"], c["y"])
+    ref = eps * np.log(c["a"].astype(np.float64)) - eps * logsumexp((g[None, :] - C) / eps, axis=1)
+    np.testing.assert_allclose(f, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_half_step_rows_subset_matches_full():
+    c = random_clouds(50, 41, 5, seed=2)
+    g = np.linspace(-0.2, 0.2, 41)
+    full = oracle.half_update(c["x"], c["y"], c["a"], g, 0.2)
+    rows = np.array([49, 0, 17, 17, 3])
+    np.testing.assert_array_equal(oracle.half_update(c["x"], c["y"], c["a"], g, 0.2, rows=rows),
+                                  full[rows])
+
+
+def test_half_step_survives_extreme_exponents():
+    # exp(-C/eps) underflows to 0 for every j in naive arithmetic here; the
+    # max-subtracted log-sum-exp must still be finite and exact.
+    x = np.array([[0.0, 0.0, 0.0], [10.0, 0.0, 0.0]])
+    y = np.array([[3.0, 0.0, 0.0], [4.0, 0.0, 0.0], [-5.0, 1.0, 0.0]])
+    a = np.array([0.5, 0.5])
+    g = np.zeros(3)
+    eps = 1e-3
+    f = oracle.half_update(x, y, a, g, eps)
+    C = dense_cost(x, y)
+    ref = eps * np.log(a) - eps * logsumexp(-C / eps, axis=1)
+    assert np.all(np.isfinite(f))
+    np.testing.assert_allclose(f, ref, rtol=1e-13)
+    # As eps -> 0 the soft-min becomes the min: f_i -> min_j C_ij.
+    np.testing.assert_allclose(f, C.min(axis=1), atol=20 * eps)
+
+
+# --------------------------------------------------------------------------- #
+# Marginal invariants: each half-step is the unique scaling that makes its    #
+# side's marginal exact.                                                       #
+# --------------------------------------------------------------------------- #
+
+@pytest.mark.parametrize("K", [1, 2, 7])
+def test_each_half_step_makes_its_marginal_exact(K):
+    c = random_clouds(23, 31, 4, seed=3)
+    eps = 0.25
+    # state after K-1 iterations, then the f half-step, then the g half-step
+    f, g = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, K - 1)
+    f_new = oracle.half_update(c["x"], c["y"], c["a"], g, eps)
+    P_half = dense_plan(c["x"], c["y"], f_new, g, eps)
+    np.testing.assert_allclose(P_half.sum(axis=1), c["a"].astype(np.float64), rtol=1e-12)
+    f_k, g_k = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, K)
+    np.testing.assert_allclose(f_k, f_new, rtol=0, atol=1e-14)
+    P = dense_plan(c["x"], c["y"], f_k, g_k, eps)
+    np.testing.assert_allclose(P.sum(axis=0), c["b"].astype(np.float64), rtol=1e-12)
+
+
+def test_iters_zero_leaves_potentials():
+    c = random_clouds(5, 6, 2, seed=4)
+    f0 = np.arange(5.0)
+    g0 = -np.arange(6.0)
+    f, g = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], 0.3, 0, f0, g0)
+    np.testing.assert_array_equal(f, f0)
+    np.testing.assert_array_equal(g, g0)
+
+
+# --------------------------------------------------------------------------- #
+# Closed forms                                                                 #
+# --------------------------------------------------------------------------- #
+
+@pytest.mark.parametrize("K", [1, 3])
+def test_single_source_point_closed_form(K):
+    # n = 1: g_j = eps log b_j + C_1j - f_1 and P_1j = b_j after every
+    # iteration; with a_1 = sum b the potentials are a fixed point.
+    rng = np.random.default_rng(5)
+    x = rng.normal(size=(1, 3))
+    y = rng.normal(size=(17, 3))
+    b = rng.dirichlet(np.ones(17))
+    a = np.array([b.sum()])
+    eps = 0.2
+    f, g = oracle.sinkhorn(x, y, a, b, eps, K)
+    C1 = dense_cost(x, y)[0]
+    f1 = eps * math.log(a[0]) - eps * logsumexp(-C1 / eps)  # first f from g = 0
+    assert f[0] == pytest.approx(f1, rel=1e-13, abs=1e-13)
+    np.testing.assert_allclose(g, eps * np.log(b) + C1 - f[0], rtol=1e-12, atol=1e-13)
+    P = dense_plan(x, y, f, g, eps)[0]
+    np.testing.assert_allclose(P, b, rtol=1e-12)
+    st = oracle.plan_stats(x, y, a, b, f, g, eps)
+    assert st["cost"] == pytest.approx(float(b @ C1), rel=1e-12)
+    assert st["marg"] == pytest.approx(0.0, abs=1e-14)
+
+
+def test_single_target_point_closed_form():
+    # m = 1, cold start: f_i = eps log a_i + C_i1, g_1 = eps log b_1 - eps log sum a,
+    # P_i1 = a_i b_1 / sum a.
+    rng = np.random.default_rng(6)
+    x = rng.normal(size=(13, 2))
+    y = rng.normal(size=(1, 2))
+    a = rng.dirichlet(np.ones(13)) * 0.7
+    b = np.array([0.7])
+    eps = 0.05
+    f, g = oracle.sinkhorn(x, y, a, b, eps, 1)
+    C = dense_cost(x, y)[:, 0]
+    np.testing.assert_allclose(f, eps * np.log(a) + C, rtol=1e-12)
+    assert g[0] == pytest.approx(eps * math.log(b[0]) - eps * math.log(a.sum()), abs=1e-13)
+    np.testing.assert_allclose(dense_plan(x, y, f, g, eps)[:, 0], a * b[0] / a.sum(), rtol=1e-11)
+
+
+def test_large_eps_gives_product_coupling():
+    # eps -> infinity: P -> a b^T and <P, C> -> sum a|x|^2 + sum b|y|^2 - 2 (sum a x).(sum b y).
+    c = random_clouds(40, 30, 3, seed=8)
+    a, b = c["a"].astype(np.float64), c["b"].astype(np.float64)
+    a, b = a / a.sum(), b / b.sum()
+    x, y = c["x"].astype(np.float64), c["y"].astype(np.float64)
+    eps = 1e7
+    f, g = oracle.sinkhorn(x, y, a, b, eps, 3)
+    P = dense_plan(x, y, f, g, eps)
+    np.testing.assert_allclose(P, np.outer(a, b), rtol=1e-5)
+    closed = a @ (x * x).sum(1) + b @ (y * y).sum(1) - 2 * (a @ x) @ (b @ y)
+    st = oracle.plan_stats(x, y, a, b, f, g, eps)
+    assert st["cost"] == pytest.approx(closed, rel=1e-5)
+
+
+# --------------------------------------------------------------------------- #
+# The pages' own form of the update and the dual shift                         #
+# --------------------------------------------------------------------------- #
+
+def test_matches_page_form_with_log_b_inside():
+    # FlashSinkhorn, Methodik 1, writes f_i <- -eps LSE_j[(g_j - C_ij)/eps + log b_j]
+    # (and the symmetric g with log a_i). That iteration, started from
+    # g' = -eps log b, must give the same plan as the oracle's form, with
+    # f = f' + eps log a and g = g' + eps log b at every iteration.
+    c = random_clouds(19, 26, 3, seed=9)
+    x, y = c["x"].astype(np.float64), c["y"].astype(np.float64)
+    a, b = c["a"].astype(np.float64), c["b"].astype(np.float64)
+    eps = 0.15
+    C = dense_cost(x, y)
+    gp = -eps * np.log(b)
+    for K in range(1, 6):
+        fp = -eps * logsumexp((gp[None, :] - C) / eps + np.log(b)[None, :], axis=1)
+        gp = -eps * logsumexp((fp[:, None] - C) / eps + np.log(a)[:, None], axis=0)
+        f, g = oracle.sinkhorn(x, y, a, b, eps, K)
+        np.testing.assert_allclose(f, fp + eps * np.log(a), rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(g, gp + eps * np.log(b), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("shift", [0.37, -2.5])
+def test_shift_covariance(shift):
+    # Potentials are defined up to (f + c, g - c) (Birkhoff page, section 2.1):
+    # starting from g0 - c gives (f + c, g - c) at every iteration, same plan.
+    c = random_clouds(14, 11, 3, seed=10)
+    eps = 0.3
+    g0 = np.linspace(-0.1, 0.2, 11)
+    f1, g1 = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, 6, g0=g0)
+    f2, g2 = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, 6, g0=g0 - shift)
+    np.testing.assert_allclose(f2, f1 + shift, atol=1e-12)
+    np.testing.assert_allclose(g2, g1 - shift, atol=1e-12)
+    np.testing.assert_allclose(dense_plan(c["x"], c["y"], f2, g2, eps),
+                               dense_plan(c["x"], c["y"], f1, g1, eps), rtol=1e-11)
+
+
+# --------------------------------------------------------------------------- #
+# Fixed point: a different algorithm (Newton on the dual) reaches the same    #
+# unique entropic plan                                                         #
+# --------------------------------------------------------------------------- #
+
+def dual_newton_plan(C, a, b, eps):
+    n, m = C.shape
+
+    def split(z):
+        return z[:n], np.concatenate([z[n:], [0.0]])  # g_m = 0 removes the shift
+
+    def fun(z):
+        f, g = split(z)
+        P = np.exp((f[:, None] + g[None, :] - C) / eps)
+        val = -(a @ f + b @ g - eps * P.sum())
+        grad = np.concatenate([P.sum(1) - a, (P.sum(0) - b)[:-1]])
+        return val, grad
+
+    def hess(z):
+        f, g = split(z)
+        P = np.exp((f[:, None] + g[None, :] - C) / eps)
+        H = np.zeros((n + m - 1, n + m - 1))
+        H[:n, :n] = np.diag(P.sum(1))
+        H[n:, n:] = np.diag(P.sum(0)[:-1])
+        H[:n, n:] = P[:, :-1]
+        H[n:, :n] = P[:, :-1].T
+        return H / eps
+
+    res = minimize(fun, np.zeros(n + m - 1), jac=True, hess=hess, method="trust-exact",
+                   options={"gtol": 1e-14, "maxiter": 500})
+    f, g = split(res.x)
+    return np.exp((f[:, None] + g[None, :] - C) / eps)
+
+
+@pytest.mark.parametrize("eps", [1.0, 0.3])
+def test_converged_plan_equals_dual_newton_plan(eps):
+    c = random_clouds(12, 9, 3, seed=11)
+    a, b = c["a"].astype(np.float64), c["b"].astype(np.float64)
+    a, b = a / a.sum(), b / b.sum()
+    f, g = oracle.sinkhorn(c["x"], c["y"], a, b, eps, 3000)
+    P = dense_plan(c["x"], c["y"], f, g, eps)
+    Pn = dual_newton_plan(dense_cost(c["x"], c["y"]), a, b, eps)
+    np.testing.assert_allclose(P, Pn, atol=1e-10 * Pn.max())
+    st = oracle.plan_stats(c["x"], c["y"], a, b, f, g, eps)
+    assert st["marg"] < 1e-10
+
+
+# --------------------------------------------------------------------------- #
+# eps -> 0: exact OT by brute force / assignment / 1-D sorting                 #
+# --------------------------------------------------------------------------- #
+
+def _small_eps_solve(x, y, a, b, eps_end):
+    eps_list = np.geomspace(1.0, eps_end, 25)
+    return oracle.sinkhorn_schedule(x, y, a, b, eps_list, 400)
+
+
+def _check_entropic_bound(x, y, ot, eps_end, n):
+    a = np.full(n, 1.0 / n)
+    f, g = _small_eps_solve(x, y, a, a, eps_end)
+    st = oracle.plan_stats(x, y, a, a, f, g, eps_end)
+    slack = st["marg"] * dense_cost(x, y).max()
+    assert st["cost"] >= ot - slack - 1e-12
+    assert st["cost"] <= ot + eps_end * math.log(n) + slack + 1e-12
+    return f, g
+
+
+@pytest.mark.parametrize("n", [3, 5, 7])
+def test_small_eps_brute_force_permutations(n):
+    rng = np.random.default_rng(100 + n)
+    x = rng.normal(size=(n, 2))
+    y = rng.normal(size=(n, 2))
+    C = dense_cost(x, y)
+    costs = {p: C[np.arange(n), list(p)].mean() for p in itertools.permutations(range(n))}
+    best = min(costs, key=costs.get)
+    f, g = _check_entropic_bound(x, y, costs[best], 2e-3, n)
+    # The plan concentrates on the optimal permutation.
+    P = dense_plan(x, y, f, g, 2e-3)
+    assert list(P.argmax(axis=1)) == list(best)
+
+
+def test_small_eps_assignment():
+    n = 40
+    rng = np.random.default_rng(12)
+    x = rng.normal(size=(n, 3))
+    y = rng.normal(size=(n, 3))
+    C = dense_cost(x, y)
+    r, cidx = linear_sum_assignment(C)
+    _check_entropic_bound(x, y, C[r, cidx].mean(), 2e-3, n)
+
+
+def test_small_eps_one_dimension_sorted_matching():
+    n = 64
+    rng = np.random.default_rng(13)
+    x = rng.normal(size=(n, 1))
+    y = rng.uniform(-1, 2, size=(n, 1))
+    ot = np.mean((np.sort(x[:, 0]) - np.sort(y[:, 0])) ** 2)
+    _check_entropic_bound(x, y, ot, 2e-3, n)
+
+
+# --------------------------------------------------------------------------- #
+# Stages (warm start)                                                          #
+# --------------------------------------------------------------------------- #
+
+def test_stage_composition_equals_longer_run():
+    c = random_clouds(16, 21, 3, seed=14)
+    f1, g1 = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], 0.2, 5)
+    f2, g2 = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], 0.2, 7, f1, g1)
+    f3, g3 = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], 0.2, 12)
+    np.testing.assert_array_equal(f2, f3)
+    np.testing.assert_array_equal(g2, g3)
+    f4, g4 = oracle.sinkhorn_schedule(c["x"], c["y"], c["a"], c["b"], [0.2, 0.2], 6)
+    np.testing.assert_array_equal(f4, f3)
+    np.testing.assert_array_equal(g4, g3)
+
+
+def test_schedule_converges_to_final_eps_fixed_point():
+    c = random_clouds(10, 8, 3, seed=15)
+    a, b = c["a"].astype(np.float64), c["b"].astype(np.float64)
+    a, b = a / a.sum(), b / b.sum()
+    f, g = oracle.sinkhorn_schedule(c["x"], c["y"], a, b, [2.0, 1.0, 0.5], 2000)
+    P = dense_plan(c["x"], c["y"], f, g, 0.5)
+    np.testing.assert_allclose(P, dual_newton_plan(dense_cost(c["x"], c["y"]), a, b, 0.5),
+                               atol=1e-10)
+
+
+# --------------------------------------------------------------------------- #
+# plan statistics                                                              #
+# --------------------------------------------------------------------------- #
+
+def test_plan_stats_column_marginal_exact_after_g_step():
+    c = random_clouds(30, 25, 3, seed=16)
+    f, g = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], 0.4, 4)
+    st = oracle.plan_stats(c["x"], c["y"], c["a"], c["b"], f, g, 0.4)
+    assert st["marg_col"] < 1e-14
+    assert st["marg_row"] > 1e-8  # not converged after 4 iterations
+    np.testing.assert_allclose(st["colsum"], c["b"], rtol=1e-12)
+
+
+# --------------------------------------------------------------------------- #
+# 4x4 Birkhoff projection                                                       #
+# --------------------------------------------------------------------------- #
+
+def test_birkhoff_converged_doubly_stochastic():
+    L = make_logits(256, (1.0, 3.0), seed=17)
+    P, it = oracle.birkhoff4(L, 1.0, 5000, 1e-12)
+    assert np.all(it < 5000)
+    np.testing.assert_allclose(P.sum(axis=2), 1.0, atol=1e-12)
+    np.testing.assert_allclose(P.sum(axis=1), 1.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("iters", [1, 20])
+def test_birkhoff_cross_ratio_invariant(iters):
+    # Every iterate is diag(u) exp(L/eps) diag(v), so the cross ratios of P are
+    # those of exp(L/eps), whatever the iteration count.
+    L = make_logits(64, (1.0, 10.0), seed=18).astype(np.float64)
+    eps = 1.0
+    P, _ = oracle.birkhoff4(L, eps, iters, -1.0)
+    for i, k in [(0, 1), (2, 3), (0, 3)]:
+        for j, l in [(0, 2), (1, 3), (1, 2)]:
+            lhs = np.log(P[:, i, j]) + np.log(P[:, k, l]) - np.log(P[:, i, l]) - np.log(P[:, k, j])
+            rhs = (L[:, i, j] + L[:, k, l] - L[:, i, l] - L[:, k, j]) / eps
+            assert np.all(np.abs(lhs - rhs) <= 1e-9 * (1 + np.abs(rhs)))
+
+
+def test_birkhoff_constant_logits():
+    L = np.full((3, 4, 4), 2.5)
+    P, it = oracle.birkhoff4(L, 1.0, 200, 1e-6)
+    np.testing.assert_allclose(P, 0.25, rtol=1e-14)
+    assert list(it) == [1, 1, 1]
+
+
+def test_birkhoff_circulant_exact_after_one_iteration():
+    # A circulant exp(L) has equal row and column sums, so the first f step
+    # already gives a doubly-stochastic plan: K / rowsum.
+    c = np.array([0.3, -1.2, 2.0, 0.7])
+    L = np.array([[c[(j - i) % 4] for j in range(4)] for i in range(4)])[None]
+    P, it = oracle.birkhoff4(L, 1.0, 200, 1e-12)
+    K = np.exp(L[0])
+    np.testing.assert_allclose(P[0], K / K.sum(axis=1, keepdims=True), rtol=1e-13)
+    assert it[0] == 1
+
+
+def test_birkhoff_dominant_permutation():
+    perm = [2, 0, 3, 1]
+    L = np.zeros((1, 4, 4))
+    L[0, np.arange(4), perm] = 30.0
+    P, _ = oracle.birkhoff4(L, 1.0, 200, 1e-9)
+    Pi = np.zeros((4, 4))
+    Pi[np.arange(4), perm] = 1.0
+    np.testing.assert_allclose(P[0], Pi, atol=1e-9)
+
+
+def test_birkhoff_limit_matches_dual_newton():
+    # Sinkhorn's theorem: the limit is the unique doubly-stochastic matrix of
+    # the form diag(u) exp(L) diag(v); Newton on the 4x4 dual finds it too.
+    L = make_logits(6, (1.0, 4.0), seed=19).astype(np.float64)
+    P, _ = oracle.birkhoff4(L, 1.0, 20000, 1e-14)
+    for k in range(L.shape[0]):
+        Pn = dual_newton_plan(-L[k], np.ones(4), np.ones(4), 1.0)
+        np.testing.assert_allclose(P[k], Pn, atol=1e-11)
+
+
+def test_birkhoff_stopping_rule_is_first_crossing():
+    L = make_logits(512, (1.0, 10.0), seed=20)
+    tol = 1e-6
+    P, it = oracle.birkhoff4(L, 1.0, 200, tol)
+    Pr, err = oracle.birkhoff4_replay(L, it, 1.0)
+    np.testing.assert_array_equal(P, Pr)
+    conv = it < 200
+    assert np.all(err[conv] <= tol)
+    assert conv.sum() > 100
+    prev = np.maximum(it - 1, 0)
+    _, err_prev = oracle.birkhoff4_replay(L, prev, 1.0)
+    assert np.all(err_prev[conv & (it > 1)] > tol)
+
+
+def test_birkhoff_fixed20_sigma_split():
+    claim = {c["id"]: c for c in json.load(open(os.path.join(GOLDEN, "page_claims.json")))["claims"]}
+    ratio_min = claim["birkhoff_fixed20_sigma"]["min_median_ratio"]
+    L = make_logits(4096, (1.0, 10.0), seed=21)
+    P, it = oracle.birkhoff4(L, 1.0, 20, -1.0)
+    assert np.all(it == 20)
+    err = np.maximum(np.abs(P.sum(2) - 1).max(1), np.abs(P.sum(1) - 1).max(1))
+    med1 = np.median(err[:2048])
+    med10 = np.median(err[2048:])
+    assert med10 > ratio_min * med1
