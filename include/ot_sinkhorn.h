@@ -1,0 +1,169 @@
+/*
+ * ot_sinkhorn.h -- C ABI of the MI355X (gfx950) log-domain Sinkhorn library.
+ *
+ * Problem (page "FlashSinkhorn: IO-Aware Entropic Optimal Transport on GPU",
+ * technical summary, "Problemstellung" and "Methodik"): entropic optimal
+ * transport between two weighted point clouds x (n points) and y (m points)
+ * in R^d with weights a and b and squared Euclidean cost
+ * C_ij = |x_i - y_j|^2, solved by stabilised log-domain Sinkhorn iterations.
+ *
+ * Convention used by every call below (the page's "Methodik" section 1 writes
+ * the same update with log b_j inside the log-sum-exp instead; the two give
+ * the same plan with f = f' + eps log a, g = g' + eps log b):
+ *
+ *   f_i <- eps*log a_i - eps*LSE_j((g_j - C_ij)/eps)
+ *   g_j <- eps*log b_j - eps*LSE_i((f_i - C_ij)/eps)      (uses the new f)
+ *   P_ij = exp((f_i + g_j - C_ij)/eps)                      (the plan)
+ *
+ * One iteration is one f update followed by one g update. C and P are never
+ * stored in memory; they are formed tile by tile on chip (page section
+ * "Methodik" 2).
+ *
+ * General rules
+ *  - Every array argument is a DEVICE pointer to memory the caller owns.
+ *    The library keeps no buffer between calls; temporary device memory is
+ *    taken with hipMallocAsync on `stream` and released with hipFreeAsync on
+ *    the same stream.
+ *  - Point arrays are contiguous row-major fp32: x[i*d + k], y[j*d + k].
+ *    Potentials and weights are contiguous fp32 vectors.  Pointers must be
+ *    4-byte aligned.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *    All work is enqueued on it and the call returns without synchronising,
+ *    except where a result is stated to be written to host memory.
+ *  - Arguments are validated on the host before anything is enqueued; an
+ *    invalid call returns OT_ERROR_INVALID_VALUE and enqueues nothing.
+ *  - Preconditions that are NOT checked (checking would need a device read):
+ *    finite inputs, a_i > 0, b_j > 0. Violations give NaN or inf results,
+ *    not an error code.
+ *  - Outputs must not alias inputs unless a call says otherwise.
+ *  - Calls are stateless; concurrent calls on different streams are safe.
+ */
+#ifndef OT_SINKHORN_H
+#define OT_SINKHORN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    OT_SUCCESS = 0,
+    OT_ERROR_INVALID_VALUE = 1,  /* bad argument; nothing was enqueued          */
+    OT_ERROR_NOT_SUPPORTED = 2,  /* valid but unsupported (e.g. d > OT_MAX_DIM) */
+    OT_ERROR_OUT_OF_MEMORY = 3,  /* a temporary device allocation failed         */
+    OT_ERROR_LAUNCH_FAILURE = 4  /* a HIP call or kernel launch reported an error */
+} ot_status;
+
+/* Largest feature dimension d the point-cloud calls accept (the fp32 matrix-
+ * core kernels keep a row's coordinates in registers up to this size). */
+#define OT_MAX_DIM 128
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *ot_status_string(ot_status s);
+
+/*
+ * ot_sinkhorn_solve -- `iters` alternating log-domain Sinkhorn iterations at
+ * regularisation eps (page "FlashSinkhorn ...", "Methodik" section 1).
+ *
+ *   x      [n*d]  source points            y  [m*d]  target points
+ *   a      [n]    source weights (> 0)     b  [m]    target weights (> 0)
+ *   n, m   >= 1   d in [1, OT_MAX_DIM]     eps > 0 and finite
+ *   iters  >= 0   (0 leaves f and g untouched)
+ *   f      [n]    in/out; overwritten by the first f update
+ *   g      [m]    in/out; read by the first f update (zeros = cold start),
+ *                 holds the last g update on return
+ *
+ * Warm start (e.g. a decreasing eps schedule) is a second call with the f, g
+ * of the first.  f and g must not overlap each other or any input.
+ * Errors: INVALID_VALUE (null pointer, n or m < 1, d < 1, eps <= 0 or not
+ * finite, iters < 0), NOT_SUPPORTED (d > OT_MAX_DIM), OUT_OF_MEMORY,
+ * LAUNCH_FAILURE.
+ */
+ot_status ot_sinkhorn_solve(const float *x, const float *y, const float *a,
+                            const float *b, int64_t n, int64_t m, int32_t d,
+                            float eps, int32_t iters, float *f, float *g,
+                            void *stream);
+
+/*
+ * ot_sinkhorn_solve_eps_scaling -- `stages` calls of ot_sinkhorn_solve with
+ * eps_s = eps0 * (eps_end/eps0)^(s/(stages-1)), s = 0..stages-1 (eps0 alone
+ * when stages == 1), `iters_per_stage` iterations each, each stage starting
+ * from the previous stage's f and g.  The schedule is not on the pages; it
+ * is the usual warm-started decreasing-eps driver around the same update.
+ * Arguments as ot_sinkhorn_solve; stages >= 1, eps0 and eps_end > 0 and
+ * finite, iters_per_stage >= 0.
+ */
+ot_status ot_sinkhorn_solve_eps_scaling(const float *x, const float *y,
+                                        const float *a, const float *b,
+                                        int64_t n, int64_t m, int32_t d,
+                                        float eps0, float eps_end,
+                                        int32_t stages, int32_t iters_per_stage,
+                                        float *f, float *g, void *stream);
+
+/*
+ * ot_plan_stats -- statistics of the plan P_ij = exp((f_i + g_j - C_ij)/eps)
+ * without storing it (page "FlashSinkhorn ...", "Methodik" section 3: the
+ * transport plan is applied by streaming, never materialised):
+ *
+ *   cost    = sum_ij P_ij * C_ij                       (device double [1])
+ *   marg[0] = sum_i |sum_j P_ij - a_i|                   (device double [2])
+ *   marg[1] = sum_j |sum_i P_ij - b_j|
+ *
+ * Either output may be NULL to skip it (both NULL is INVALID_VALUE); a, b
+ * may be NULL when marg is NULL.  Per-pair terms are fp32 with fp64 partial
+ * sums combined in a fixed order, so repeated calls give identical results.
+ * Errors as ot_sinkhorn_solve.
+ */
+ot_status ot_plan_stats(const float *x, const float *y, const float *a,
+                        const float *b, const float *f, const float *g,
+                        int64_t n, int64_t m, int32_t d, float eps,
+                        double *cost, double *marg, void *stream);
+
+/* ot_plan_cost -- ot_plan_stats with cost only (device double [1]). */
+ot_status ot_plan_cost(const float *x, const float *y, const float *f,
+                       const float *g, int64_t n, int64_t m, int32_t d,
+                       float eps, double *cost, void *stream);
+
+/* ot_marginal_error -- ot_plan_stats with marg only (device double [2] =
+ * {row L1 error, column L1 error}). */
+ot_status ot_marginal_error(const float *x, const float *y, const float *a,
+                            const float *b, const float *f, const float *g,
+                            int64_t n, int64_t m, int32_t d, float eps,
+                            double *marg, void *stream);
+
+/*
+ * ot_birkhoff_project_batched -- project each 4x4 matrix of a batch onto the
+ * doubly-stochastic matrices (page "Aceleración de la Proyección de Birkhoff
+ * para Hiper-conexiones ...", sections 1-2: the projection is entropic OT
+ * with unit marginals and cost -L, iterated by Sinkhorn-Knopp), here in the
+ * log domain with the maximum subtracted before exponentiating (section 2.1):
+ *
+ *   g = 0; repeat:  f_i = -eps*LSE_j((g_j + L_ij)/eps)
+ *                   g_j = -eps*LSE_i((f_i + L_ij)/eps)
+ *   out_ij = exp((f_i + g_j + L_ij)/eps)
+ *
+ *   logits    [batch*16]  row-major 4x4 matrices L (fp32)
+ *   batch     >= 0        (0 is a no-op)
+ *   eps       > 0 and finite
+ *   max_iters >= 0        iteration cap (0 returns exp(L/eps))
+ *   tol       < 0: run exactly max_iters iterations;
+ *             >= 0: stop a matrix after the first iteration k >= 1 whose plan
+ *             has max_i |sum_j out_ij - 1| <= tol (column sums equal 1 up to
+ *             rounding after every iteration), or at max_iters.  NaN is invalid.
+ *   out       [batch*16]  result; may alias logits exactly (in place)
+ *   iters_out [batch]     nullable; iterations each matrix ran (int32)
+ *
+ * Errors: INVALID_VALUE (null logits/out, batch < 0, eps <= 0 or not finite,
+ * max_iters < 0, NaN tol, partial overlap of out and logits), LAUNCH_FAILURE.
+ */
+ot_status ot_birkhoff_project_batched(const float *logits, int64_t batch,
+                                      float eps, int32_t max_iters, float tol,
+                                      float *out, int32_t *iters_out,
+                                      void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OT_SINKHORN_H */

@@ -1,0 +1,265 @@
+// Host side of the C ABI declared in include/ot_sinkhorn.h: argument checks,
+// stream-ordered scratch, and the launch sequence of each call.
+#include "ot_sinkhorn.h"
+#include "ot_internal.h"
+
+#include <math.h>
+#include <stdint.h>
+
+namespace otsk {
+
+Layout choose_layout(int d) {
+    Layout L;
+    L.d = d;
+    if (d < 32) {
+        // VALU kernels: coordinates padded to 4k-1 so coordinates + bias fill
+        // whole float4s (d = 3: one 16-byte record).
+        L.kp = (d + 1 + 3) / 4 * 4 - 1;
+        L.rs = L.kp + 1;
+        L.mfma = false;
+    } else {
+        // MFMA kernels: coordinates padded to a multiple of 16 (each lane
+        // half reads KP/2 floats as whole float4s); bias at KP; stride KP + 4.
+        L.kp = (d + 15) / 16 * 16;
+        L.rs = L.kp + 4;
+        L.mfma = true;
+    }
+    return L;
+}
+
+}  // namespace otsk
+
+using namespace otsk;
+
+namespace {
+
+ot_status map_error(hipError_t e) {
+    if (e == hipSuccess)
+        return OT_SUCCESS;
+    if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
+        return OT_ERROR_OUT_OF_MEMORY;
+    return OT_ERROR_LAUNCH_FAILURE;
+}
+
+bool overlaps(const void *p, size_t pb, const void *q, size_t qb) {
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+    return a < b + qb && b < a + pb;
+}
+
+bool finite_pos(float v) { return isfinite(v) && v > 0.f; }
+
+// Arguments every point-cloud call shares. Invalid values first, then
+// what is valid but not supported.
+ot_status check_clouds(const float *x, const float *y, int64_t n, int64_t m, int32_t d,
+                       float eps) {
+    if (!x || !y || n < 1 || m < 1 || d < 1 || !finite_pos(eps))
+        return OT_ERROR_INVALID_VALUE;
+    return OT_SUCCESS;
+}
+
+ot_status check_supported(int64_t n, int64_t m, int32_t d) {
+    if (d > OT_MAX_DIM)
+        return OT_ERROR_NOT_SUPPORTED;
+    // 64-bit index arithmetic everywhere; keep point counts well inside it.
+    if (n > ((int64_t)1 << 40) || m > ((int64_t)1 << 40))
+        return OT_ERROR_NOT_SUPPORTED;
+    return OT_SUCCESS;
+}
+
+// A block of device scratch memory taken and released on the call's stream.
+struct Scratch {
+    void *ptr = nullptr;
+    hipStream_t s;
+    explicit Scratch(hipStream_t st) : s(st) {}
+    hipError_t alloc(size_t bytes) { return hipMallocAsync(&ptr, bytes < 256 ? 256 : bytes, s); }
+    ~Scratch() {
+        if (ptr)
+            (void)hipFreeAsync(ptr, s);
+    }
+};
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+ot_status run_schedule(const float *x, const float *y, const float *a, const float *b, int64_t n,
+                       int64_t m, int32_t d, const double *eps_list, int stages, int iters,
+                       float *f, float *g, hipStream_t s) {
+    const Layout L = choose_layout(d);
+    const int64_t n_pad = pad_points(n), m_pad = pad_points(m);
+    size_t part = L.mfma ? half_step_partials_mfma(n, m_pad) : half_step_partials(L, n, m_pad);
+    const size_t part2 =
+        L.mfma ? half_step_partials_mfma(m, n_pad) : half_step_partials(L, m, n_pad);
+    if (part2 > part)
+        part = part2;
+    const size_t xb = align_up((size_t)n_pad * L.rs * sizeof(float), 256);
+    const size_t yb = align_up((size_t)m_pad * L.rs * sizeof(float), 256);
+    const size_t pb = part * sizeof(float2);
+    Scratch sc(s);
+    hipError_t e = sc.alloc(xb + yb + pb);
+    if (e != hipSuccess)
+        return map_error(e);
+    float *xrec = static_cast<float *>(sc.ptr);
+    float *yrec = reinterpret_cast<float *>(static_cast<char *>(sc.ptr) + xb);
+    float2 *partials = reinterpret_cast<float2 *>(static_cast<char *>(sc.ptr) + xb + yb);
+
+    if ((e = launch_prep_side(x, nullptr, n, n_pad, L, 0.f, kBiasZero, xrec, s)) != hipSuccess)
+        return map_error(e);
+    for (int st = 0; st < stages; ++st) {
+        const double eps = eps_list[st];
+        const float hat_scale = (float)(kLog2e / eps);
+        // Column bias of the first f update, from the caller's (or the
+        // previous stage's) g at this stage's eps.
+        if ((e = launch_prep_side(y, g, m, m_pad, L, hat_scale, kBiasHat, yrec, s)) != hipSuccess)
+            return map_error(e);
+        HalfStep hf{xrec, xrec, a, yrec, f, n, m_pad, (float)(2.0 * kLog2e / eps),
+                    (float)(eps * kLn2), partials, n_pad};
+        HalfStep hg{yrec, yrec, b, xrec, g, m, n_pad, (float)(2.0 * kLog2e / eps),
+                    (float)(eps * kLn2), partials, m_pad};
+        for (int it = 0; it < iters; ++it) {
+            e = L.mfma ? launch_half_step_mfma(hf, L, s) : launch_half_step_valu(hf, L, s);
+            if (e != hipSuccess)
+                return map_error(e);
+            e = L.mfma ? launch_half_step_mfma(hg, L, s) : launch_half_step_valu(hg, L, s);
+            if (e != hipSuccess)
+                return map_error(e);
+        }
+    }
+    return OT_SUCCESS;
+}
+
+ot_status check_solve_outputs(const float *x, const float *y, const float *a, const float *b,
+                              int64_t n, int64_t m, int32_t d, const float *f, const float *g) {
+    if (!a || !b || !f || !g)
+        return OT_ERROR_INVALID_VALUE;
+    const size_t fb = (size_t)n * 4, gb = (size_t)m * 4;
+    if (overlaps(f, fb, g, gb))
+        return OT_ERROR_INVALID_VALUE;
+    const void *ins[4] = {x, y, a, b};
+    const size_t inb[4] = {(size_t)n * d * 4, (size_t)m * d * 4, fb, gb};
+    for (int k = 0; k < 4; ++k)
+        if (overlaps(f, fb, ins[k], inb[k]) || overlaps(g, gb, ins[k], inb[k]))
+            return OT_ERROR_INVALID_VALUE;
+    return OT_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ot_status_string(ot_status s) {
+    switch (s) {
+    case OT_SUCCESS: return "OT_SUCCESS";
+    case OT_ERROR_INVALID_VALUE: return "OT_ERROR_INVALID_VALUE";
+    case OT_ERROR_NOT_SUPPORTED: return "OT_ERROR_NOT_SUPPORTED";
+    case OT_ERROR_OUT_OF_MEMORY: return "OT_ERROR_OUT_OF_MEMORY";
+    case OT_ERROR_LAUNCH_FAILURE: return "OT_ERROR_LAUNCH_FAILURE";
+    default: return "OT_ERROR_UNKNOWN";
+    }
+}
+
+ot_status ot_sinkhorn_solve(const float *x, const float *y, const float *a, const float *b,
+                            int64_t n, int64_t m, int32_t d, float eps, int32_t iters, float *f,
+                            float *g, void *stream) {
+    ot_status st = check_clouds(x, y, n, m, d, eps);
+    if (st == OT_SUCCESS && iters < 0)
+        st = OT_ERROR_INVALID_VALUE;
+    if (st == OT_SUCCESS)
+        st = check_solve_outputs(x, y, a, b, n, m, d, f, g);
+    if (st == OT_SUCCESS)
+        st = check_supported(n, m, d);
+    if (st != OT_SUCCESS || iters == 0)
+        return st;
+    const double e = eps;
+    return run_schedule(x, y, a, b, n, m, d, &e, 1, iters, f, g, (hipStream_t)stream);
+}
+
+ot_status ot_sinkhorn_solve_eps_scaling(const float *x, const float *y, const float *a,
+                                        const float *b, int64_t n, int64_t m, int32_t d,
+                                        float eps0, float eps_end, int32_t stages,
+                                        int32_t iters_per_stage, float *f, float *g,
+                                        void *stream) {
+    ot_status st = check_clouds(x, y, n, m, d, eps0);
+    if (st == OT_SUCCESS && (!finite_pos(eps_end) || stages < 1 || iters_per_stage < 0))
+        st = OT_ERROR_INVALID_VALUE;
+    if (st == OT_SUCCESS)
+        st = check_solve_outputs(x, y, a, b, n, m, d, f, g);
+    if (st == OT_SUCCESS)
+        st = check_supported(n, m, d);
+    if (st == OT_SUCCESS && stages > 4096)
+        st = OT_ERROR_NOT_SUPPORTED;
+    if (st != OT_SUCCESS || iters_per_stage == 0)
+        return st;
+    double eps_list[4096];
+    for (int s = 0; s < stages; ++s)
+        eps_list[s] = stages == 1 ? (double)eps0
+                                  : (double)eps0 * pow((double)eps_end / (double)eps0,
+                                                       (double)s / (double)(stages - 1));
+    return run_schedule(x, y, a, b, n, m, d, eps_list, stages, iters_per_stage, f, g,
+                        (hipStream_t)stream);
+}
+
+ot_status ot_plan_stats(const float *x, const float *y, const float *a, const float *b,
+                        const float *f, const float *g, int64_t n, int64_t m, int32_t d, float eps,
+                        double *cost, double *marg, void *stream) {
+    ot_status st = check_clouds(x, y, n, m, d, eps);
+    if (st == OT_SUCCESS && (!f || !g || (!cost && !marg) || (marg && (!a || !b))))
+        st = OT_ERROR_INVALID_VALUE;
+    if (st == OT_SUCCESS)
+        st = check_supported(n, m, d);
+    if (st != OT_SUCCESS)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    const Layout L = choose_layout(d);
+    const int64_t n_pad = pad_points(n), m_pad = pad_points(m);
+    const size_t xb = align_up((size_t)n_pad * L.rs * sizeof(float), 256);
+    const size_t yb = align_up((size_t)m_pad * L.rs * sizeof(float), 256);
+    const size_t db = plan_stats_scratch_doubles(L, n, m, n_pad, m_pad) * sizeof(double);
+    Scratch sc(s);
+    hipError_t e = sc.alloc(xb + yb + db);
+    if (e != hipSuccess)
+        return map_error(e);
+    float *xrec = static_cast<float *>(sc.ptr);
+    float *yrec = reinterpret_cast<float *>(static_cast<char *>(sc.ptr) + xb);
+    double *dsc = reinterpret_cast<double *>(static_cast<char *>(sc.ptr) + xb + yb);
+    if ((e = launch_prep_side(x, f, n, n_pad, L, 0.f, kBiasRaw, xrec, s)) != hipSuccess)
+        return map_error(e);
+    if ((e = launch_prep_side(y, g, m, m_pad, L, 0.f, kBiasRaw, yrec, s)) != hipSuccess)
+        return map_error(e);
+    e = launch_plan_stats(xrec, yrec, a, b, n, m, n_pad, m_pad, L, eps, cost, marg, dsc, s);
+    return map_error(e);
+}
+
+ot_status ot_plan_cost(const float *x, const float *y, const float *f, const float *g, int64_t n,
+                       int64_t m, int32_t d, float eps, double *cost, void *stream) {
+    if (!cost)
+        return OT_ERROR_INVALID_VALUE;
+    return ot_plan_stats(x, y, nullptr, nullptr, f, g, n, m, d, eps, cost, nullptr, stream);
+}
+
+ot_status ot_marginal_error(const float *x, const float *y, const float *a, const float *b,
+                            const float *f, const float *g, int64_t n, int64_t m, int32_t d,
+                            float eps, double *marg, void *stream) {
+    if (!marg)
+        return OT_ERROR_INVALID_VALUE;
+    return ot_plan_stats(x, y, a, b, f, g, n, m, d, eps, nullptr, marg, stream);
+}
+
+ot_status ot_birkhoff_project_batched(const float *logits, int64_t batch, float eps,
+                                      int32_t max_iters, float tol, float *out,
+                                      int32_t *iters_out, void *stream) {
+    if (!logits || !out || batch < 0 || !finite_pos(eps) || max_iters < 0 || isnan(tol))
+        return OT_ERROR_INVALID_VALUE;
+    if (((uintptr_t)logits & 15) || ((uintptr_t)out & 15))
+        return OT_ERROR_INVALID_VALUE;
+    const size_t bytes = (size_t)batch * 16 * sizeof(float);
+    if (logits != out && overlaps(logits, bytes, out, bytes))
+        return OT_ERROR_INVALID_VALUE;
+    if (iters_out && (overlaps(iters_out, (size_t)batch * 4, out, bytes) ||
+                      overlaps(iters_out, (size_t)batch * 4, logits, bytes)))
+        return OT_ERROR_INVALID_VALUE;
+    if (batch == 0)
+        return OT_SUCCESS;
+    return map_error(launch_birkhoff4(logits, batch, eps, max_iters, tol, out, iters_out,
+                                      (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,122 @@
+// Batched projection of 4x4 matrices onto the doubly-stochastic matrices.
+//
+// "Aceleración de la Proyección de Birkhoff para Hiper-conexiones con
+// Restricción de Variedad" (and its French twin), sections 1-2: the Birkhoff
+// projection is entropic OT with unit marginals and cost -L, solved by
+// Sinkhorn-Knopp; section 2.1 subtracts the maximum before exponentiating;
+// section 1 names the common fixed budget of 20 iterations. In base 2, with
+// l_ij = L_ij * log2(e)/eps and potentials in units of eps/log2(e):
+//
+//   f_i = -log2 sum_j 2^(g_j + l_ij),   g_j = -log2 sum_i 2^(f_i + l_ij)
+//   out_ij = 2^(f_i + g_j + l_ij)
+//
+// One matrix per lane, everything in registers, no cross-lane traffic (the
+// page's kernel puts two matrices in a 32-lane warp and exchanges values by
+// shuffles; with one matrix per lane on 64-wide wavefronts there is nothing to
+// exchange). Convergence test: after iteration k the columns sum to 1 by
+// construction (up to rounding), and row i sums to 2^(f_i + m_i) * s_i where
+// (m_i, s_i) is the max / shifted sum that the next f update needs anyway, so
+// the test costs one exp2 per row and no extra pass over the matrix.
+#include "ot_internal.h"
+
+#include <math.h>
+
+namespace otsk {
+
+namespace {
+
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// max-subtracted base-2 log-sum-exp of 4 values: returns m, writes s = sum 2^(v-m)
+__device__ __forceinline__ float lse4_parts(float v0, float v1, float v2, float v3, float &s) {
+    const float m = fmaxf(fmaxf(v0, v1), fmaxf(v2, v3));
+    s = (hw_exp2(v0 - m) + hw_exp2(v1 - m)) + (hw_exp2(v2 - m) + hw_exp2(v3 - m));
+    return m;
+}
+
+__global__ __launch_bounds__(256) void birkhoff4_kernel(const float *logits, int64_t batch,
+                                                        float scale, int max_iters, float tol,
+                                                        float *out, int32_t *iters_out) {
+    const int64_t bi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (bi >= batch)
+        return;
+    const float4 *src = reinterpret_cast<const float4 *>(logits) + 4 * bi;
+    float l[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float4 v = src[r];
+        l[r][0] = v.x * scale;
+        l[r][1] = v.y * scale;
+        l[r][2] = v.z * scale;
+        l[r][3] = v.w * scale;
+    }
+    float f[4] = {0.f, 0.f, 0.f, 0.f};
+    float g[4] = {0.f, 0.f, 0.f, 0.f};
+    int k = 0;
+    if (max_iters > 0) {
+        const bool check = tol >= 0.f;
+        float m[4], s[4];
+        // first f update (from g = 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            m[i] = lse4_parts(l[i][0], l[i][1], l[i][2], l[i][3], s[i]);
+            f[i] = -(m[i] + hw_log2(s[i]));
+        }
+        for (k = 1;; ++k) {
+            // g update from the current f: iterate k is complete afterwards
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float sj;
+                const float mj = lse4_parts(f[0] + l[0][j], f[1] + l[1][j], f[2] + l[2][j],
+                                            f[3] + l[3][j], sj);
+                g[j] = -(mj + hw_log2(sj));
+            }
+            if (k >= max_iters)
+                break;
+            // the next f update's row statistics
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                m[i] = lse4_parts(g[0] + l[i][0], g[1] + l[i][1], g[2] + l[i][2], g[3] + l[i][3],
+                                  s[i]);
+            if (check) {
+                float err = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    err = fmaxf(err, fabsf(hw_exp2(f[i] + m[i]) * s[i] - 1.f));
+                if (err <= tol)
+                    break;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                f[i] = -(m[i] + hw_log2(s[i]));
+        }
+    }
+    float4 *dst = reinterpret_cast<float4 *>(out) + 4 * bi;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float4 v;
+        v.x = hw_exp2(f[r] + g[0] + l[r][0]);
+        v.y = hw_exp2(f[r] + g[1] + l[r][1]);
+        v.z = hw_exp2(f[r] + g[2] + l[r][2]);
+        v.w = hw_exp2(f[r] + g[3] + l[r][3]);
+        dst[r] = v;
+    }
+    if (iters_out)
+        iters_out[bi] = k;
+}
+
+}  // namespace
+
+hipError_t launch_birkhoff4(const float *logits, int64_t batch, float eps, int max_iters, float tol,
+                            float *out, int32_t *iters_out, hipStream_t s) {
+    if (batch == 0)
+        return hipSuccess;
+    const float scale = (float)(kLog2e / (double)eps);
+    const unsigned blocks = (unsigned)((batch + 255) / 256);
+    hipLaunchKernelGGL(birkhoff4_kernel, dim3(blocks), dim3(256), 0, s, logits, batch, scale,
+                       max_iters, tol, out, iters_out);
+    return hipGetLastError();
+}
+
+}  // namespace otsk

@@ -1,0 +1,82 @@
+// Internal declarations shared by the host code and the kernels of the
+// gfx950 log-domain Sinkhorn library. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace otsk {
+
+// Bias of padding records. Finite on purpose: with -inf, an all-padding
+// chunk would give (-inf) - (-inf) = NaN in the running-max update.
+constexpr float kPadBias = -1.0e30f;
+
+// Every side's record array is padded to a multiple of this many points, so
+// the column loops of all kernels run over whole tiles with no tail code.
+constexpr int kPointPad = 256;
+
+// log2(e) and ln(2).
+constexpr double kLog2e = 1.4426950408889634074;
+constexpr double kLn2 = 0.69314718055994530942;
+
+// How one side of the problem is laid out in device scratch memory.
+//
+// rec[i*rs + k], k < kp : raw coordinate k of point i (zero for k >= d and for
+//                         padding points i >= count)
+// rec[i*rs + kp]        : the point's log2-domain bias ("hat" potential)
+//                         (f_i - |x_i|^2) * log2(e)/eps, kPadBias for padding
+// rec[i*rs + k], k > kp : zero
+struct Layout {
+    int d;        // feature dimension
+    int kp;       // coordinates stored per record (>= d)
+    int rs;       // floats per record (multiple of 4, > kp)
+    bool mfma;    // true: the MFMA kernels; false: the VALU kernels
+};
+
+Layout choose_layout(int d);
+
+inline int64_t pad_points(int64_t count) {
+    return (count + kPointPad - 1) / kPointPad * kPointPad;
+}
+
+// Arguments of one half-step: update the potentials of the "row" side from
+// the records (coordinates + bias) of the "column" side.
+struct HalfStep {
+    const float *row_rec;   // rows' own records (coordinates read)
+    float *row_bias;        // = row_rec: bias slots written (stride rs, offset kp)
+    const float *row_w;     // row weights (count rows)
+    const float *col_rec;   // columns' records (coordinates + bias read)
+    float *pot_out;         // row potentials written (count rows)
+    int64_t rows;           // real row count
+    int64_t cols_pad;       // padded column count (multiple of kPointPad)
+    float scale;            // 2*log2(e)/eps, applied to the rows' coordinates
+    float eps_ln2;          // eps*ln(2)
+    float2 *partials;       // split-column scratch, >= nsplit * rows_pad entries
+    int64_t rows_pad;
+};
+
+// Launch helpers (each returns hipSuccess or the first HIP error).
+hipError_t launch_prep_side(const float *pts, const float *pot, int64_t count, int64_t padded,
+                            const Layout &L, float hat_scale, int bias_mode, float *rec,
+                            hipStream_t s);
+hipError_t launch_half_step_valu(const HalfStep &h, const Layout &L, hipStream_t s);
+hipError_t launch_half_step_mfma(const HalfStep &h, const Layout &L, hipStream_t s);
+size_t half_step_partials(const Layout &L, int64_t rows, int64_t cols_pad);
+size_t half_step_partials_mfma(int64_t rows, int64_t cols_pad);
+hipError_t launch_merge(const HalfStep &h, const Layout &L, int nsplit, hipStream_t s);
+
+// x_rec / y_rec: records whose bias slot holds the raw potential (f or g).
+hipError_t launch_plan_stats(const float *x_rec, const float *y_rec, const float *a, const float *b,
+                             int64_t n, int64_t m, int64_t n_pad, int64_t m_pad, const Layout &L,
+                             float eps, double *cost, double *marg, double *scratch,
+                             hipStream_t s);
+size_t plan_stats_scratch_doubles(const Layout &L, int64_t n, int64_t m, int64_t n_pad,
+                                  int64_t m_pad);
+
+hipError_t launch_birkhoff4(const float *logits, int64_t batch, float eps, int max_iters, float tol,
+                            float *out, int32_t *iters_out, hipStream_t s);
+
+// bias_mode values of launch_prep_side
+enum { kBiasZero = 0, kBiasHat = 1, kBiasRaw = 2 };
+
+}  // namespace otsk

@@ -1,0 +1,111 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares, and rejects invalid arguments before touching the device.
+Only calls that fail host validation are made here (no device is needed)."""
+import ctypes
+import math
+
+import pytest
+
+import log_domain_sinkhorn_amd as lds
+
+INVALID = lds.OT_ERROR_INVALID_VALUE
+UNSUPPORTED = lds.OT_ERROR_NOT_SUPPORTED
+
+# Distinct fake, non-overlapping, 256-byte aligned addresses: never dereferenced
+# because every call below fails validation first.
+X, Y, A, B, F, G, C, MG = (0x10000000 * k for k in range(1, 9))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return lds.load_library()
+
+
+def test_header_declares_expected_functions():
+    assert lds.declared_functions() == sorted([
+        "ot_status_string", "ot_sinkhorn_solve", "ot_sinkhorn_solve_eps_scaling",
+        "ot_plan_stats", "ot_plan_cost", "ot_marginal_error", "ot_birkhoff_project_batched",
+    ])
+
+
+def test_every_declared_function_is_exported(lib):
+    for name in lds.declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_header_max_dim_matches_binding():
+    text = open(lds._HEADER).read()
+    assert f"#define OT_MAX_DIM {lds.OT_MAX_DIM}" in text
+
+
+def test_status_strings(lib):
+    assert lds.ot_status_string(0) == "OT_SUCCESS"
+    assert lds.ot_status_string(INVALID) == "OT_ERROR_INVALID_VALUE"
+    assert lds.ot_status_string(UNSUPPORTED) == "OT_ERROR_NOT_SUPPORTED"
+    assert lds.ot_status_string(3) == "OT_ERROR_OUT_OF_MEMORY"
+    assert lds.ot_status_string(4) == "OT_ERROR_LAUNCH_FAILURE"
+    assert lds.ot_status_string(99) == "OT_ERROR_UNKNOWN"
+
+
+def solve(lib, x=X, y=Y, a=A, b=B, n=10, m=12, d=3, eps=0.1, iters=5, f=F, g=G):
+    return lib.ot_sinkhorn_solve(x, y, a, b, n, m, d, eps, iters, f, g, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(y=None), dict(a=None), dict(b=None), dict(f=None), dict(g=None),
+    dict(n=0), dict(m=0), dict(n=-3), dict(d=0), dict(eps=0.0), dict(eps=-1.0),
+    dict(eps=math.inf), dict(eps=math.nan), dict(iters=-1),
+    dict(f=A), dict(g=X), dict(f=G),            # outputs alias inputs / each other
+])
+def test_solve_rejects_invalid(lib, kw):
+    assert solve(lib, **kw) == INVALID
+
+
+def test_solve_invalid_beats_unsupported(lib):
+    assert solve(lib, d=lds.OT_MAX_DIM + 1, eps=-1.0) == INVALID
+
+
+def test_solve_unsupported_dim(lib):
+    assert solve(lib, d=lds.OT_MAX_DIM + 1) == UNSUPPORTED
+
+
+def test_eps_scaling_rejects_invalid(lib):
+    f = lib.ot_sinkhorn_solve_eps_scaling
+    assert f(X, Y, A, B, 10, 12, 3, 1.0, 0.01, 0, 5, F, G, None) == INVALID   # stages < 1
+    assert f(X, Y, A, B, 10, 12, 3, 1.0, 0.0, 8, 5, F, G, None) == INVALID    # eps_end
+    assert f(X, Y, A, B, 10, 12, 3, math.nan, 0.1, 8, 5, F, G, None) == INVALID
+    assert f(X, Y, A, B, 10, 12, 3, 1.0, 0.1, 8, -1, F, G, None) == INVALID
+    assert f(X, Y, A, B, 10, 12, 129, 1.0, 0.1, 8, 5, F, G, None) == UNSUPPORTED
+
+
+def test_plan_stats_rejects_invalid(lib):
+    ps = lib.ot_plan_stats
+    assert ps(X, Y, A, B, F, G, 10, 12, 3, 0.1, None, None, None) == INVALID   # no output
+    assert ps(X, Y, None, B, F, G, 10, 12, 3, 0.1, None, MG, None) == INVALID  # marg needs a
+    assert ps(X, Y, A, B, None, G, 10, 12, 3, 0.1, C, None, None) == INVALID
+    assert ps(X, Y, A, B, F, G, 10, 12, 3, 0.0, C, None, None) == INVALID
+    assert ps(X, Y, A, B, F, G, 10, 12, 500, 0.1, C, None, None) == UNSUPPORTED
+    assert lib.ot_plan_cost(X, Y, F, G, 10, 12, 3, 0.1, None, None) == INVALID
+    assert lib.ot_marginal_error(X, Y, A, B, F, G, 10, 12, 3, 0.1, None, None) == INVALID
+    assert lib.ot_marginal_error(X, Y, None, B, F, G, 10, 12, 3, 0.1, MG, None) == INVALID
+
+
+def test_birkhoff_rejects_invalid(lib):
+    bp = lib.ot_birkhoff_project_batched
+    assert bp(None, 4, 1.0, 20, -1.0, F, None, None) == INVALID
+    assert bp(X, 4, 1.0, 20, -1.0, None, None, None) == INVALID
+    assert bp(X, -1, 1.0, 20, -1.0, F, None, None) == INVALID
+    assert bp(X, 4, 0.0, 20, -1.0, F, None, None) == INVALID
+    assert bp(X, 4, 1.0, -1, -1.0, F, None, None) == INVALID
+    assert bp(X, 4, 1.0, 20, math.nan, F, None, None) == INVALID
+    assert bp(X + 4, 4, 1.0, 20, -1.0, F, None, None) == INVALID          # misaligned
+    assert bp(X, 4, 1.0, 20, -1.0, X + 64, None, None) == INVALID         # partial overlap
+    assert bp(X, 4, 1.0, 20, -1.0, F, X + 16, None) == INVALID            # counts overlap
+    # batch == 0 is a valid no-op that never touches the device
+    assert bp(X, 0, 1.0, 20, -1.0, F, None, None) == 0
+
+
+def test_solve_zero_iters_is_a_host_noop(lib):
+    # valid arguments with iters == 0 return before any device call
+    assert solve(lib, iters=0) == 0

@@ -1,0 +1,230 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+* Whole solves at sizes the oracle finishes in seconds, spanning several
+  tiles, column splits and ragged tails, at the workloads' eps and iteration
+  counts (the eps-scaling workload with its 8-stage schedule).
+* At the workloads' full sizes (same launch configuration as the benchmark):
+  one f and one g half-step from identical inputs, checked on sampled rows
+  and columns the oracle computes one by one, plus plan statistics.
+* Edge cases: n = 1, m = 1, tiny and odd shapes, d at every kernel boundary,
+  iters = 0, warm starts, determinism.
+
+The update being checked: "FlashSinkhorn: IO-Aware Entropic Optimal Transport
+on GPU", Methodik section 1 (log-domain f/g updates; exact online LSE,
+section 2).
+"""
+import numpy as np
+import pytest
+import torch
+
+import log_domain_sinkhorn_amd as lds
+import oracle
+from workloads import make_clouds, random_clouds
+
+from gpu_helpers import (DEV, TOL_COST, TOL_MARG, TOL_POT, dev, gpu_plan_stats, gpu_solve,
+                         gpu_solve_schedule, rel_inf)
+
+pytestmark = pytest.mark.gpu
+
+# one exact half-step from identical fp32 inputs: fp32 rounding only
+TOL_HALF = 1e-5
+
+
+def _check_solve(c, eps, iters, label):
+    f, g = gpu_solve(c, eps, iters)
+    fo, go = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, iters)
+    ef, eg = rel_inf(f, fo), rel_inf(g, go)
+    print(f"{label}: rel err f {ef:.2e} g {eg:.2e}", flush=True)
+    assert ef <= TOL_POT and eg <= TOL_POT
+    return f, g, fo, go
+
+
+def _check_stats(c, f, g, fo, go, eps, label):
+    st = gpu_plan_stats(c, f, g, eps)
+    so = oracle.plan_stats(c["x"], c["y"], c["a"], c["b"], fo, go, eps)
+    ec = abs(st["cost"] - so["cost"]) / abs(so["cost"])
+    em = abs(st["marg"] - so["marg"])
+    print(f"{label}: cost {st['cost']:.8g} vs {so['cost']:.8g} (rel {ec:.1e}); "
+          f"marg {st['marg']:.3e} vs {so['marg']:.3e} (abs {em:.1e})", flush=True)
+    assert ec <= TOL_COST
+    assert em <= TOL_MARG
+    # the kernel alone: same fp32 (f, g) on both sides
+    sk = oracle.plan_stats(c["x"], c["y"], c["a"], c["b"], f, g, eps)
+    assert abs(st["cost"] - sk["cost"]) <= 1e-6 * abs(sk["cost"])
+    assert abs(st["marg_row"] - sk["marg_row"]) <= 1e-6
+    assert abs(st["marg_col"] - sk["marg_col"]) <= 1e-6
+
+
+# --------------------------------------------------------------------------- #
+# whole solves                                                                  #
+# --------------------------------------------------------------------------- #
+
+def test_gauss3d_1k_full_workload():
+    c = make_clouds("gauss3d_1k")
+    eps, iters = c["eps"][0], c["iters"]
+    f, g, fo, go = _check_solve(c, eps, iters, "gauss3d_1k")
+    _check_stats(c, f, g, fo, go, eps, "gauss3d_1k")
+
+
+@pytest.mark.parametrize("name,n,m", [
+    ("cube_gauss3d_16k", 2048, 2048),
+    ("cube_gauss3d_16k", 3001, 2777),
+    ("feature64_64k", 2048, 2048),
+    ("feature64_64k", 1500, 2600),
+])
+def test_workload_distributions_reduced_size(name, n, m):
+    c = make_clouds(name, n=n, m=m)
+    eps, iters = c["eps"][0], c["iters"]
+    f, g, fo, go = _check_solve(c, eps, iters, f"{name}[{n}x{m}]")
+    _check_stats(c, f, g, fo, go, eps, f"{name}[{n}x{m}]")
+
+
+def test_eps_scaling_schedule_reduced_size():
+    c = make_clouds("mixture_sphere3d_eps_scaling", n=2048, m=1536)
+    eps_list = c["eps"]
+    f, g = gpu_solve_schedule(c, eps_list[0], eps_list[-1], len(eps_list), c["iters"])
+    fo, go = oracle.sinkhorn_schedule(c["x"], c["y"], c["a"], c["b"], eps_list, c["iters"])
+    ef, eg = rel_inf(f, fo), rel_inf(g, go)
+    print(f"mixture schedule: rel err f {ef:.2e} g {eg:.2e}", flush=True)
+    assert ef <= TOL_POT and eg <= TOL_POT
+    _check_stats(c, f, g, fo, go, eps_list[-1], "mixture schedule")
+
+
+SHAPES = [
+    (1, 1, 3), (1, 97, 3), (97, 1, 3), (7, 7, 3), (1023, 777, 3), (129, 4097, 1),
+    (300, 200, 2), (2000, 1500, 5), (5000, 300, 3), (300, 5000, 3), (256, 256, 31),
+    (256, 256, 32), (256, 256, 33), (512, 384, 64), (200, 300, 128), (257, 1000, 48),
+]
+
+
+@pytest.mark.parametrize("n,m,d", SHAPES)
+def test_shapes(n, m, d):
+    c = random_clouds(n, m, d, seed=n * 7 + m * 3 + d)
+    eps = 0.5 * d ** 0.5
+    _check_solve(c, eps, 10, f"shape {n}x{m}x{d}")
+
+
+def test_iters_zero_leaves_potentials():
+    c = random_clouds(100, 80, 3, seed=1)
+    f0 = np.linspace(-1, 1, 100).astype(np.float32)
+    g0 = np.linspace(2, 3, 80).astype(np.float32)
+    f, g = gpu_solve(c, 0.3, 0, g0=g0, f0=f0)
+    np.testing.assert_array_equal(f, f0)
+    np.testing.assert_array_equal(g, g0)
+
+
+def test_warm_start_continues_the_iteration():
+    c = random_clouds(700, 900, 3, seed=2)
+    eps = 0.2
+    f1, g1 = gpu_solve(c, eps, 5)
+    f2, g2 = gpu_solve(c, eps, 7, g0=g1)
+    fo, go = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, 12)
+    assert rel_inf(f2, fo) <= TOL_POT and rel_inf(g2, go) <= TOL_POT
+
+
+def test_warm_start_from_shifted_g():
+    # (f + c, g - c) covariance of the iteration (Birkhoff page, section 2.1)
+    c = random_clouds(600, 500, 3, seed=3)
+    eps, shift = 0.25, 0.75
+    f1, g1 = gpu_solve(c, eps, 6)
+    f2, g2 = gpu_solve(c, eps, 6, g0=np.full(500, -shift, np.float32))
+    np.testing.assert_allclose(f2, f1 + shift, atol=2e-5)
+    np.testing.assert_allclose(g2, g1 - shift, atol=2e-5)
+
+
+@pytest.mark.parametrize("n,m,d", [(1024, 1024, 3), (65536, 4096, 3), (3000, 2000, 64)])
+def test_bitwise_deterministic(n, m, d):
+    c = random_clouds(n, m, d, seed=4)
+    f1, g1 = gpu_solve(c, 0.3, 3)
+    f2, g2 = gpu_solve(c, 0.3, 3)
+    np.testing.assert_array_equal(f1, f2)
+    np.testing.assert_array_equal(g1, g2)
+    s1 = gpu_plan_stats(c, f1, g1, 0.3)
+    s2 = gpu_plan_stats(c, f1, g1, 0.3)
+    assert s1 == s2
+
+
+def test_plan_cost_and_marginal_error_wrappers():
+    c = random_clouds(500, 400, 3, seed=5)
+    f, g = gpu_solve(c, 0.3, 4)
+    st = gpu_plan_stats(c, f, g, 0.3)
+    x, y, a, b = dev(c["x"]), dev(c["y"]), dev(c["a"]), dev(c["b"])
+    ft, gt = dev(f), dev(g)
+    cost = torch.zeros(1, dtype=torch.float64, device=DEV)
+    marg = torch.zeros(2, dtype=torch.float64, device=DEV)
+    lds.ot_plan_cost(x, y, ft, gt, 0.3, cost)
+    lds.ot_marginal_error(x, y, a, b, ft, gt, 0.3, marg)
+    torch.cuda.synchronize()
+    assert cost.item() == st["cost"]
+    assert marg[0].item() == st["marg_row"] and marg[1].item() == st["marg_col"]
+
+
+def test_single_source_point_closed_form_on_gpu():
+    # n = 1: after one iteration P_1j = b_j, so cost = sum_j b_j C_1j and the
+    # column error is zero (closed form, independent of the oracle).
+    rng = np.random.default_rng(6)
+    c = {"x": rng.normal(size=(1, 3)).astype(np.float32),
+         "y": rng.normal(size=(3000, 3)).astype(np.float32)}
+    b = rng.dirichlet(np.ones(3000)).astype(np.float32)
+    c["b"] = b
+    c["a"] = np.array([b.astype(np.float64).sum()], np.float32)
+    f, g = gpu_solve(c, 0.2, 2)
+    st = gpu_plan_stats(c, f, g, 0.2)
+    C1 = ((c["x"].astype(np.float64) - c["y"].astype(np.float64)) ** 2).sum(1)
+    assert st["cost"] == pytest.approx(float(b.astype(np.float64) @ C1), rel=1e-5)
+    assert st["marg_col"] < 1e-5
+
+
+# --------------------------------------------------------------------------- #
+# full sizes: sampled half-steps                                               #
+# --------------------------------------------------------------------------- #
+
+FULL = [("cube_gauss3d_16k", 5), ("feature64_64k", 3), ("cube_gauss3d_64k", 3)]
+
+
+def _sampled_half_steps(c, eps, gK, label, seed=7, k=96):
+    f1, g1 = gpu_solve(c, eps, 1, g0=gK)
+    rng = np.random.default_rng(seed)
+    n, m = c["x"].shape[0], c["y"].shape[0]
+    rows = np.unique(np.concatenate([[0, n - 1], rng.choice(n, k, replace=False)]))
+    cols = np.unique(np.concatenate([[0, m - 1], rng.choice(m, k, replace=False)]))
+    f_ref = oracle.half_update(c["x"], c["y"], c["a"], gK, eps, rows=rows)
+    g_ref = oracle.half_update(c["y"], c["x"], c["b"], f1, eps, rows=cols)
+    ef, eg = rel_inf(f1[rows], f_ref), rel_inf(g1[cols], g_ref)
+    print(f"{label}: sampled half-step rel err f {ef:.2e} g {eg:.2e}", flush=True)
+    assert ef <= TOL_HALF and eg <= TOL_HALF
+    return f1, g1
+
+
+@pytest.mark.parametrize("name,K", FULL)
+def test_full_size_sampled_half_steps(name, K):
+    c = make_clouds(name)
+    eps = c["eps"][0]
+    print(f"{name}: {K} GPU iterations", flush=True)
+    _, gK = gpu_solve(c, eps, K)
+    f1, g1 = _sampled_half_steps(c, eps, gK, name)
+    st = gpu_plan_stats(c, f1, g1, eps)
+    assert np.isfinite(st["cost"]) and st["cost"] > 0
+    assert st["marg_col"] < 1e-4  # the last half-step fixed the column marginal
+
+
+def test_full_size_eps_scaling_then_sampled_half_steps():
+    c = make_clouds("mixture_sphere3d_eps_scaling")
+    e = c["eps"]
+    print("mixture full schedule on GPU", flush=True)
+    f, g = gpu_solve_schedule(c, e[0], e[-1], len(e), c["iters"])
+    assert np.all(np.isfinite(f)) and np.all(np.isfinite(g))
+    _sampled_half_steps(c, e[-1], g, "mixture full")
+
+
+def test_full_size_plan_stats_cube_gauss3d_16k():
+    c = make_clouds("cube_gauss3d_16k")
+    eps = c["eps"][0]
+    f, g = gpu_solve(c, eps, 20)
+    st = gpu_plan_stats(c, f, g, eps)
+    sk = oracle.plan_stats(c["x"], c["y"], c["a"], c["b"], f, g, eps)
+    print(f"16k stats: cost {st['cost']:.10g} vs {sk['cost']:.10g}; marg {st['marg']:.4e} vs "
+          f"{sk['marg']:.4e}", flush=True)
+    assert abs(st["cost"] - sk["cost"]) <= 1e-6 * abs(sk["cost"])
+    assert abs(st["marg_row"] - sk["marg_row"]) <= 1e-6
+    assert abs(st["marg_col"] - sk["marg_col"]) <= 1e-6
