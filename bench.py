@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of the log-domain Sinkhorn hot path on one MI355X.
+
+One step = one whole solve of the workload (cold start, every iteration of
+alternating f/g half-steps) followed by its plan statistics (transport cost
+and marginal errors), on seeded synthetic inputs already resident in HBM.
+The headline workload is the 65536 x 65536 point-cloud problem in d = 64
+(fp32, Dirichlet weights, eps = 0.5, 100 iterations), whose half-steps run on
+the fp32 matrix cores. ``value`` = n*m*iterations*steps / timed seconds.
+
+Printed: one JSON line with the metric, the roofline of the dominant kernel
+(the half-step), the fp64 CPU oracle timed on a bounded sample of the same
+workload on this host's cores, and secondary measurements of the other
+workloads (d = 3 VALU path, eps-scaling schedule, batched 4x4 projection).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       [--no-cpu-baseline] [--no-secondary]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Sinkhorn pair-evals/sec (n·m·iters/s) at n=m=65536 + % of FP32/exp roofline"
+
+# MI355X published peaks used for the roofline fractions.
+PEAK_MFMA_FP32_TFLOPS = 157.3
+# ALU ceiling of the d < 32 half-step, derived from the chip's issue slots
+# (256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz) and the per-pair-side instruction
+# mix of that kernel: kp fp64 FMAs + 1 fp64 add (the score, formed in fp64),
+# 1 f64->f32 convert, 1/2 v_max3_f32, 1 v_exp_f32 and 1 fp32 add. Every
+# instruction takes one issue slot except v_exp_f32, which issues at half
+# rate on gfx950 (measured: 31 vs 59 lane-ops/clk/CU for v_fma_f32; exp and
+# FMA streams do not overlap).
+ISSUE_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
+EXP_SLOTS = 2.0
+
+HALF_STEP_KERNELS = ("lse_rows_mfma_kernel", "lse_rows_valu_kernel")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=1)
+    p.add_argument("--workload", default="feature64_64k")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-secondary", action="store_true")
+    p.add_argument("--secondary-only", default=None,
+                   help="comma list of secondary workloads to run (default: all)")
+    return p.parse_args()
+
+
+def alu_peak_pair_sides(d: int) -> float:
+    """Pair-sides/s ceiling of the VALU half-step for feature dimension d."""
+    kp = (d + 1 + 3) // 4 * 4 - 1
+    slots = kp + 1 + 1 + 0.5 + EXP_SLOTS + 1
+    return ISSUE_SLOTS_PER_S / slots
+
+
+def source_digest(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, only while
+    the kernel source still matches the one the counters were taken on."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{kernel}:{workload}")
+    except (ValueError, OSError):
+        return None
+    if not rec:
+        return None
+    if rec.get("source_digest") != source_digest(rec.get("sources", [])):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Timer:
+    """HIP events on the stream the library launches on (torch's current)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.a.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record()
+
+    def ms(self) -> float:
+        self.b.synchronize()
+        return self.a.elapsed_time(self.b)
+
+
+def run_cloud_workload(name, steps, warmup, torch, lds, with_stats=True):
+    from workloads import make_clouds
+
+    c = make_clouds(name)
+    dev = torch.device("cuda:0")
+    x, y, a, b = (torch.from_numpy(c[k]).to(dev) for k in "xyab")
+    n, m, d = c["n"], c["m"], c["d"]
+    eps_list, iters = c["eps"], c["iters"]
+    f = torch.zeros(n, device=dev)
+    g = torch.zeros(m, device=dev)
+    cost = torch.zeros(1, dtype=torch.float64, device=dev)
+    marg = torch.zeros(2, dtype=torch.float64, device=dev)
+
+    def solve():
+        g.zero_()
+        if len(eps_list) == 1:
+            lds.ot_sinkhorn_solve(x, y, a, b, eps_list[0], iters, f, g)
+        else:
+            lds.ot_sinkhorn_solve_eps_scaling(x, y, a, b, eps_list[0], eps_list[-1],
+                                              len(eps_list), iters, f, g)
+
+    def stats():
+        lds.ot_plan_stats(x, y, a, b, f, g, eps_list[-1], cost, marg)
+
+    for _ in range(warmup):
+        solve()
+        if with_stats:
+            stats()
+    torch.cuda.synchronize()
+    solve_ms, stats_ms = [], []
+    t0 = time.perf_counter()
+    with Timer(torch) as total:
+        for _ in range(steps):
+            with Timer(torch) as ts:
+                solve()
+            solve_ms.append(ts)
+            if with_stats:
+                with Timer(torch) as tp:
+                    stats()
+                stats_ms.append(tp)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = total.ms()
+    solve_ms = [t.ms() for t in solve_ms]
+    stats_ms = [t.ms() for t in stats_ms]
+    total_iters = iters * len(eps_list)
+    half_steps = 2 * total_iters
+    half_ms = sum(solve_ms) / steps / half_steps
+    return {
+        "name": name, "n": n, "m": m, "d": d, "eps": list(eps_list), "iters": iters,
+        "total_iters": total_iters, "steps": steps, "total_ms": total_ms, "wall_s": wall,
+        "ms_per_step": total_ms / steps, "solve_ms": sum(solve_ms) / steps,
+        "stats_ms": (sum(stats_ms) / steps) if stats_ms else None,
+        "half_step_ms": half_ms,
+        "pair_evals_per_s": n * m * total_iters * steps / (total_ms / 1e3),
+        "cost": cost.item(), "marg": marg.cpu().tolist(),
+    }
+
+
+def roofline_for(r, workload):
+    n, m, d = r["n"], r["m"], r["d"]
+    launch_s = r["half_step_ms"] / 1e3
+    if d >= 32:
+        flops = 2.0 * d * n * m  # algorithmic fp32 MFMA flops per half-step launch
+        ach = flops / launch_s / 1e12
+        return {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_FP32_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / PEAK_MFMA_FP32_TFLOPS,
+                "traffic": traffic_for("lse_rows_mfma_kernel", workload),
+                "kernel": "lse_rows_mfma_kernel<64>", "launch_ms": r["half_step_ms"],
+                "work_per_launch": f"{n}*{m} pair-sides x {2 * d} flops"}
+    flops_per_ps = 2 * d + 3
+    ach = flops_per_ps * n * m / launch_s / 1e12
+    peak = alu_peak_pair_sides(d) * flops_per_ps / 1e12
+    return {"bound": "alu", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+            "frac": ach / peak, "traffic": traffic_for("lse_rows_valu_kernel", workload),
+            "kernel": "lse_rows_valu_kernel", "launch_ms": r["half_step_ms"],
+            "work_per_launch": f"{n}*{m} pair-sides x ({flops_per_ps} flops + 1 exp2)"}
+
+
+def cpu_baseline(name):
+    import oracle
+    from workloads import make_clouds
+
+    c = make_clouds(name)
+    ns = min(c["n"], 16384 if c["d"] >= 32 else 32768)
+    ms = min(c["m"], ns)
+    it = 3 if c["d"] >= 32 else 4
+    sub = {"x": c["x"][:ns], "y": c["y"][:ms], "a": c["a"][:ns], "b": c["b"][:ms]}
+    t0 = time.perf_counter()
+    oracle.sinkhorn(sub["x"], sub["y"], sub["a"], sub["b"], c["eps"][0], it)
+    dt = time.perf_counter() - t0
+    return {"value": ns * ms * it / dt, "unit": "pair-evals/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 oracle solve of the first {ns} x {ms} points of {name}, {it} "
+                      f"iterations at eps={c['eps'][0]} ({dt:.1f} s)"}
+
+
+def run_birkhoff(name, torch, lds, reps=5):
+    from workloads import BIRKHOFF_WORKLOADS, make_logits
+
+    w = BIRKHOFF_WORKLOADS[name]
+    L = torch.from_numpy(make_logits(w.batch, w.sigmas, seed=0)).to("cuda:0")
+    out = torch.empty_like(L)
+    it = torch.empty(w.batch, dtype=torch.int32, device=L.device)
+    lds.ot_birkhoff_project_batched(L, w.eps, w.max_iters, w.tol, out, it)
+    torch.cuda.synchronize()
+    with Timer(torch) as t:
+        for _ in range(reps):
+            lds.ot_birkhoff_project_batched(L, w.eps, w.max_iters, w.tol, out, it)
+    ms = t.ms() / reps
+    iters = it.to(torch.int64)
+    issued = int(iters.view(-1, 64).max(dim=1).values.sum().item()) * 64
+    useful = int(iters.sum().item())
+    return {"name": name, "batch": w.batch, "max_iters": w.max_iters, "tol": w.tol,
+            "ms": ms, "matrices_per_s": w.batch / (ms / 1e3),
+            "useful_matrix_iters_per_s": useful / (ms / 1e3),
+            "issued_matrix_iters_per_s": issued / (ms / 1e3),
+            "mean_iters": useful / w.batch,
+            "hbm_gb_per_s": w.batch * (64 + 64 + 4) / (ms / 1e3) / 1e9}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import log_domain_sinkhorn_amd as lds
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    lds.load_library()
+
+    print(f"# headline {args.workload}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
+          flush=True)
+    r = run_cloud_workload(args.workload, args.steps, args.warmup, torch, lds)
+    out = {
+        "metric": METRIC, "value": r["pair_evals_per_s"], "unit": "pair-evals/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "n": r["n"], "m": r["m"], "d": r["d"],
+                   "eps": r["eps"], "iters": r["iters"],
+                   "step": "cold-start solve + plan statistics"},
+        "roofline": roofline_for(r, args.workload),
+        "detail": {"solve_ms": r["solve_ms"], "stats_ms": r["stats_ms"],
+                   "half_step_ms": r["half_step_ms"], "cost": r["cost"], "marg": r["marg"]},
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(args.workload)
+    if not args.no_secondary:
+        sec = {}
+        wanted = None if args.secondary_only is None else set(args.secondary_only.split(","))
+        for name in ("cube_gauss3d_64k", "cube_gauss3d_16k", "mixture_sphere3d_eps_scaling"):
+            if name == args.workload or (wanted is not None and name not in wanted):
+                continue
+            print(f"# secondary {name}", file=sys.stderr, flush=True)
+            s = run_cloud_workload(name, 1, 1, torch, lds)
+            sec[name] = {"pair_evals_per_s": s["pair_evals_per_s"], "ms_per_step": s["ms_per_step"],
+                         "solve_ms": s["solve_ms"], "stats_ms": s["stats_ms"],
+                         "roofline": roofline_for(s, name)}
+        for name in ("birkhoff4x4_1m_fixed20", "birkhoff4x4_1m"):
+            if wanted is not None and name not in wanted:
+                continue
+            print(f"# secondary {name}", file=sys.stderr, flush=True)
+            sec[name] = run_birkhoff(name, torch, lds)
+        out["secondary"] = sec
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -148,9 +148,10 @@ ot_status ot_marginal_error(const float *x, const float *y, const float *a,
  *   eps       > 0 and finite
  *   max_iters >= 0        iteration cap (0 returns exp(L/eps))
  *   tol       < 0: run exactly max_iters iterations;
- *             >= 0: stop a matrix after the first iteration k >= 1 whose plan
- *             has max_i |sum_j out_ij - 1| <= tol (column sums equal 1 up to
- *             rounding after every iteration), or at max_iters.  NaN is invalid.
+ *             >= 0: stop a matrix after the first iteration k >= 1 whose
+ *             plan, as written in fp32, has every row sum and every column
+ *             sum within tol of 1 (evaluated in fp32), or at max_iters.
+ *             NaN is invalid.
  *   out       [batch*16]  result; may alias logits exactly (in place)
  *   iters_out [batch]     nullable; iterations each matrix ran (int32)
  *

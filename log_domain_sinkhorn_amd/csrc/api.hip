@@ -17,12 +17,14 @@ Layout choose_layout(int d) {
         L.kp = (d + 1 + 3) / 4 * 4 - 1;
         L.rs = L.kp + 1;
         L.mfma = false;
+        L.f64 = true;
     } else {
         // MFMA kernels: coordinates padded to a multiple of 16 (each lane
         // half reads KP/2 floats as whole float4s); bias at KP; stride KP + 4.
         L.kp = (d + 15) / 16 * 16;
         L.rs = L.kp + 4;
         L.mfma = true;
+        L.f64 = false;
     }
     return L;
 }
@@ -90,30 +92,30 @@ ot_status run_schedule(const float *x, const float *y, const float *a, const flo
         L.mfma ? half_step_partials_mfma(m, n_pad) : half_step_partials(L, m, n_pad);
     if (part2 > part)
         part = part2;
-    const size_t xb = align_up((size_t)n_pad * L.rs * sizeof(float), 256);
-    const size_t yb = align_up((size_t)m_pad * L.rs * sizeof(float), 256);
-    const size_t pb = part * sizeof(float2);
+    const size_t xb = align_up((size_t)n_pad * L.record_bytes(), 256);
+    const size_t yb = align_up((size_t)m_pad * L.record_bytes(), 256);
+    const size_t pb = part * sizeof(Partial);
     Scratch sc(s);
     hipError_t e = sc.alloc(xb + yb + pb);
     if (e != hipSuccess)
         return map_error(e);
-    float *xrec = static_cast<float *>(sc.ptr);
-    float *yrec = reinterpret_cast<float *>(static_cast<char *>(sc.ptr) + xb);
-    float2 *partials = reinterpret_cast<float2 *>(static_cast<char *>(sc.ptr) + xb + yb);
+    void *xrec = sc.ptr;
+    void *yrec = static_cast<char *>(sc.ptr) + xb;
+    Partial *partials = reinterpret_cast<Partial *>(static_cast<char *>(sc.ptr) + xb + yb);
 
-    if ((e = launch_prep_side(x, nullptr, n, n_pad, L, 0.f, kBiasZero, xrec, s)) != hipSuccess)
+    if ((e = launch_prep_side(x, nullptr, n, n_pad, L, 0.0, kBiasZero, xrec, s)) != hipSuccess)
         return map_error(e);
     for (int st = 0; st < stages; ++st) {
         const double eps = eps_list[st];
-        const float hat_scale = (float)(kLog2e / eps);
+        const double hat_scale = kLog2e / eps;
         // Column bias of the first f update, from the caller's (or the
         // previous stage's) g at this stage's eps.
         if ((e = launch_prep_side(y, g, m, m_pad, L, hat_scale, kBiasHat, yrec, s)) != hipSuccess)
             return map_error(e);
-        HalfStep hf{xrec, xrec, a, yrec, f, n, m_pad, (float)(2.0 * kLog2e / eps),
-                    (float)(eps * kLn2), partials, n_pad};
-        HalfStep hg{yrec, yrec, b, xrec, g, m, n_pad, (float)(2.0 * kLog2e / eps),
-                    (float)(eps * kLn2), partials, m_pad};
+        HalfStep hf{xrec, xrec, a, yrec, f, n, m_pad, 2.0 * kLog2e / eps, eps * kLn2, partials,
+                    n_pad};
+        HalfStep hg{yrec, yrec, b, xrec, g, m, n_pad, 2.0 * kLog2e / eps, eps * kLn2, partials,
+                    m_pad};
         for (int it = 0; it < iters; ++it) {
             e = L.mfma ? launch_half_step_mfma(hf, L, s) : launch_half_step_valu(hf, L, s);
             if (e != hipSuccess)
@@ -208,10 +210,12 @@ ot_status ot_plan_stats(const float *x, const float *y, const float *a, const fl
     if (st != OT_SUCCESS)
         return st;
     hipStream_t s = (hipStream_t)stream;
-    const Layout L = choose_layout(d);
+    // The statistics passes read fp32 records (raw potentials in the bias slot).
+    Layout L = choose_layout(d);
+    L.f64 = false;
     const int64_t n_pad = pad_points(n), m_pad = pad_points(m);
-    const size_t xb = align_up((size_t)n_pad * L.rs * sizeof(float), 256);
-    const size_t yb = align_up((size_t)m_pad * L.rs * sizeof(float), 256);
+    const size_t xb = align_up((size_t)n_pad * L.record_bytes(), 256);
+    const size_t yb = align_up((size_t)m_pad * L.record_bytes(), 256);
     const size_t db = plan_stats_scratch_doubles(L, n, m, n_pad, m_pad) * sizeof(double);
     Scratch sc(s);
     hipError_t e = sc.alloc(xb + yb + db);
@@ -220,9 +224,9 @@ ot_status ot_plan_stats(const float *x, const float *y, const float *a, const fl
     float *xrec = static_cast<float *>(sc.ptr);
     float *yrec = reinterpret_cast<float *>(static_cast<char *>(sc.ptr) + xb);
     double *dsc = reinterpret_cast<double *>(static_cast<char *>(sc.ptr) + xb + yb);
-    if ((e = launch_prep_side(x, f, n, n_pad, L, 0.f, kBiasRaw, xrec, s)) != hipSuccess)
+    if ((e = launch_prep_side(x, f, n, n_pad, L, 0.0, kBiasRaw, xrec, s)) != hipSuccess)
         return map_error(e);
-    if ((e = launch_prep_side(y, g, m, m_pad, L, 0.f, kBiasRaw, yrec, s)) != hipSuccess)
+    if ((e = launch_prep_side(y, g, m, m_pad, L, 0.0, kBiasRaw, yrec, s)) != hipSuccess)
         return map_error(e);
     e = launch_plan_stats(xrec, yrec, a, b, n, m, n_pad, m_pad, L, eps, cost, marg, dsc, s);
     return map_error(e);

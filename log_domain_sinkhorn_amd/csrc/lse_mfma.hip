@@ -65,12 +65,14 @@ __global__ __launch_bounds__(kThreads) void lse_rows_mfma_kernel(HalfStep h, int
     const int tend = min(tbeg + tiles_per_split, ntiles);
 
     // Stationary B operands: this lane's half of its row's scaled coordinates.
+    const float scale = (float)h.scale;
     const int64_t i = (int64_t)blockIdx.x * kRowsPerBlock + wave * 32 + li;
     const int64_t ic = i < h.rows ? i : h.rows - 1;
     float bx[KH];
     float nrm_half = 0.f;
     {
-        const float4 *p = reinterpret_cast<const float4 *>(h.row_rec + ic * RS + hl * KH);
+        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(h.row_rec) +
+                                                         ic * RS + hl * KH);
 #pragma unroll
         for (int q = 0; q < KH / 4; ++q) {
             const float4 v = p[q];
@@ -78,14 +80,14 @@ __global__ __launch_bounds__(kThreads) void lse_rows_mfma_kernel(HalfStep h, int
             nrm_half = fmaf(v.y, v.y, nrm_half);
             nrm_half = fmaf(v.z, v.z, nrm_half);
             nrm_half = fmaf(v.w, v.w, nrm_half);
-            bx[4 * q + 0] = v.x * h.scale;
-            bx[4 * q + 1] = v.y * h.scale;
-            bx[4 * q + 2] = v.z * h.scale;
-            bx[4 * q + 3] = v.w * h.scale;
+            bx[4 * q + 0] = v.x * scale;
+            bx[4 * q + 1] = v.y * scale;
+            bx[4 * q + 2] = v.z * scale;
+            bx[4 * q + 3] = v.w * scale;
         }
     }
 
-    const float4 *col4 = reinterpret_cast<const float4 *>(h.col_rec);
+    const float4 *col4 = static_cast<const float4 *>(h.col_rec);
     float M = -INFINITY;
     float S = 0.f;
 
@@ -178,10 +180,10 @@ __global__ __launch_bounds__(kThreads) void lse_rows_mfma_kernel(HalfStep h, int
         if (gridDim.y == 1) {
             const float lse = Mm + hw_log2(Sm);
             const float hat = log2f(h.row_w[i]) - lse;
-            h.row_bias[i * RS + KP] = hat;
-            h.pot_out[i] = fmaf(h.eps_ln2, hat, nrm);
+            static_cast<float *>(h.row_bias)[i * RS + KP] = hat;
+            h.pot_out[i] = fmaf((float)h.eps_ln2, hat, nrm);
         } else {
-            h.partials[(int64_t)split * h.rows_pad + i] = make_float2(Mm, Sm);
+            h.partials[(int64_t)split * h.rows_pad + i] = Partial{(double)Mm, Sm, 0.f};
         }
     }
 }

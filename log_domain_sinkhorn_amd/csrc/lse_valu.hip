@@ -18,17 +18,27 @@
 // which is pot_i = eps*log w_i - eps*LSE_j((pot_j - C_ij)/eps) with
 // C_ij = |p_i|^2 + |q_j|^2 - 2 p_i.q_j; the |p_i|^2 term leaves the sum.
 //
+// Precision: the score cancels terms of size (2/eps)|p||q| down to the few
+// units that matter, so in fp32 its rounding error grows like 1/eps (about
+// 3e-5 log2 units per term at eps = 0.01 with unit-size clouds). The score
+// is therefore formed in fp64 -- d fp64 FMAs plus one fp64 add, which issue
+// at the same rate as their fp32 forms on gfx950 -- relative to the row's
+// running maximum, then rounded once to fp32 for v_exp_f32 and the fp32
+// sums. The biases (the iteration state) are kept in fp64.
+//
 // Mapping onto the hardware:
-//  * each lane owns R rows (their scaled coordinates, running max M and
+//  * each lane owns R rows (their scaled fp64 coordinates, running max M and
 //    running sum S live in VGPRs for the whole column sweep);
 //  * a 256-lane workgroup streams column records through a double-buffered
-//    LDS tile (one coalesced 16-byte load per lane per tile, one barrier per
-//    tile); every lane of a wave reads the same record, so the LDS read is a
-//    conflict-free broadcast;
-//  * per chunk of T columns: the scores, one max per row, a rescale only when
-//    the chunk maximum exceeds M by more than 64 (so every term stays below
-//    2^64 and the sum cannot overflow), then exp2 and a chunk-local sum that
-//    is added to S (blocked summation);
+//    LDS tile (coalesced 16-byte loads, one barrier per tile); every lane of a
+//    wave reads the same record, so LDS reads are conflict-free broadcasts;
+//  * per chunk of T columns: the T shifted scores u = s - M per row, their
+//    maximum (v_max3_f32), and only when some lane's chunk maximum exceeds
+//    kLazy a wave-uniform rescale branch (M moves up, S is scaled down, the
+//    chunk is recomputed against the new M); every term therefore stays below
+//    2^kLazy, the sum cannot overflow, and the common path is
+//    fp64 FMAs + cvt + exp2 + add;
+//  * blocked summation: each chunk is summed locally and then added to S;
 //  * when the columns are split over several workgroups (grid.y > 1) each
 //    writes its (M, S) pair and a merge kernel combines them in split order.
 // No atomics: the result is bitwise reproducible.
@@ -41,171 +51,215 @@ namespace otsk {
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Largest shifted score a term may have before the row's maximum is moved.
+constexpr float kLazy = 8.0f;
+
 // --------------------------------------------------------------------------
 // Record preparation: copy coordinates (zero padded to kp), write the bias.
 // --------------------------------------------------------------------------
+template <typename E>
 __global__ __launch_bounds__(256) void prep_side_kernel(const float *__restrict__ pts,
                                                         const float *__restrict__ pot, int64_t count,
                                                         int64_t padded, int d, int kp, int rs,
-                                                        float hat_scale, int bias_mode,
-                                                        float *__restrict__ rec) {
+                                                        double hat_scale, int bias_mode,
+                                                        E *__restrict__ rec) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= padded)
         return;
-    float *r = rec + i * rs;
+    E *r = rec + i * rs;
     if (i < count) {
-        float nrm = 0.f;
+        double nrm = 0.0;
         for (int k = 0; k < kp; ++k) {
             const float v = k < d ? pts[i * d + k] : 0.f;
-            r[k] = v;
-            nrm = fmaf(v, v, nrm);
+            r[k] = (E)v;
+            nrm = fma((double)v, (double)v, nrm);
         }
-        float bias = 0.f;
+        double bias = 0.0;
         if (bias_mode == kBiasHat)
-            bias = (pot[i] - nrm) * hat_scale;
+            bias = ((double)pot[i] - nrm) * hat_scale;
         else if (bias_mode == kBiasRaw)
             bias = pot[i];
-        r[kp] = bias;
+        r[kp] = (E)bias;
     } else {
         for (int k = 0; k < kp; ++k)
-            r[k] = 0.f;
-        r[kp] = kPadBias;
+            r[k] = (E)0;
+        r[kp] = (E)kPadBias;
     }
     for (int k = kp + 1; k < rs; ++k)
-        r[k] = 0.f;
+        r[k] = (E)0;
 }
 
 hipError_t launch_prep_side(const float *pts, const float *pot, int64_t count, int64_t padded,
-                            const Layout &L, float hat_scale, int bias_mode, float *rec,
+                            const Layout &L, double hat_scale, int bias_mode, void *rec,
                             hipStream_t s) {
     const unsigned blocks = (unsigned)((padded + 255) / 256);
-    hipLaunchKernelGGL(prep_side_kernel, dim3(blocks), dim3(256), 0, s, pts, pot, count, padded,
-                       L.d, L.kp, L.rs, hat_scale, bias_mode, rec);
+    if (L.f64)
+        hipLaunchKernelGGL(prep_side_kernel<double>, dim3(blocks), dim3(256), 0, s, pts, pot,
+                           count, padded, L.d, L.kp, L.rs, hat_scale, bias_mode,
+                           static_cast<double *>(rec));
+    else
+        hipLaunchKernelGGL(prep_side_kernel<float>, dim3(blocks), dim3(256), 0, s, pts, pot,
+                           count, padded, L.d, L.kp, L.rs, hat_scale, bias_mode,
+                           static_cast<float *>(rec));
     return hipGetLastError();
 }
 
 // --------------------------------------------------------------------------
-// Epilogue shared by the one-pass kernels and the merge: from the final
-// (M, S) of row i write its bias slot and its potential.
+// Epilogue shared by the one-pass kernel and the merge: from the final
+// (M, S) of row i write its fp64 bias slot and its potential.
 // --------------------------------------------------------------------------
-__device__ __forceinline__ void finish_row(const HalfStep &h, int kp, int rs, int64_t i, float M,
-                                           float S, float nrm) {
-    const float lse = M + hw_log2(S);
-    const float hat = log2f(h.row_w[i]) - lse;
-    h.row_bias[i * rs + kp] = hat;
-    h.pot_out[i] = fmaf(h.eps_ln2, hat, nrm);
+__device__ __forceinline__ void finish_row_f64(const HalfStep &h, int kp, int rs, int64_t i,
+                                               double M, float S, double nrm) {
+    const double lse = M + (double)hw_log2(S);
+    const double hat = log2((double)h.row_w[i]) - lse;
+    static_cast<double *>(h.row_bias)[i * rs + kp] = hat;
+    h.pot_out[i] = (float)fma(h.eps_ln2, hat, nrm);
 }
 
 // --------------------------------------------------------------------------
-// The tiled half-step. KP coordinates per record (RS = KP + 1 floats),
+// The tiled half-step. KP coordinates per record (RS = KP + 1 doubles),
 // R rows per lane, TJ columns per LDS tile.
 // --------------------------------------------------------------------------
 template <int KP, int R, int TJ>
 __global__ __launch_bounds__(256) void lse_rows_valu_kernel(HalfStep h, int tiles_per_split,
                                                             int ntiles) {
     constexpr int RS = KP + 1;
-    static_assert(RS % 4 == 0, "record stride must be a multiple of 4 floats");
-    constexpr int RS4 = RS / 4;
-    constexpr int TILE4 = TJ * RS4;
-    constexpr int PF = (TILE4 + 255) / 256;
-    constexpr int T = 8;
+    static_assert(RS % 4 == 0, "record stride must be a multiple of 4 elements");
+    constexpr int RS2 = RS / 2;          // 16-byte words per record
+    constexpr int TILE2 = TJ * RS2;
+    constexpr int PF = (TILE2 + 255) / 256;
+    // Columns per chunk: the chunk's records are held in VGPRs, so longer
+    // records get shorter chunks.
+    constexpr int T = RS <= 4 ? 8 : (RS <= 8 ? 4 : (RS <= 16 ? 2 : 1));
     static_assert(TJ % T == 0, "tile must hold whole chunks");
-    __shared__ float4 lds[2][TILE4];
+    __shared__ double2 lds[2][TILE2];
 
     const int tid = threadIdx.x;
     const int64_t row0 = (int64_t)blockIdx.x * (256 * R);
     const int split = blockIdx.y;
     const int tbeg = split * tiles_per_split;
     const int tend = min(tbeg + tiles_per_split, ntiles);
+    const double *row_rec = static_cast<const double *>(h.row_rec);
+    const double2 *col2 = static_cast<const double2 *>(h.col_rec);
 
-    float xs[R][KP];
-    float nrm[R], M[R], S[R];
+    double xs[R][KP];
+    double nrm[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         int64_t i = row0 + tid + r * 256;
         i = i < h.rows ? i : h.rows - 1;
-        const float *p = h.row_rec + i * RS;
-        float q = 0.f;
+        const double *p = row_rec + i * RS;
+        double q = 0.0;
 #pragma unroll
         for (int k = 0; k < KP; ++k) {
-            const float v = p[k];
-            q = fmaf(v, v, q);
+            const double v = p[k];
+            q = fma(v, v, q);
             xs[r][k] = v * h.scale;
         }
         nrm[r] = q;
-        M[r] = -INFINITY;
-        S[r] = 0.f;
     }
 
-    const float4 *col4 = reinterpret_cast<const float4 *>(h.col_rec);
 #pragma unroll
     for (int q = 0; q < PF; ++q) {
         const int idx = tid + q * 256;
-        if (TILE4 % 256 == 0 || idx < TILE4)
-            lds[0][idx] = col4[(int64_t)tbeg * TILE4 + idx];
+        if (TILE2 % 256 == 0 || idx < TILE2)
+            lds[0][idx] = col2[(int64_t)tbeg * TILE2 + idx];
     }
     __syncthreads();
+
+    // Start every row's maximum at its score against the split's first
+    // column, so M is finite from the start.
+    double M[R];
+    float S[R];
+    {
+        const double *rec = reinterpret_cast<const double *>(lds[0]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            double acc = rec[KP];
+#pragma unroll
+            for (int k = KP - 1; k >= 0; --k)
+                acc = fma(xs[r][k], rec[k], acc);
+            M[r] = acc;
+            S[r] = 0.f;
+        }
+    }
+
     for (int t = tbeg; t < tend; ++t) {
         const int b = (t - tbeg) & 1;
         // Next tile (the last iteration reloads its own tile; the copy into
         // the idle buffer is then unused). Unconditional, so the prefetch
         // stays in registers.
         const int tn = t + 1 < tend ? t + 1 : t;
-        float4 pre[PF];
-        {
+        double2 pre[PF];
 #pragma unroll
-            for (int q = 0; q < PF; ++q) {
-                const int idx = min(tid + q * 256, TILE4 - 1);
-                pre[q] = col4[(int64_t)tn * TILE4 + idx];
-            }
+        for (int q = 0; q < PF; ++q) {
+            const int idx = min(tid + q * 256, TILE2 - 1);
+            pre[q] = col2[(int64_t)tn * TILE2 + idx];
         }
-        const float4 *tile = lds[b];
+        const double *tile = reinterpret_cast<const double *>(lds[b]);
         for (int c0 = 0; c0 < TJ; c0 += T) {
-            float s[R][T];
+            float u[R][T];
 #pragma unroll
-            for (int u = 0; u < T; ++u) {
-                float rec[RS];
-#pragma unroll
-                for (int q = 0; q < RS4; ++q) {
-                    const float4 v = tile[(c0 + u) * RS4 + q];
-                    rec[4 * q + 0] = v.x;
-                    rec[4 * q + 1] = v.y;
-                    rec[4 * q + 2] = v.z;
-                    rec[4 * q + 3] = v.w;
-                }
+            for (int v = 0; v < T; ++v) {
+                const double *rec = tile + (c0 + v) * RS;
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    float acc = rec[KP];
+                    double acc = rec[KP] - M[r];
 #pragma unroll
                     for (int k = KP - 1; k >= 0; --k)
-                        acc = fmaf(xs[r][k], rec[k], acc);
-                    s[r][u] = acc;
+                        acc = fma(xs[r][k], rec[k], acc);
+                    u[r][v] = (float)acc;
+                }
+            }
+            float mx[R];
+            bool need = false;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float m = u[r][0];
+#pragma unroll
+                for (int v = 1; v < T; ++v)
+                    m = fmaxf(m, u[r][v]);
+                mx[r] = m;
+                need |= m > kLazy;
+            }
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                // Rare: move the maximum up and recompute this chunk in fp64
+                // against it, so no precision is lost on the rescaled terms.
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if (mx[r] > kLazy) {
+                        const double Mn = M[r] + (double)mx[r];
+                        S[r] *= hw_exp2((float)(M[r] - Mn));
+                        M[r] = Mn;
+                    }
+                }
+#pragma unroll
+                for (int v = 0; v < T; ++v) {
+                    const double *rec = tile + (c0 + v) * RS;
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        double acc = rec[KP] - M[r];
+#pragma unroll
+                        for (int k = KP - 1; k >= 0; --k)
+                            acc = fma(xs[r][k], rec[k], acc);
+                        u[r][v] = (float)acc;
+                    }
                 }
             }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                float mx = s[r][0];
-#pragma unroll
-                for (int u = 1; u < T; ++u)
-                    mx = fmaxf(mx, s[r][u]);
-                if (mx > M[r] + 64.f) {
-                    S[r] *= hw_exp2(M[r] - mx);
-                    M[r] = mx;
-                }
                 float c = 0.f;
 #pragma unroll
-                for (int u = 0; u < T; ++u)
-                    c += hw_exp2(s[r][u] - M[r]);
+                for (int v = 0; v < T; ++v)
+                    c += hw_exp2(u[r][v]);
                 S[r] += c;
             }
         }
-        {
 #pragma unroll
-            for (int q = 0; q < PF; ++q) {
-                const int idx = tid + q * 256;
-                if (TILE4 % 256 == 0 || idx < TILE4)
-                    lds[b ^ 1][idx] = pre[q];
-            }
+        for (int q = 0; q < PF; ++q) {
+            const int idx = tid + q * 256;
+            if (TILE2 % 256 == 0 || idx < TILE2)
+                lds[b ^ 1][idx] = pre[q];
         }
         __syncthreads();
     }
@@ -215,36 +269,54 @@ __global__ __launch_bounds__(256) void lse_rows_valu_kernel(HalfStep h, int tile
         const int64_t i = row0 + tid + r * 256;
         if (i < h.rows) {
             if (gridDim.y == 1)
-                finish_row(h, KP, RS, i, M[r], S[r], nrm[r]);
+                finish_row_f64(h, KP, RS, i, M[r], S[r], nrm[r]);
             else
-                h.partials[(int64_t)split * h.rows_pad + i] = make_float2(M[r], S[r]);
+                h.partials[(int64_t)split * h.rows_pad + i] = Partial{M[r], S[r], 0.f};
         }
     }
 }
 
-// Combine the per-split (M, S) pairs of each row in split order.
+// Combine the per-split (M, S) pairs of each row in split order. F64 selects
+// the record element type the bias is written into.
+template <bool F64>
 __global__ __launch_bounds__(256) void lse_merge_kernel(HalfStep h, int nsplit, int kp, int rs) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= h.rows)
         return;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s)
-        M = fmaxf(M, h.partials[(int64_t)s * h.rows_pad + i].x);
+    double M = h.partials[i].m;
+    for (int s = 1; s < nsplit; ++s)
+        M = fmax(M, h.partials[(int64_t)s * h.rows_pad + i].m);
     float S = 0.f;
     for (int s = 0; s < nsplit; ++s) {
-        const float2 p = h.partials[(int64_t)s * h.rows_pad + i];
-        S = fmaf(p.y, hw_exp2(p.x - M), S);
+        const Partial p = h.partials[(int64_t)s * h.rows_pad + i];
+        S = fmaf(p.s, hw_exp2((float)(p.m - M)), S);
     }
-    const float *p = h.row_rec + i * rs;
-    float q = 0.f;
-    for (int k = 0; k < kp; ++k)
-        q = fmaf(p[k], p[k], q);
-    finish_row(h, kp, rs, i, M, S, q);
+    if (F64) {
+        const double *p = static_cast<const double *>(h.row_rec) + i * rs;
+        double q = 0.0;
+        for (int k = 0; k < kp; ++k)
+            q = fma(p[k], p[k], q);
+        finish_row_f64(h, kp, rs, i, M, S, q);
+    } else {
+        const float *p = static_cast<const float *>(h.row_rec) + i * rs;
+        float q = 0.f;
+        for (int k = 0; k < kp; ++k)
+            q = fmaf(p[k], p[k], q);
+        const float lse = (float)M + hw_log2(S);
+        const float hat = log2f(h.row_w[i]) - lse;
+        static_cast<float *>(h.row_bias)[i * rs + kp] = hat;
+        h.pot_out[i] = fmaf((float)h.eps_ln2, hat, q);
+    }
 }
 
 hipError_t launch_merge(const HalfStep &h, const Layout &L, int nsplit, hipStream_t s) {
     const unsigned blocks = (unsigned)((h.rows + 255) / 256);
-    hipLaunchKernelGGL(lse_merge_kernel, dim3(blocks), dim3(256), 0, s, h, nsplit, L.kp, L.rs);
+    if (L.f64)
+        hipLaunchKernelGGL(lse_merge_kernel<true>, dim3(blocks), dim3(256), 0, s, h, nsplit, L.kp,
+                           L.rs);
+    else
+        hipLaunchKernelGGL(lse_merge_kernel<false>, dim3(blocks), dim3(256), 0, s, h, nsplit,
+                           L.kp, L.rs);
     return hipGetLastError();
 }
 
@@ -255,7 +327,8 @@ namespace {
 
 constexpr int kTargetBlocks = 2048;  // 8 waves per SIMD on 256 CUs x 4 SIMDs
 
-int tile_cols(int rs) { return rs <= 8 ? 256 : (rs <= 16 ? 128 : 64); }
+// Columns per LDS tile: 8 KB of fp64 records per buffer.
+constexpr int tile_cols_for(int rs) { return rs <= 4 ? 256 : (rs <= 8 ? 128 : (rs <= 16 ? 64 : 32)); }
 
 struct ValuPlan {
     int R;
@@ -268,9 +341,9 @@ struct ValuPlan {
 
 ValuPlan plan_valu(const Layout &L, int64_t rows, int64_t cols_pad) {
     ValuPlan p;
-    p.TJ = tile_cols(L.rs);
+    p.TJ = tile_cols_for(L.rs);
     p.ntiles = (int)(cols_pad / p.TJ);
-    const int max_r = L.kp <= 7 ? 4 : 2;
+    const int max_r = L.kp <= 3 ? 4 : (L.kp <= 15 ? 2 : 1);
     p.R = 1;
     for (int R = max_r; R >= 1; R /= 2) {
         const int64_t rb = (rows + 256 * R - 1) / (256 * R);
@@ -294,7 +367,7 @@ ValuPlan plan_valu(const Layout &L, int64_t rows, int64_t cols_pad) {
 
 template <int KP, int R>
 hipError_t launch_kr(const HalfStep &h, const ValuPlan &p, hipStream_t s) {
-    constexpr int TJ = (KP + 1) <= 8 ? 256 : ((KP + 1) <= 16 ? 128 : 64);
+    constexpr int TJ = tile_cols_for(KP + 1);
     dim3 grid((unsigned)p.row_blocks, (unsigned)p.nsplit);
     hipLaunchKernelGGL((lse_rows_valu_kernel<KP, R, TJ>), grid, dim3(256), 0, s, h,
                        p.tiles_per_split, p.ntiles);
@@ -305,11 +378,13 @@ template <int KP>
 hipError_t launch_k(const HalfStep &h, const ValuPlan &p, hipStream_t s) {
     switch (p.R) {
     case 4:
-        if constexpr (KP <= 7)
+        if constexpr (KP <= 3)
             return launch_kr<KP, 4>(h, p, s);
         return hipErrorInvalidValue;
     case 2:
-        return launch_kr<KP, 2>(h, p, s);
+        if constexpr (KP <= 15)
+            return launch_kr<KP, 2>(h, p, s);
+        return hipErrorInvalidValue;
     default:
         return launch_kr<KP, 1>(h, p, s);
     }
@@ -318,8 +393,6 @@ hipError_t launch_k(const HalfStep &h, const ValuPlan &p, hipStream_t s) {
 }  // namespace
 
 size_t half_step_partials(const Layout &L, int64_t rows, int64_t cols_pad) {
-    if (L.mfma)
-        return 0;  // sized by the MFMA planner
     const ValuPlan p = plan_valu(L, rows, cols_pad);
     return p.nsplit > 1 ? (size_t)p.nsplit * (size_t)pad_points(rows) : 0;
 }

@@ -19,7 +19,8 @@ constexpr int kPointPad = 256;
 constexpr double kLog2e = 1.4426950408889634074;
 constexpr double kLn2 = 0.69314718055994530942;
 
-// How one side of the problem is laid out in device scratch memory.
+// How one side of the problem is laid out in device scratch memory: one
+// record of rs elements (fp64 when f64, else fp32) per point.
 //
 // rec[i*rs + k], k < kp : raw coordinate k of point i (zero for k >= d and for
 //                         padding points i >= count)
@@ -29,8 +30,18 @@ constexpr double kLn2 = 0.69314718055994530942;
 struct Layout {
     int d;        // feature dimension
     int kp;       // coordinates stored per record (>= d)
-    int rs;       // floats per record (multiple of 4, > kp)
+    int rs;       // elements per record (multiple of 4, > kp)
     bool mfma;    // true: the MFMA kernels; false: the VALU kernels
+    bool f64;     // record elements are fp64 (VALU solve) or fp32
+    size_t record_bytes() const { return (size_t)rs * (f64 ? 8 : 4); }
+};
+
+// Per-split partial of a row's streamed log-sum-exp: running max (log2
+// units) and the sum of 2^(s - m) over the split's columns.
+struct Partial {
+    double m;
+    float s;
+    float pad;
 };
 
 Layout choose_layout(int d);
@@ -42,22 +53,22 @@ inline int64_t pad_points(int64_t count) {
 // Arguments of one half-step: update the potentials of the "row" side from
 // the records (coordinates + bias) of the "column" side.
 struct HalfStep {
-    const float *row_rec;   // rows' own records (coordinates read)
-    float *row_bias;        // = row_rec: bias slots written (stride rs, offset kp)
+    const void *row_rec;    // rows' own records (coordinates read)
+    void *row_bias;         // = row_rec: bias slots written (stride rs, offset kp)
     const float *row_w;     // row weights (count rows)
-    const float *col_rec;   // columns' records (coordinates + bias read)
+    const void *col_rec;    // columns' records (coordinates + bias read)
     float *pot_out;         // row potentials written (count rows)
     int64_t rows;           // real row count
     int64_t cols_pad;       // padded column count (multiple of kPointPad)
-    float scale;            // 2*log2(e)/eps, applied to the rows' coordinates
-    float eps_ln2;          // eps*ln(2)
-    float2 *partials;       // split-column scratch, >= nsplit * rows_pad entries
+    double scale;           // 2*log2(e)/eps, applied to the rows' coordinates
+    double eps_ln2;         // eps*ln(2)
+    Partial *partials;      // split-column scratch, >= nsplit * rows_pad entries
     int64_t rows_pad;
 };
 
 // Launch helpers (each returns hipSuccess or the first HIP error).
 hipError_t launch_prep_side(const float *pts, const float *pot, int64_t count, int64_t padded,
-                            const Layout &L, float hat_scale, int bias_mode, float *rec,
+                            const Layout &L, double hat_scale, int bias_mode, void *rec,
                             hipStream_t s);
 hipError_t launch_half_step_valu(const HalfStep &h, const Layout &L, hipStream_t s);
 hipError_t launch_half_step_mfma(const HalfStep &h, const Layout &L, hipStream_t s);

@@ -24,10 +24,13 @@ def dev(a, dtype=None):
     return t.to(DEV)
 
 
-def rel_inf(v, ref) -> float:
+def rel_inf(v, ref, floor: float = 0.0) -> float:
+    """max|v - ref| / max(max|ref|, floor). The floor (eps for potentials)
+    keeps the measure defined when the reference potential is ~0, e.g. a
+    single target point, where g* is zero up to rounding."""
     v = np.asarray(v, np.float64)
     ref = np.asarray(ref, np.float64)
-    den = np.max(np.abs(ref))
+    den = max(float(np.max(np.abs(ref))) if ref.size else 0.0, floor)
     return float(np.max(np.abs(v - ref)) / (den if den > 0 else 1.0))
 
 

@@ -33,7 +33,7 @@ TOL_HALF = 1e-5
 def _check_solve(c, eps, iters, label):
     f, g = gpu_solve(c, eps, iters)
     fo, go = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, iters)
-    ef, eg = rel_inf(f, fo), rel_inf(g, go)
+    ef, eg = rel_inf(f, fo, eps), rel_inf(g, go, eps)
     print(f"{label}: rel err f {ef:.2e} g {eg:.2e}", flush=True)
     assert ef <= TOL_POT and eg <= TOL_POT
     return f, g, fo, go
