@@ -111,6 +111,19 @@ class Timer:
         return self.a.elapsed_time(self.b)
 
 
+COPY_BYTES = 64 << 20
+
+
+def calibration_copy(torch):
+    """One plain device-to-device copy of COPY_BYTES: the reference kernel that
+    scales the FETCH_SIZE / WRITE_SIZE counters of a profiled run."""
+    src = torch.ones(COPY_BYTES // 4, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    return COPY_BYTES
+
+
 def run_cloud_workload(name, steps, warmup, torch, lds, with_stats=True):
     from workloads import make_clouds
 
@@ -197,7 +210,7 @@ def cpu_baseline(name):
     c = make_clouds(name)
     ns = min(c["n"], 16384 if c["d"] >= 32 else 32768)
     ms = min(c["m"], ns)
-    it = 3 if c["d"] >= 32 else 4
+    it = 10 if c["d"] >= 32 else 4
     sub = {"x": c["x"][:ns], "y": c["y"][:ms], "a": c["a"][:ns], "b": c["b"][:ms]}
     t0 = time.perf_counter()
     oracle.sinkhorn(sub["x"], sub["y"], sub["a"], sub["b"], c["eps"][0], it)
@@ -246,6 +259,7 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     lds.load_library()
+    copy_bytes = calibration_copy(torch)
 
     print(f"# headline {args.workload}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
           flush=True)
@@ -259,7 +273,8 @@ def main():
                    "eps": r["eps"], "iters": r["iters"],
                    "step": "cold-start solve + plan statistics"},
         "roofline": roofline_for(r, args.workload),
-        "detail": {"solve_ms": r["solve_ms"], "stats_ms": r["stats_ms"],
+        "detail": {"calibration_copy_bytes": copy_bytes,
+                   "solve_ms": r["solve_ms"], "stats_ms": r["stats_ms"],
                    "half_step_ms": r["half_step_ms"], "cost": r["cost"], "marg": r["marg"]},
     }
     if not args.no_cpu_baseline:
