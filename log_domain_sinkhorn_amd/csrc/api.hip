@@ -94,28 +94,38 @@ ot_status run_schedule(const float *x, const float *y, const float *a, const flo
         part = part2;
     const size_t xb = align_up((size_t)n_pad * L.record_bytes(), 256);
     const size_t yb = align_up((size_t)m_pad * L.record_bytes(), 256);
-    const size_t pb = part * sizeof(Partial);
+    const size_t pb = align_up(part * sizeof(Partial), 256);
+    // MFMA layout: biases in separate contiguous fp32 arrays.
+    const size_t xbb = L.mfma ? align_up((size_t)n_pad * sizeof(float), 256) : 0;
+    const size_t ybb = L.mfma ? align_up((size_t)m_pad * sizeof(float), 256) : 0;
     Scratch sc(s);
-    hipError_t e = sc.alloc(xb + yb + pb);
+    hipError_t e = sc.alloc(xb + yb + pb + xbb + ybb);
     if (e != hipSuccess)
         return map_error(e);
-    void *xrec = sc.ptr;
-    void *yrec = static_cast<char *>(sc.ptr) + xb;
-    Partial *partials = reinterpret_cast<Partial *>(static_cast<char *>(sc.ptr) + xb + yb);
+    char *base = static_cast<char *>(sc.ptr);
+    void *xrec = base;
+    void *yrec = base + xb;
+    Partial *partials = reinterpret_cast<Partial *>(base + xb + yb);
+    void *xbias = L.mfma ? static_cast<void *>(base + xb + yb + pb) : xrec;
+    void *ybias = L.mfma ? static_cast<void *>(base + xb + yb + pb + xbb) : yrec;
+    const int bstride = L.mfma ? 1 : L.rs;
+    const int boff = L.mfma ? 0 : L.kp;
 
-    if ((e = launch_prep_side(x, nullptr, n, n_pad, L, 0.0, kBiasZero, xrec, s)) != hipSuccess)
+    if ((e = launch_prep_side(x, nullptr, n, n_pad, L, 0.0, kBiasZero, xrec, xbias, bstride, boff,
+                              s)) != hipSuccess)
         return map_error(e);
     for (int st = 0; st < stages; ++st) {
         const double eps = eps_list[st];
         const double hat_scale = kLog2e / eps;
         // Column bias of the first f update, from the caller's (or the
         // previous stage's) g at this stage's eps.
-        if ((e = launch_prep_side(y, g, m, m_pad, L, hat_scale, kBiasHat, yrec, s)) != hipSuccess)
+        if ((e = launch_prep_side(y, g, m, m_pad, L, hat_scale, kBiasHat, yrec, ybias, bstride,
+                                  boff, s)) != hipSuccess)
             return map_error(e);
-        HalfStep hf{xrec, xrec, a, yrec, f, n, m_pad, 2.0 * kLog2e / eps, eps * kLn2, partials,
-                    n_pad};
-        HalfStep hg{yrec, yrec, b, xrec, g, m, n_pad, 2.0 * kLog2e / eps, eps * kLn2, partials,
-                    m_pad};
+        HalfStep hf{xrec, xbias, a, yrec, ybias, bstride, boff, f, n, m_pad,
+                    2.0 * kLog2e / eps, eps * kLn2, partials, n_pad};
+        HalfStep hg{yrec, ybias, b, xrec, xbias, bstride, boff, g, m, n_pad,
+                    2.0 * kLog2e / eps, eps * kLn2, partials, m_pad};
         for (int it = 0; it < iters; ++it) {
             e = L.mfma ? launch_half_step_mfma(hf, L, s) : launch_half_step_valu(hf, L, s);
             if (e != hipSuccess)
@@ -224,9 +234,11 @@ ot_status ot_plan_stats(const float *x, const float *y, const float *a, const fl
     float *xrec = static_cast<float *>(sc.ptr);
     float *yrec = reinterpret_cast<float *>(static_cast<char *>(sc.ptr) + xb);
     double *dsc = reinterpret_cast<double *>(static_cast<char *>(sc.ptr) + xb + yb);
-    if ((e = launch_prep_side(x, f, n, n_pad, L, 0.0, kBiasRaw, xrec, s)) != hipSuccess)
+    if ((e = launch_prep_side(x, f, n, n_pad, L, 0.0, kBiasRaw, xrec, xrec, L.rs, L.kp, s)) !=
+        hipSuccess)
         return map_error(e);
-    if ((e = launch_prep_side(y, g, m, m_pad, L, 0.0, kBiasRaw, yrec, s)) != hipSuccess)
+    if ((e = launch_prep_side(y, g, m, m_pad, L, 0.0, kBiasRaw, yrec, yrec, L.rs, L.kp, s)) !=
+        hipSuccess)
         return map_error(e);
     e = launch_plan_stats(xrec, yrec, a, b, n, m, n_pad, m_pad, L, eps, cost, marg, dsc, s);
     return map_error(e);

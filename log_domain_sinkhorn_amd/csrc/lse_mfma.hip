@@ -20,10 +20,32 @@
 // chain are KP/2 contiguous floats: 16-byte LDS reads and loads.
 //
 // A workgroup of 8 waves owns 256 rows (32 per wave, the B operands stay in
-// VGPRs for the whole sweep) and streams the column records of its split
-// through a double-buffered LDS tile of 64 columns, shared by all 8 waves.
-// Record stride KP + 4 floats rotates LDS banks by 4 per record, so the
+// VGPRs for the whole sweep) and streams the column records and biases of
+// its split through a double-buffered LDS tile of 64 columns, shared by all 8
+// waves. Record stride KP + 4 floats rotates LDS banks by 4 per record, so the
 // per-lane 16-byte operand reads of 32 consecutive records do not conflict.
+//
+// Tiles are copied with gfx950's direct global->LDS loads
+// (global_load_lds_dwordx4 for coordinates, _dword for biases): each wave
+// issues whole chunks for the next tile at the top of an iteration and only
+// waits for them at the tile's barrier, so no VGPRs hold the prefetch and the
+// load latency hides behind a tile's worth of MFMAs.
+//
+// On gfx950 fp32 MFMAs and vector-ALU instructions do not execute
+// concurrently on a SIMD (measured: an MFMA stream plus an FMA or exp2 stream
+// takes the sum of their times, in one wave or spread over several), so a
+// half-step costs MFMA cycles plus epilogue cycles and the epilogue is kept
+// minimal:
+//  * the column bias and the row's running maximum M enter through one extra
+//    MFMA per subtile (k-slot 0: bias_j x 1, k-slot 1: 1 x -M_i) on a zero
+//    accumulator, so the MFMA chain yields u_ji = s_ij - M_i directly;
+//  * M is shared by the two lane halves holding row i and moves lazily: the
+//    common epilogue is one exp2 and one add per value; only when a chunk's
+//    sum leaves [2^-64, 2^16] (a term above 2^16, or no mass yet) does a
+//    wave-uniform branch recompute the row maximum and rescale.
+// The loop is software-pipelined over 32-column subtiles with two
+// accumulators so a subtile's MFMA chain and the previous subtile's epilogue
+// sit in one basic block, interleaved.
 #include "ot_internal.h"
 
 #include <math.h>
@@ -35,13 +57,123 @@ hipError_t launch_merge(const HalfStep &h, const Layout &L, int nsplit, hipStrea
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 constexpr int kThreads = 512;   // 8 waves
+constexpr int kWaves = kThreads / 64;
 constexpr int kRowsPerBlock = 256;
 constexpr int kTileCols = 64;
+// LDS operand of the extra MFMA, per 32-column subtile: 32 column biases
+// (read by lane half 0) followed by 32 ones (read by lane half 1).
+constexpr int kBiasSlots = 2 * kTileCols;
+
+// Start the copy of column tile t into LDS buffers (rec, bias). Coordinates:
+// whole 64-lane chunks of 16 bytes; lane l lands 16 bytes after lane l-1 at
+// the wave-uniform chunk base. Biases: two 32-lane dword loads, one per
+// subtile, each into the first half of that subtile's slot pair.
+template <int TILE4>
+__device__ __forceinline__ void issue_tile(const float4 *__restrict__ col4,
+                                           const float *__restrict__ colb, int t, float4 *rec,
+                                           float *bias, int wave, int lane) {
+    const float4 *src = col4 + (int64_t)t * TILE4;
+#pragma unroll
+    for (int c = 0; c < TILE4 / 64; c += kWaves) {
+        const int chunk = c + wave;
+        if (TILE4 / 64 % kWaves == 0 || chunk < TILE4 / 64)
+            __builtin_amdgcn_global_load_lds(src + chunk * 64 + lane,
+                                             (lds_void *)(rec + chunk * 64), 16, 0, 0);
+    }
+    if (wave >= kWaves - 2 && lane < 32) {
+        const int sub = wave - (kWaves - 2);
+        __builtin_amdgcn_global_load_lds(colb + (int64_t)t * kTileCols + sub * 32 + lane,
+                                         (lds_void *)(bias + sub * 64), 4, 0, 0);
+    }
+}
+
+// u[j][i] = s_ij - Mu_i for the 32 columns of subtile `sub`: the extra MFMA
+// (bias and -Mu) on a zero accumulator, then KP/2 MFMAs over k.
+template <int KP>
+__device__ __forceinline__ floatx16 score_tile(const float4 *rec, const float *bias, int sub,
+                                               int lane, int li, int hl, const float (&bx)[KP / 2],
+                                               float Mu) {
+    constexpr int RS4 = (KP + 4) / 4;
+    constexpr int KH = KP / 2;
+    const floatx16 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
+                           0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const float a0 = bias[sub * 64 + lane];
+    const float b0 = hl ? -Mu : 1.f;
+    floatx16 acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, zero, 0, 0, 0);
+    const float4 *ap = rec + (sub * 32 + li) * RS4 + hl * (KH / 4);
+#pragma unroll
+    for (int q4 = 0; q4 < KH / 4; ++q4) {
+        const float4 av = ap[q4];
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, bx[4 * q4 + 0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, bx[4 * q4 + 1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, bx[4 * q4 + 2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, bx[4 * q4 + 3], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// Common part of the epilogue: the sum of 2^u over the lane's 16 values.
+__device__ __forceinline__ float chunk_sum(const floatx16 &u) {
+    float c0 = hw_exp2(u[0]), c1 = hw_exp2(u[1]);
+#pragma unroll
+    for (int v = 2; v < 16; v += 2) {
+        c0 += hw_exp2(u[v]);
+        c1 += hw_exp2(u[v + 1]);
+    }
+    return c0 + c1;
+}
+
+// Fold a subtile (values u relative to Mu, sum c) into the row's (M, S).
+// Lanes l and l^32 hold the same row and keep the same M.
+__device__ __forceinline__ void fold(const floatx16 &u, float Mu, float c, float &M, float &S) {
+    const bool need = !(c <= 0x1p16f) || !(S + c >= 0x1p-64f) || Mu != M;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+        // Rare (wave-uniform): move M to the larger of this subtile's row
+        // maximum and the mass already accumulated, rescale, recompute c.
+        float mh = u[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v)
+            mh = fmaxf(mh, u[v]);
+        mh = fmaxf(mh + Mu, M + hw_log2(S));
+        const float Mn = fmaxf(mh, __shfl_xor(mh, 32));
+        // S is 0 or >= 2^-64 (the common path only adds when S + c >= 2^-64)
+        // and Mn >= M + log2 S, so the factor stays below 2^64; S = 0 is kept
+        // apart because M may move down by ~1e30 past a padding-only chunk.
+        S = S > 0.f ? S * hw_exp2(M - Mn) : 0.f;
+        const float off = Mn - Mu;
+        float c0 = 0.f, c1 = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+            c0 += hw_exp2(u[v] - off);
+            c1 += hw_exp2(u[v + 1] - off);
+        }
+        c = c0 + c1;
+        M = Mn;
+    }
+    S += c;
+}
+
+// Keep the running (M, S) computed here: the fold above it may not be moved
+// past this point (in particular not past the tile barrier that follows).
+__device__ __forceinline__ void pin(float &M, float &S) { asm volatile("" : "+v"(M), "+v"(S)); }
+
+// Ask the scheduler to alternate one MFMA with one vector-ALU instruction
+// (transcendentals included) for a subtile's MFMA chain, so the previous
+// subtile's exp2 / add work sits between the MFMAs.
+template <int KP>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+    for (int q = 0; q < KP / 2 + 1; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);  // VALU / TRANS
+    }
+}
 
 template <int KP>
 __global__ __launch_bounds__(kThreads) void lse_rows_mfma_kernel(HalfStep h, int tiles_per_split,
@@ -49,11 +181,11 @@ __global__ __launch_bounds__(kThreads) void lse_rows_mfma_kernel(HalfStep h, int
     constexpr int RS = KP + 4;
     constexpr int RS4 = RS / 4;
     constexpr int TILE4 = kTileCols * RS4;
-    constexpr int PF = (TILE4 + kThreads - 1) / kThreads;
     constexpr int KH = KP / 2;
     static_assert(KP % 8 == 0, "each lane half reads whole float4s");
+    static_assert(TILE4 % 64 == 0, "tiles are whole 64-lane chunks");
     __shared__ float4 lrec[2][TILE4];
-    __shared__ float4 lbias[2][kTileCols / 4];
+    __shared__ float lbias[2][kBiasSlots];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -63,16 +195,26 @@ __global__ __launch_bounds__(kThreads) void lse_rows_mfma_kernel(HalfStep h, int
     const int split = blockIdx.y;
     const int tbeg = split * tiles_per_split;
     const int tend = min(tbeg + tiles_per_split, ntiles);
+    const float4 *col4 = static_cast<const float4 *>(h.col_rec);
+    const float *colb = static_cast<const float *>(h.col_bias);
 
-    // Stationary B operands: this lane's half of its row's scaled coordinates.
+    // The ones of the extra MFMA's operand (never overwritten by the copies).
+    if (tid < 2 * kBiasSlots) {
+        const int e = tid % kBiasSlots;
+        if ((e / 32) & 1)
+            lbias[tid / kBiasSlots][e] = 1.f;
+    }
+    // Start the first tile's copy, then load the stationary B operands: this
+    // lane's half of its row's scaled coordinates.
+    issue_tile<TILE4>(col4, colb, tbeg, lrec[0], lbias[0], wave, lane);
     const float scale = (float)h.scale;
     const int64_t i = (int64_t)blockIdx.x * kRowsPerBlock + wave * 32 + li;
     const int64_t ic = i < h.rows ? i : h.rows - 1;
     float bx[KH];
     float nrm_half = 0.f;
     {
-        const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(h.row_rec) +
-                                                         ic * RS + hl * KH);
+        const float4 *p = reinterpret_cast<const float4 *>(
+            static_cast<const float *>(h.row_rec) + ic * RS + hl * KH);
 #pragma unroll
         for (int q = 0; q < KH / 4; ++q) {
             const float4 v = p[q];
@@ -86,104 +228,52 @@ __global__ __launch_bounds__(kThreads) void lse_rows_mfma_kernel(HalfStep h, int
             bx[4 * q + 3] = v.w * scale;
         }
     }
-
-    const float4 *col4 = static_cast<const float4 *>(h.col_rec);
-    float M = -INFINITY;
-    float S = 0.f;
-
-#pragma unroll
-    for (int q = 0; q < PF; ++q) {
-        const int idx = tid + q * kThreads;
-        if (TILE4 % kThreads == 0 || idx < TILE4) {
-            const float4 v = col4[(int64_t)tbeg * TILE4 + idx];
-            lrec[0][idx] = v;
-            const int c = idx / RS4;
-            if (idx - c * RS4 == KP / 4)
-                reinterpret_cast<float *>(lbias[0])[c] = v.x;
-        }
-    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+
+    // Running reference M (shared by the row's two lane halves) and sum S.
+    float M = 0.f;
+    float S = 0.f;
+    float Mu0 = M;
+    floatx16 acc0 = score_tile<KP>(lrec[0], lbias[0], 0, lane, li, hl, bx, Mu0);
     for (int t = tbeg; t < tend; ++t) {
         const int b = (t - tbeg) & 1;
-        // Next tile (the last iteration reloads its own tile; the copy into
-        // the idle buffer is then unused). Unconditional, so the prefetch
-        // stays in registers.
-        const int tn = t + 1 < tend ? t + 1 : t;
-        float4 pre[PF];
-        {
-#pragma unroll
-            for (int q = 0; q < PF; ++q) {
-                const int idx = min(tid + q * kThreads, TILE4 - 1);
-                pre[q] = col4[(int64_t)tn * TILE4 + idx];
-            }
-        }
-#pragma unroll
-        for (int sub = 0; sub < kTileCols / 32; ++sub) {
-            floatx16 acc;
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const float4 bv = lbias[b][sub * 8 + 2 * g4 + hl];
-                acc[4 * g4 + 0] = bv.x;
-                acc[4 * g4 + 1] = bv.y;
-                acc[4 * g4 + 2] = bv.z;
-                acc[4 * g4 + 3] = bv.w;
-            }
-            const float4 *ap = &lrec[b][(sub * 32 + li) * RS4 + hl * (KH / 4)];
-#pragma unroll
-            for (int q4 = 0; q4 < KH / 4; ++q4) {
-                const float4 av = ap[q4];
-                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, bx[4 * q4 + 0], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, bx[4 * q4 + 1], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, bx[4 * q4 + 2], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, bx[4 * q4 + 3], acc, 0, 0, 0);
-            }
-            float mx = acc[0];
-#pragma unroll
-            for (int v = 1; v < 16; ++v)
-                mx = fmaxf(mx, acc[v]);
-            if (mx > M + 64.f) {
-                S *= hw_exp2(M - mx);
-                M = mx;
-            }
-            float c = 0.f;
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                c += hw_exp2(acc[v] - M);
-            S += c;
-        }
-        {
-#pragma unroll
-            for (int q = 0; q < PF; ++q) {
-                const int idx = tid + q * kThreads;
-                if (TILE4 % kThreads == 0 || idx < TILE4) {
-                    lrec[b ^ 1][idx] = pre[q];
-                    const int c = idx / RS4;
-                    if (idx - c * RS4 == KP / 4)
-                        reinterpret_cast<float *>(lbias[b ^ 1])[c] = pre[q].x;
-                }
-            }
-        }
+        if (t + 1 < tend)
+            issue_tile<TILE4>(col4, colb, t + 1, lrec[b ^ 1], lbias[b ^ 1], wave, lane);
+        const float Mu1 = M;
+        const floatx16 acc1 = score_tile<KP>(lrec[b], lbias[b], 1, lane, li, hl, bx, Mu1);
+        const float c0 = chunk_sum(acc0);
+        interleave<KP>();
+        fold(acc0, Mu0, c0, M, S);
+        pin(M, S);
+        // The next tile has landed for every wave, and every wave is done
+        // reading this one.
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        // First subtile of the next tile. On the last iteration this reads
+        // the idle buffer and the result is never folded.
+        Mu0 = M;
+        acc0 = score_tile<KP>(lrec[b ^ 1], lbias[b ^ 1], 0, lane, li, hl, bx, Mu0);
+        const float c1 = chunk_sum(acc1);
+        interleave<KP>();
+        fold(acc1, Mu1, c1, M, S);
+        pin(M, S);
     }
 
-    // Merge the two lane halves (same row i, disjoint columns). Both halves
-    // form the same sums in the same order, so they agree bitwise.
-    const float Mo = __shfl_xor(M, 32);
+    // Merge the two lane halves (same row i, same M, disjoint columns). Both
+    // halves add the same two numbers, so they agree bitwise.
     const float So = __shfl_xor(S, 32);
     const float no = __shfl_xor(nrm_half, 32);
-    const float Mm = fmaxf(M, Mo);
-    const float e0 = S * hw_exp2(M - Mm);
-    const float e1 = So * hw_exp2(Mo - Mm);
-    const float Sm = hl == 0 ? e0 + e1 : e1 + e0;
+    const float Sm = hl == 0 ? S + So : So + S;
     const float nrm = hl == 0 ? nrm_half + no : no + nrm_half;
     if (hl == 0 && i < h.rows) {
         if (gridDim.y == 1) {
-            const float lse = Mm + hw_log2(Sm);
+            const float lse = M + hw_log2(Sm);
             const float hat = log2f(h.row_w[i]) - lse;
-            static_cast<float *>(h.row_bias)[i * RS + KP] = hat;
+            static_cast<float *>(h.row_bias)[i] = hat;
             h.pot_out[i] = fmaf((float)h.eps_ln2, hat, nrm);
         } else {
-            h.partials[(int64_t)split * h.rows_pad + i] = Partial{(double)Mm, Sm, 0.f};
+            h.partials[(int64_t)split * h.rows_pad + i] = Partial{(double)M, Sm, 0.f};
         }
     }
 }

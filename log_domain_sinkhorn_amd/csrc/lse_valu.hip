@@ -61,8 +61,8 @@ template <typename E>
 __global__ __launch_bounds__(256) void prep_side_kernel(const float *__restrict__ pts,
                                                         const float *__restrict__ pot, int64_t count,
                                                         int64_t padded, int d, int kp, int rs,
-                                                        double hat_scale, int bias_mode,
-                                                        E *__restrict__ rec) {
+                                                        double hat_scale, int bias_mode, E *rec,
+                                                        E *bias, int bias_stride, int bias_off) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= padded)
         return;
@@ -74,33 +74,35 @@ __global__ __launch_bounds__(256) void prep_side_kernel(const float *__restrict_
             r[k] = (E)v;
             nrm = fma((double)v, (double)v, nrm);
         }
-        double bias = 0.0;
+        double bv = 0.0;
         if (bias_mode == kBiasHat)
-            bias = ((double)pot[i] - nrm) * hat_scale;
+            bv = ((double)pot[i] - nrm) * hat_scale;
         else if (bias_mode == kBiasRaw)
-            bias = pot[i];
-        r[kp] = (E)bias;
-    } else {
-        for (int k = 0; k < kp; ++k)
+            bv = pot[i];
+        for (int k = kp; k < rs; ++k)
             r[k] = (E)0;
-        r[kp] = (E)kPadBias;
+        bias[i * bias_stride + bias_off] = (E)bv;
+    } else {
+        for (int k = 0; k < rs; ++k)
+            r[k] = (E)0;
+        bias[i * bias_stride + bias_off] = (E)kPadBias;
     }
-    for (int k = kp + 1; k < rs; ++k)
-        r[k] = (E)0;
 }
 
 hipError_t launch_prep_side(const float *pts, const float *pot, int64_t count, int64_t padded,
                             const Layout &L, double hat_scale, int bias_mode, void *rec,
-                            hipStream_t s) {
+                            void *bias, int bias_stride, int bias_off, hipStream_t s) {
     const unsigned blocks = (unsigned)((padded + 255) / 256);
     if (L.f64)
         hipLaunchKernelGGL(prep_side_kernel<double>, dim3(blocks), dim3(256), 0, s, pts, pot,
                            count, padded, L.d, L.kp, L.rs, hat_scale, bias_mode,
-                           static_cast<double *>(rec));
+                           static_cast<double *>(rec), static_cast<double *>(bias), bias_stride,
+                           bias_off);
     else
         hipLaunchKernelGGL(prep_side_kernel<float>, dim3(blocks), dim3(256), 0, s, pts, pot,
                            count, padded, L.d, L.kp, L.rs, hat_scale, bias_mode,
-                           static_cast<float *>(rec));
+                           static_cast<float *>(rec), static_cast<float *>(bias), bias_stride,
+                           bias_off);
     return hipGetLastError();
 }
 
@@ -112,7 +114,7 @@ __device__ __forceinline__ void finish_row_f64(const HalfStep &h, int kp, int rs
                                                double M, float S, double nrm) {
     const double lse = M + (double)hw_log2(S);
     const double hat = log2((double)h.row_w[i]) - lse;
-    static_cast<double *>(h.row_bias)[i * rs + kp] = hat;
+    static_cast<double *>(h.row_bias)[i * h.bias_stride + h.bias_off] = hat;
     h.pot_out[i] = (float)fma(h.eps_ln2, hat, nrm);
 }
 
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(HalfStep h, int nsplit, 
             q = fmaf(p[k], p[k], q);
         const float lse = (float)M + hw_log2(S);
         const float hat = log2f(h.row_w[i]) - lse;
-        static_cast<float *>(h.row_bias)[i * rs + kp] = hat;
+        static_cast<float *>(h.row_bias)[i * h.bias_stride + h.bias_off] = hat;
         h.pot_out[i] = fmaf((float)h.eps_ln2, hat, q);
     }
 }

@@ -51,12 +51,20 @@ inline int64_t pad_points(int64_t count) {
 }
 
 // Arguments of one half-step: update the potentials of the "row" side from
-// the records (coordinates + bias) of the "column" side.
+// the records (coordinates) and biases of the "column" side.
+//
+// Where a side's bias lives: element i*bias_stride + bias_off of its bias
+// base. VALU layout: inside the fp64 record (base = records, stride rs,
+// offset kp). MFMA layout: a separate contiguous fp32 array (stride 1,
+// offset 0), so whole bias tiles load with one instruction.
 struct HalfStep {
     const void *row_rec;    // rows' own records (coordinates read)
-    void *row_bias;         // = row_rec: bias slots written (stride rs, offset kp)
+    void *row_bias;         // rows' bias base: new biases written here
     const float *row_w;     // row weights (count rows)
-    const void *col_rec;    // columns' records (coordinates + bias read)
+    const void *col_rec;    // columns' records (coordinates read)
+    const void *col_bias;   // columns' bias base (read)
+    int bias_stride;        // elements between consecutive points' biases
+    int bias_off;           // offset of a point's bias from its base element
     float *pot_out;         // row potentials written (count rows)
     int64_t rows;           // real row count
     int64_t cols_pad;       // padded column count (multiple of kPointPad)
@@ -67,9 +75,11 @@ struct HalfStep {
 };
 
 // Launch helpers (each returns hipSuccess or the first HIP error).
+// Write the records of one side and its biases (bias of point i at
+// bias[i*bias_stride + bias_off], in the records' element type).
 hipError_t launch_prep_side(const float *pts, const float *pot, int64_t count, int64_t padded,
                             const Layout &L, double hat_scale, int bias_mode, void *rec,
-                            hipStream_t s);
+                            void *bias, int bias_stride, int bias_off, hipStream_t s);
 hipError_t launch_half_step_valu(const HalfStep &h, const Layout &L, hipStream_t s);
 hipError_t launch_half_step_mfma(const HalfStep &h, const Layout &L, hipStream_t s);
 size_t half_step_partials(const Layout &L, int64_t rows, int64_t cols_pad);
