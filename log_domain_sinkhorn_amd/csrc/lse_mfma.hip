@@ -21,7 +21,7 @@
 //
 // A workgroup of 8 waves owns 256 rows (32 per wave, the B operands stay in
 // VGPRs for the whole sweep) and streams the column records and biases of
-// its split through a double-buffered LDS tile of 64 columns, shared by all 8
+// its split through a double-buffered LDS tile of 128 columns, shared by all 8
 // waves. Record stride KP + 4 floats rotates LDS banks by 4 per record, so the
 // per-lane 16-byte operand reads of 32 consecutive records do not conflict.
 //
@@ -45,7 +45,7 @@
 //    wave-uniform branch recompute the row maximum and rescale.
 // The loop is software-pipelined over 32-column subtiles with two
 // accumulators so a subtile's MFMA chain and the previous subtile's epilogue
-// sit in one basic block, interleaved.
+// sit next to each other in one basic block.
 #include "ot_internal.h"
 
 #include <math.h>
@@ -62,10 +62,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-constexpr int kThreads = 512;   // 8 waves
-constexpr int kWaves = kThreads / 64;
-constexpr int kRowsPerBlock = 256;
-constexpr int kTileCols = 64;
+constexpr int kWaves = 8;                 // waves per workgroup, 32 rows each
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerBlock = 32 * kWaves;
+constexpr int kTileCols = 128;            // columns per LDS tile
+constexpr int kSub = kTileCols / 32;      // 32-column subtiles per tile
+static_assert(kSub <= kWaves, "one wave copies each subtile's biases");
 // LDS operand of the extra MFMA, per 32-column subtile: 32 column biases
 // (read by lane half 0) followed by 32 ones (read by lane half 1).
 constexpr int kBiasSlots = 2 * kTileCols;
@@ -86,8 +88,8 @@ __device__ __forceinline__ void issue_tile(const float4 *__restrict__ col4,
             __builtin_amdgcn_global_load_lds(src + chunk * 64 + lane,
                                              (lds_void *)(rec + chunk * 64), 16, 0, 0);
     }
-    if (wave >= kWaves - 2 && lane < 32) {
-        const int sub = wave - (kWaves - 2);
+    if (wave >= kWaves - kSub && lane < 32) {
+        const int sub = wave - (kWaves - kSub);
         __builtin_amdgcn_global_load_lds(colb + (int64_t)t * kTileCols + sub * 32 + lane,
                                          (lds_void *)(bias + sub * 64), 4, 0, 0);
     }
@@ -163,18 +165,6 @@ __device__ __forceinline__ void fold(const floatx16 &u, float Mu, float c, float
 // past this point (in particular not past the tile barrier that follows).
 __device__ __forceinline__ void pin(float &M, float &S) { asm volatile("" : "+v"(M), "+v"(S)); }
 
-// Ask the scheduler to alternate one MFMA with one vector-ALU instruction
-// (transcendentals included) for a subtile's MFMA chain, so the previous
-// subtile's exp2 / add work sits between the MFMAs.
-template <int KP>
-__device__ __forceinline__ void interleave() {
-#pragma unroll
-    for (int q = 0; q < KP / 2 + 1; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);  // VALU / TRANS
-    }
-}
-
 template <int KP>
 __global__ __launch_bounds__(kThreads) void lse_rows_mfma_kernel(HalfStep h, int tiles_per_split,
                                                                  int ntiles) {
@@ -199,10 +189,10 @@ __global__ __launch_bounds__(kThreads) void lse_rows_mfma_kernel(HalfStep h, int
     const float *colb = static_cast<const float *>(h.col_bias);
 
     // The ones of the extra MFMA's operand (never overwritten by the copies).
-    if (tid < 2 * kBiasSlots) {
-        const int e = tid % kBiasSlots;
+    for (int k = tid; k < 2 * kBiasSlots; k += kThreads) {
+        const int e = k % kBiasSlots;
         if ((e / 32) & 1)
-            lbias[tid / kBiasSlots][e] = 1.f;
+            lbias[k / kBiasSlots][e] = 1.f;
     }
     // Start the first tile's copy, then load the stationary B operands: this
     // lane's half of its row's scaled coordinates.
@@ -232,32 +222,41 @@ __global__ __launch_bounds__(kThreads) void lse_rows_mfma_kernel(HalfStep h, int
     __syncthreads();
 
     // Running reference M (shared by the row's two lane halves) and sum S.
+    // Software pipeline over subtiles: the MFMA chain of one subtile is
+    // issued before the previous subtile is folded.
     float M = 0.f;
     float S = 0.f;
-    float Mu0 = M;
-    floatx16 acc0 = score_tile<KP>(lrec[0], lbias[0], 0, lane, li, hl, bx, Mu0);
+    float Mu_prev = M;
+    floatx16 acc_prev = score_tile<KP>(lrec[0], lbias[0], 0, lane, li, hl, bx, Mu_prev);
     for (int t = tbeg; t < tend; ++t) {
         const int b = (t - tbeg) & 1;
         if (t + 1 < tend)
             issue_tile<TILE4>(col4, colb, t + 1, lrec[b ^ 1], lbias[b ^ 1], wave, lane);
-        const float Mu1 = M;
-        const floatx16 acc1 = score_tile<KP>(lrec[b], lbias[b], 1, lane, li, hl, bx, Mu1);
-        const float c0 = chunk_sum(acc0);
-        interleave<KP>();
-        fold(acc0, Mu0, c0, M, S);
-        pin(M, S);
+#pragma unroll
+        for (int sub = 1; sub < kSub; ++sub) {
+            const float Mu_cur = M;
+            const floatx16 acc_cur =
+                score_tile<KP>(lrec[b], lbias[b], sub, lane, li, hl, bx, Mu_cur);
+            const float c = chunk_sum(acc_prev);
+            fold(acc_prev, Mu_prev, c, M, S);
+            pin(M, S);
+            acc_prev = acc_cur;
+            Mu_prev = Mu_cur;
+        }
         // The next tile has landed for every wave, and every wave is done
         // reading this one.
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         // First subtile of the next tile. On the last iteration this reads
         // the idle buffer and the result is never folded.
-        Mu0 = M;
-        acc0 = score_tile<KP>(lrec[b ^ 1], lbias[b ^ 1], 0, lane, li, hl, bx, Mu0);
-        const float c1 = chunk_sum(acc1);
-        interleave<KP>();
-        fold(acc1, Mu1, c1, M, S);
+        const float Mu_cur = M;
+        const floatx16 acc_cur =
+            score_tile<KP>(lrec[b ^ 1], lbias[b ^ 1], 0, lane, li, hl, bx, Mu_cur);
+        const float c = chunk_sum(acc_prev);
+        fold(acc_prev, Mu_prev, c, M, S);
         pin(M, S);
+        acc_prev = acc_cur;
+        Mu_prev = Mu_cur;
     }
 
     // Merge the two lane halves (same row i, same M, disjoint columns). Both
