@@ -8,8 +8,10 @@ upcast to fp64 here; every result is fp64.
 The arithmetic lives in ``sinkhorn_oracle.c`` (plain C, OpenMP over rows),
 which states the update it follows ("FlashSinkhorn: IO-Aware Entropic Optimal
 Transport on GPU", Methodik section 1; the Birkhoff-projection page, section
-2). This module only marshals arrays, plus :func:`sinkhorn_schedule`, which
-runs stages of :func:`sinkhorn` one after another (warm start).
+2). This module only marshals arrays, plus thin compositions of those
+functions: :func:`sinkhorn_schedule` runs stages of :func:`sinkhorn` one
+after another (warm start); :func:`barycentric_map` and :func:`grad_x` combine
+one :func:`transport_apply` with the weights or the points.
 
 Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``):
 
@@ -20,6 +22,9 @@ Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``
   fixed point at the final eps); the schedule itself is not on the pages.
 * ``birkhoff4``, ``birkhoff4_replay``: pinned (doubly-stochastic limit,
   cross-ratio invariant, constant and circulant logits, stopping rule).
+* ``transport_apply``, ``barycentric_map``, ``grad_x``: pinned (n = 1 closed
+  form, product-coupling limit, eps -> 0 permutation limit, finite
+  differences of the converged dual value, marginal sums).
 """
 from __future__ import annotations
 
@@ -70,6 +75,9 @@ def _load():
         lib.oracle_plan_stats.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int64,
                                           ctypes.c_int64, ctypes.c_int, ctypes.c_double,
                                           _dp, _dp, _dp, _dp]
+        lib.oracle_transport_apply.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64,
+                                               ctypes.c_int, ctypes.c_double, _dp, ctypes.c_int,
+                                               _dp]
         lib.oracle_birkhoff4.argtypes = [_dp, ctypes.c_int64, ctypes.c_double, ctypes.c_int,
                                          ctypes.c_double, _dp, _i32p]
         lib.oracle_birkhoff4_replay.argtypes = [_dp, ctypes.c_int64, ctypes.c_double, _i32p,
@@ -163,6 +171,38 @@ def plan_stats(x, y, a, b, f, g, eps: float) -> dict:
                               float(eps), _ptr(cost), _ptr(marg), _ptr(rs), _ptr(cs))
     return {"cost": float(cost[0]), "marg_row": float(marg[0]), "marg_col": float(marg[1]),
             "marg": float(marg[0] + marg[1]), "rowsum": rs, "colsum": cs}
+
+
+def transport_apply(x, y, f, g, eps: float, v) -> np.ndarray:
+    """out_i = sum_j P_ij v_j with P_ij = exp((f_i + g_j - |x_i - y_j|^2)/eps);
+    v is (m,) or (m, dv). Returns (n,) or (n, dv)."""
+    x, y = _points(x, "x"), _points(y, "y")
+    f, g = _d(f), _d(g)
+    v = _d(v)
+    flat = v.ndim == 1
+    v2 = v.reshape(v.shape[0], -1)
+    n, m, d = x.shape[0], y.shape[0], x.shape[1]
+    if y.shape[1] != d or f.shape != (n,) or g.shape != (m,) or v2.shape[0] != m:
+        raise ValueError("shape mismatch")
+    out = np.empty((n, v2.shape[1]))
+    _load().oracle_transport_apply(_ptr(x), _ptr(y), _ptr(f), _ptr(g), n, m, d, float(eps),
+                                   _ptr(np.ascontiguousarray(v2)), v2.shape[1], _ptr(out))
+    return out[:, 0] if flat else out
+
+
+def barycentric_map(x, y, a, f, g, eps: float) -> np.ndarray:
+    """T(x_i) = sum_j P_ij y_j / a_i (Methodik section 3)."""
+    return transport_apply(x, y, f, g, eps, y) / _d(a)[:, None]
+
+
+def grad_x(x, y, f, g, eps: float) -> np.ndarray:
+    """d/dx_i of sum_ij P_ij C_ij at the fixed plan P of (f, g):
+    2 sum_j P_ij (x_i - y_j) = 2 (r_i x_i - sum_j P_ij y_j). At the
+    optimal (f, g) this is the gradient of OT_eps with respect to x_i."""
+    x, y = _points(x, "x"), _points(y, "y")
+    ones = np.ones((y.shape[0], 1))
+    w = transport_apply(x, y, f, g, eps, np.hstack([y, ones]))
+    return 2.0 * (w[:, -1:] * x - w[:, :-1])
 
 
 def birkhoff4(logits, eps: float = 1.0, max_iters: int = 200, tol: float = 1e-6):

@@ -163,6 +163,29 @@ void oracle_plan_stats(const double *x, const double *y, const double *a,
     free(cs);
 }
 
+/*
+ * Transport application ("FlashSinkhorn ...", Methodik section 3: the
+ * barycentric projection and the gradients are weighted averages under the
+ * plan, computed without storing it):
+ *   out[i*dv + k] = sum_j P_ij v[j*dv + k],  P_ij = exp((f_i + g_j - C_ij)/eps)
+ * Terms are added in index order j.
+ */
+void oracle_transport_apply(const double *x, const double *y, const double *f,
+                            const double *g, int64_t n, int64_t m, int d,
+                            double eps, const double *v, int dv, double *out)
+{
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < n; ++i) {
+        for (int k = 0; k < dv; ++k)
+            out[i * dv + k] = 0.0;
+        for (int64_t j = 0; j < m; ++j) {
+            double p = exp((f[i] + g[j] - sq_dist(x + i * (int64_t)d, y + j * (int64_t)d, d)) / eps);
+            for (int k = 0; k < dv; ++k)
+                out[i * dv + k] += p * v[j * dv + k];
+        }
+    }
+}
+
 /* ---------------------------------------------------------------------- */
 /* Batched 4x4 Birkhoff projection: EOT with a = b = 1 and cost = -L.       */
 /* ---------------------------------------------------------------------- */

@@ -425,3 +425,79 @@ def test_birkhoff_fixed20_sigma_split():
     med1 = np.median(err[:2048])
     med10 = np.median(err[2048:])
     assert med10 > ratio_min * med1
+
+
+# --------------------------------------------------------------------------- #
+# Transport application (FlashSinkhorn page, Methodik section 3)               #
+# --------------------------------------------------------------------------- #
+
+def test_transport_apply_single_source_closed_form():
+    # n = 1 after an iteration: P_1j = b_j, so sum_j P_1j v_j = sum_j b_j v_j.
+    rng = np.random.default_rng(30)
+    x = rng.normal(size=(1, 3))
+    y = rng.normal(size=(23, 3))
+    b = rng.dirichlet(np.ones(23))
+    a = np.array([b.sum()])
+    f, g = oracle.sinkhorn(x, y, a, b, 0.3, 2)
+    v = rng.normal(size=(23, 4))
+    np.testing.assert_allclose(oracle.transport_apply(x, y, f, g, 0.3, v)[0], b @ v, rtol=1e-12)
+    np.testing.assert_allclose(oracle.barycentric_map(x, y, a, f, g, 0.3)[0], (b @ y) / a[0],
+                               rtol=1e-12)
+
+
+def test_transport_apply_product_coupling_limit():
+    c = random_clouds(20, 15, 3, seed=31)
+    a, b = c["a"].astype(np.float64), c["b"].astype(np.float64)
+    a, b = a / a.sum(), b / b.sum()
+    eps = 1e7
+    f, g = oracle.sinkhorn(c["x"], c["y"], a, b, eps, 3)
+    v = np.random.default_rng(32).normal(size=(15, 2))
+    np.testing.assert_allclose(oracle.transport_apply(c["x"], c["y"], f, g, eps, v),
+                               np.outer(a, b @ v), rtol=1e-5, atol=1e-12)
+
+
+def test_transport_apply_of_ones_is_the_row_marginal_after_an_f_step():
+    c = random_clouds(17, 21, 3, seed=33)
+    eps = 0.2
+    f, g = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, 3)
+    f_new = oracle.half_update(c["x"], c["y"], c["a"], g, eps)
+    np.testing.assert_allclose(oracle.transport_apply(c["x"], c["y"], f_new, g, eps, np.ones(21)),
+                               c["a"], rtol=1e-12)
+
+
+def test_barycentric_map_small_eps_is_the_optimal_matching():
+    n = 5
+    rng = np.random.default_rng(34)
+    x = rng.normal(size=(n, 2))
+    y = rng.normal(size=(n, 2))
+    C = dense_cost(x, y)
+    best = min(itertools.permutations(range(n)), key=lambda p: C[np.arange(n), list(p)].sum())
+    a = np.full(n, 1.0 / n)
+    eps = 2e-3
+    f, g = _small_eps_solve(x, y, a, a, eps)
+    T = oracle.barycentric_map(x, y, a, f, g, eps)
+    np.testing.assert_allclose(T, y[list(best)], atol=1e-3)
+
+
+def _entropic_value(x, y, a, b, eps, iters=4000):
+    f, g = oracle.sinkhorn(x, y, a, b, eps, iters)
+    return a @ f + b @ g, f, g
+
+
+def test_grad_x_matches_finite_differences_of_the_entropic_value():
+    # Envelope theorem: at the optimum, d/dx_i OT_eps = 2 sum_j P_ij (x_i - y_j).
+    rng = np.random.default_rng(35)
+    x = rng.normal(size=(6, 2))
+    y = rng.normal(size=(5, 2))
+    a = rng.dirichlet(np.ones(6))
+    b = rng.dirichlet(np.ones(5))
+    eps = 0.5
+    _, f, g = _entropic_value(x, y, a, b, eps)
+    G = oracle.grad_x(x, y, f, g, eps)
+    h = 1e-5
+    for i, k in [(0, 0), (3, 1), (5, 0)]:
+        xp, xm = x.copy(), x.copy()
+        xp[i, k] += h
+        xm[i, k] -= h
+        fd = (_entropic_value(xp, y, a, b, eps)[0] - _entropic_value(xm, y, a, b, eps)[0]) / (2 * h)
+        assert G[i, k] == pytest.approx(fd, rel=1e-6, abs=1e-9)
