@@ -132,6 +132,51 @@ ot_status ot_marginal_error(const float *x, const float *y, const float *a,
                             int64_t n, int64_t m, int32_t d, float eps,
                             double *marg, void *stream);
 
+/* Largest number of value channels ot_transport_apply accepts. */
+#define OT_MAX_VALUE_DIM 1024
+
+/*
+ * ot_transport_apply -- out_i = sum_j P_ij v_j for the plan
+ * P_ij = exp((f_i + g_j - C_ij)/eps) of the given potentials, without storing
+ * P (page "FlashSinkhorn ...", "Methodik" section 3: applying the transport
+ * plan is an attention-like weighted average over the streamed tiles).
+ *
+ *   v    [m*dv]  values attached to the target points, row-major
+ *   dv   in [1, OT_MAX_VALUE_DIM]
+ *   out  [n*dv]  row-major; must not overlap any input
+ *
+ * Other arguments as ot_plan_stats. Terms of P are formed in fp64 and
+ * exponentiated in fp32; sums over j are fp64 in a fixed order.
+ * Errors: INVALID_VALUE (null pointer, sizes < 1, bad eps, overlap),
+ * NOT_SUPPORTED (d > OT_MAX_DIM, dv > OT_MAX_VALUE_DIM), OUT_OF_MEMORY,
+ * LAUNCH_FAILURE.
+ */
+ot_status ot_transport_apply(const float *x, const float *y, const float *f,
+                             const float *g, int64_t n, int64_t m, int32_t d,
+                             float eps, const float *v, int32_t dv, float *out,
+                             void *stream);
+
+/*
+ * ot_barycentric_map -- out_i = sum_j P_ij y_j / a_i (n*d): the barycentric
+ * projection of each source point under the plan (page "FlashSinkhorn ...",
+ * "Methodik" section 3). a [n] are the source weights (> 0).
+ */
+ot_status ot_barycentric_map(const float *x, const float *y, const float *a,
+                             const float *f, const float *g, int64_t n,
+                             int64_t m, int32_t d, float eps, float *out,
+                             void *stream);
+
+/*
+ * ot_cost_gradient_x -- out_i = 2 sum_j P_ij (x_i - y_j) (n*d): the gradient of
+ * sum_ij P_ij C_ij with respect to x_i at the fixed plan of (f, g); at the
+ * optimal potentials this is the gradient of the entropic OT cost with
+ * respect to the source points (envelope theorem; page "FlashSinkhorn ...",
+ * "Methodik" section 3, gradients as weighted averages).
+ */
+ot_status ot_cost_gradient_x(const float *x, const float *y, const float *f,
+                             const float *g, int64_t n, int64_t m, int32_t d,
+                             float eps, float *out, void *stream);
+
 /*
  * ot_birkhoff_project_batched -- project each 4x4 matrix of a batch onto the
  * doubly-stochastic matrices (page "Aceleración de la Proyección de Birkhoff

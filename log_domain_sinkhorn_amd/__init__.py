@@ -32,8 +32,12 @@ __all__ = [
     "ot_plan_stats",
     "ot_plan_cost",
     "ot_marginal_error",
+    "ot_transport_apply",
+    "ot_barycentric_map",
+    "ot_cost_gradient_x",
     "ot_birkhoff_project_batched",
     "OT_MAX_DIM",
+    "OT_MAX_VALUE_DIM",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -47,6 +51,7 @@ OT_ERROR_NOT_SUPPORTED = 2
 OT_ERROR_OUT_OF_MEMORY = 3
 OT_ERROR_LAUNCH_FAILURE = 4
 OT_MAX_DIM = 128
+OT_MAX_VALUE_DIM = 1024
 
 _lock = threading.Lock()
 _handle = None
@@ -64,6 +69,10 @@ _SIGNATURES = {
     "ot_plan_stats": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _f32, _p, _p, _p], ctypes.c_int),
     "ot_plan_cost": ([_p, _p, _p, _p, _i64, _i64, _i32, _f32, _p, _p], ctypes.c_int),
     "ot_marginal_error": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _f32, _p, _p], ctypes.c_int),
+    "ot_transport_apply": ([_p, _p, _p, _p, _i64, _i64, _i32, _f32, _p, _i32, _p, _p],
+                           ctypes.c_int),
+    "ot_barycentric_map": ([_p, _p, _p, _p, _p, _i64, _i64, _i32, _f32, _p, _p], ctypes.c_int),
+    "ot_cost_gradient_x": ([_p, _p, _p, _p, _i64, _i64, _i32, _f32, _p, _p], ctypes.c_int),
     "ot_birkhoff_project_batched": ([_p, _i64, _f32, _i32, _f32, _p, _p, _p], ctypes.c_int),
 }
 
@@ -235,6 +244,41 @@ def ot_marginal_error(x, y, a, b, f, g, eps: float, marg, stream=None) -> None:
     _dev_tensor(marg, "marg", "f64", (2,))
     _call("ot_marginal_error", _ptr(x), _ptr(y), _ptr(a), _ptr(b), _ptr(f), _ptr(g), n, m, d,
           float(eps), _ptr(marg), _stream_of(x, stream))
+
+
+def ot_transport_apply(x, y, f, g, eps: float, v, out, stream=None) -> None:
+    """out (n, dv) = P v for v (m, dv), P_ij = exp((f_i + g_j - |x_i - y_j|^2)/eps)."""
+    n, m, d = _clouds(x, y)
+    _dev_tensor(f, "f", "f32", (n,))
+    _dev_tensor(g, "g", "f32", (m,))
+    _dev_tensor(v, "v", "f32")
+    if v.dim() != 2 or v.shape[0] != m:
+        raise ValueError("v must be (m, dv)")
+    dv = v.shape[1]
+    _dev_tensor(out, "out", "f32", (n, dv))
+    _call("ot_transport_apply", _ptr(x), _ptr(y), _ptr(f), _ptr(g), n, m, d, float(eps), _ptr(v),
+          dv, _ptr(out), _stream_of(x, stream))
+
+
+def ot_barycentric_map(x, y, a, f, g, eps: float, out, stream=None) -> None:
+    """out (n, d): T(x_i) = sum_j P_ij y_j / a_i."""
+    n, m, d = _clouds(x, y)
+    _dev_tensor(a, "a", "f32", (n,))
+    _dev_tensor(f, "f", "f32", (n,))
+    _dev_tensor(g, "g", "f32", (m,))
+    _dev_tensor(out, "out", "f32", (n, d))
+    _call("ot_barycentric_map", _ptr(x), _ptr(y), _ptr(a), _ptr(f), _ptr(g), n, m, d, float(eps),
+          _ptr(out), _stream_of(x, stream))
+
+
+def ot_cost_gradient_x(x, y, f, g, eps: float, out, stream=None) -> None:
+    """out (n, d): 2 (r_i x_i - sum_j P_ij y_j) with r_i = sum_j P_ij."""
+    n, m, d = _clouds(x, y)
+    _dev_tensor(f, "f", "f32", (n,))
+    _dev_tensor(g, "g", "f32", (m,))
+    _dev_tensor(out, "out", "f32", (n, d))
+    _call("ot_cost_gradient_x", _ptr(x), _ptr(y), _ptr(f), _ptr(g), n, m, d, float(eps),
+          _ptr(out), _stream_of(x, stream))
 
 
 def ot_birkhoff_project_batched(logits, eps: float, max_iters: int, tol: float, out,

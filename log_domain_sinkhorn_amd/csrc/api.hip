@@ -259,6 +259,137 @@ ot_status ot_marginal_error(const float *x, const float *y, const float *a, cons
     return ot_plan_stats(x, y, a, b, f, g, n, m, d, eps, nullptr, marg, stream);
 }
 
+// out_i = sum_j P_ij v_j: records with hat biases of f and g, then the
+// VALU (d < 32) or MFMA (d >= 32) streaming kernel. rowsum (MFMA path only,
+// nullable) also receives r_i = sum_j P_ij.
+static ot_status transport_apply_impl(const float *x, const float *y, const float *f,
+                                      const float *g, int64_t n, int64_t m, int32_t d, float eps,
+                                      const float *v, int32_t dv, float *out, float *rowsum,
+                                      hipStream_t s) {
+    const Layout L = choose_layout(d);
+    if (rowsum && !L.mfma)
+        return OT_ERROR_INVALID_VALUE;
+    const int64_t n_pad = pad_points(n), m_pad = pad_points(m);
+    const size_t xb = align_up((size_t)n_pad * L.record_bytes(), 256);
+    const size_t yb = align_up((size_t)m_pad * L.record_bytes(), 256);
+    const size_t xbb = L.mfma ? align_up((size_t)n_pad * sizeof(float), 256) : 0;
+    const size_t ybb = L.mfma ? align_up((size_t)m_pad * sizeof(float), 256) : 0;
+    const size_t pd = L.mfma ? transport_mfma_scratch_doubles(n, m_pad, dv, rowsum != nullptr)
+                             : transport_scratch_doubles(L, n, m_pad, dv);
+    Scratch sc(s);
+    hipError_t e = sc.alloc(xb + yb + xbb + ybb + pd * sizeof(double));
+    if (e != hipSuccess)
+        return map_error(e);
+    char *base = static_cast<char *>(sc.ptr);
+    void *xrec = base, *yrec = base + xb;
+    void *xbias = L.mfma ? static_cast<void *>(base + xb + yb) : xrec;
+    void *ybias = L.mfma ? static_cast<void *>(base + xb + yb + xbb) : yrec;
+    double *part = reinterpret_cast<double *>(base + xb + yb + xbb + ybb);
+    const int bstride = L.mfma ? 1 : L.rs;
+    const int boff = L.mfma ? 0 : L.kp;
+    const double hat_scale = kLog2e / (double)eps;
+    if ((e = launch_prep_side(x, f, n, n_pad, L, hat_scale, kBiasHat, xrec, xbias, bstride, boff,
+                              s)) != hipSuccess)
+        return map_error(e);
+    if ((e = launch_prep_side(y, g, m, m_pad, L, hat_scale, kBiasHat, yrec, ybias, bstride, boff,
+                              s)) != hipSuccess)
+        return map_error(e);
+    const double scale = 2.0 * kLog2e / (double)eps;
+    if (L.mfma)
+        e = launch_transport_apply_mfma(L, xrec, static_cast<const float *>(xbias), yrec,
+                                        static_cast<const float *>(ybias), v, n, n_pad, m, m_pad,
+                                        dv, scale, part, out, rowsum, s);
+    else
+        e = launch_transport_apply(L, xrec, yrec, v, n, n_pad, m, m_pad, dv, scale, part, out, s);
+    return map_error(e);
+}
+
+ot_status ot_transport_apply(const float *x, const float *y, const float *f, const float *g,
+                             int64_t n, int64_t m, int32_t d, float eps, const float *v,
+                             int32_t dv, float *out, void *stream) {
+    ot_status st = check_clouds(x, y, n, m, d, eps);
+    if (st == OT_SUCCESS && (!f || !g || !v || !out || dv < 1))
+        st = OT_ERROR_INVALID_VALUE;
+    if (st == OT_SUCCESS) {
+        const size_t ob = (size_t)n * dv * 4;
+        const void *ins[5] = {x, y, f, g, v};
+        const size_t inb[5] = {(size_t)n * d * 4, (size_t)m * d * 4, (size_t)n * 4,
+                               (size_t)m * 4, (size_t)m * dv * 4};
+        for (int k = 0; k < 5; ++k)
+            if (overlaps(out, ob, ins[k], inb[k]))
+                st = OT_ERROR_INVALID_VALUE;
+    }
+    if (st == OT_SUCCESS)
+        st = check_supported(n, m, d);
+    if (st == OT_SUCCESS && dv > OT_MAX_VALUE_DIM)
+        st = OT_ERROR_NOT_SUPPORTED;
+    if (st != OT_SUCCESS)
+        return st;
+    return transport_apply_impl(x, y, f, g, n, m, d, eps, v, dv, out, nullptr,
+                                (hipStream_t)stream);
+}
+
+// The barycentric map (mode 0) and the x-gradient (mode 1) from one
+// application. The map applies the plan to y and divides by a. The gradient
+// also needs the row sums r_i: the MFMA kernel forms them beside its value
+// channels; the VALU path applies the plan to [y | 1] instead.
+static ot_status map_or_grad(const float *x, const float *y, const float *a, const float *f,
+                             const float *g, int64_t n, int64_t m, int32_t d, float eps,
+                             float *out, int mode, void *stream) {
+    ot_status st = check_clouds(x, y, n, m, d, eps);
+    if (st == OT_SUCCESS && (!f || !g || !out || (mode == 0 && !a)))
+        st = OT_ERROR_INVALID_VALUE;
+    if (st == OT_SUCCESS) {
+        const size_t ob = (size_t)n * d * 4;
+        const void *ins[5] = {x, y, f, g, a};
+        const size_t inb[5] = {(size_t)n * d * 4, (size_t)m * d * 4, (size_t)n * 4,
+                               (size_t)m * 4, a ? (size_t)n * 4 : 0};
+        for (int k = 0; k < 5; ++k)
+            if (ins[k] && overlaps(out, ob, ins[k], inb[k]))
+                st = OT_ERROR_INVALID_VALUE;
+    }
+    if (st == OT_SUCCESS)
+        st = check_supported(n, m, d);
+    if (st != OT_SUCCESS)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    const bool mfma = choose_layout(d).mfma;
+    const bool ones = mode == 1 && !mfma;  // values [y | 1]
+    const int dv = ones ? d + 1 : d;
+    const size_t vb = ones ? align_up((size_t)m * dv * sizeof(float), 256) : 0;
+    const size_t wb = align_up((size_t)n * dv * sizeof(float), 256);
+    const size_t rb = mode == 1 && mfma ? align_up((size_t)n * sizeof(float), 256) : 0;
+    Scratch sc(s);
+    hipError_t e = sc.alloc(vb + wb + rb);
+    if (e != hipSuccess)
+        return map_error(e);
+    char *base = static_cast<char *>(sc.ptr);
+    const float *v = y;
+    if (ones) {
+        if ((e = launch_values_y1(y, m, d, reinterpret_cast<float *>(base), s)) != hipSuccess)
+            return map_error(e);
+        v = reinterpret_cast<const float *>(base);
+    }
+    float *w = reinterpret_cast<float *>(base + vb);
+    float *r = rb ? reinterpret_cast<float *>(base + vb + wb) : nullptr;
+    st = transport_apply_impl(x, y, f, g, n, m, d, eps, v, dv, w, r, s);
+    if (st != OT_SUCCESS)
+        return st;
+    return map_error(launch_combine(w, dv, r, x, a, n, d, mode, out, s));
+}
+
+ot_status ot_barycentric_map(const float *x, const float *y, const float *a, const float *f,
+                             const float *g, int64_t n, int64_t m, int32_t d, float eps,
+                             float *out, void *stream) {
+    return map_or_grad(x, y, a, f, g, n, m, d, eps, out, 0, stream);
+}
+
+ot_status ot_cost_gradient_x(const float *x, const float *y, const float *f, const float *g,
+                             int64_t n, int64_t m, int32_t d, float eps, float *out,
+                             void *stream) {
+    return map_or_grad(x, y, nullptr, f, g, n, m, d, eps, out, 1, stream);
+}
+
 ot_status ot_birkhoff_project_batched(const float *logits, int64_t batch, float eps,
                                       int32_t max_iters, float tol, float *out,
                                       int32_t *iters_out, void *stream) {

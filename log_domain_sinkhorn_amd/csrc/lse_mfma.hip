@@ -46,7 +46,7 @@
 // The loop is software-pipelined over 32-column subtiles with two
 // accumulators so a subtile's MFMA chain and the previous subtile's epilogue
 // sit next to each other in one basic block.
-#include "ot_internal.h"
+#include "mfma_common.h"
 
 #include <math.h>
 
@@ -56,11 +56,7 @@ hipError_t launch_merge(const HalfStep &h, const Layout &L, int nsplit, hipStrea
 
 namespace {
 
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+using namespace mfma;
 
 constexpr int kWaves = 8;                 // waves per workgroup, 32 rows each
 constexpr int kThreads = 64 * kWaves;
@@ -68,57 +64,7 @@ constexpr int kRowsPerBlock = 32 * kWaves;
 constexpr int kTileCols = 128;            // columns per LDS tile
 constexpr int kSub = kTileCols / 32;      // 32-column subtiles per tile
 static_assert(kSub <= kWaves, "one wave copies each subtile's biases");
-// LDS operand of the extra MFMA, per 32-column subtile: 32 column biases
-// (read by lane half 0) followed by 32 ones (read by lane half 1).
 constexpr int kBiasSlots = 2 * kTileCols;
-
-// Start the copy of column tile t into LDS buffers (rec, bias). Coordinates:
-// whole 64-lane chunks of 16 bytes; lane l lands 16 bytes after lane l-1 at
-// the wave-uniform chunk base. Biases: two 32-lane dword loads, one per
-// subtile, each into the first half of that subtile's slot pair.
-template <int TILE4>
-__device__ __forceinline__ void issue_tile(const float4 *__restrict__ col4,
-                                           const float *__restrict__ colb, int t, float4 *rec,
-                                           float *bias, int wave, int lane) {
-    const float4 *src = col4 + (int64_t)t * TILE4;
-#pragma unroll
-    for (int c = 0; c < TILE4 / 64; c += kWaves) {
-        const int chunk = c + wave;
-        if (TILE4 / 64 % kWaves == 0 || chunk < TILE4 / 64)
-            __builtin_amdgcn_global_load_lds(src + chunk * 64 + lane,
-                                             (lds_void *)(rec + chunk * 64), 16, 0, 0);
-    }
-    if (wave >= kWaves - kSub && lane < 32) {
-        const int sub = wave - (kWaves - kSub);
-        __builtin_amdgcn_global_load_lds(colb + (int64_t)t * kTileCols + sub * 32 + lane,
-                                         (lds_void *)(bias + sub * 64), 4, 0, 0);
-    }
-}
-
-// u[j][i] = s_ij - Mu_i for the 32 columns of subtile `sub`: the extra MFMA
-// (bias and -Mu) on a zero accumulator, then KP/2 MFMAs over k.
-template <int KP>
-__device__ __forceinline__ floatx16 score_tile(const float4 *rec, const float *bias, int sub,
-                                               int lane, int li, int hl, const float (&bx)[KP / 2],
-                                               float Mu) {
-    constexpr int RS4 = (KP + 4) / 4;
-    constexpr int KH = KP / 2;
-    const floatx16 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
-                           0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    const float a0 = bias[sub * 64 + lane];
-    const float b0 = hl ? -Mu : 1.f;
-    floatx16 acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, zero, 0, 0, 0);
-    const float4 *ap = rec + (sub * 32 + li) * RS4 + hl * (KH / 4);
-#pragma unroll
-    for (int q4 = 0; q4 < KH / 4; ++q4) {
-        const float4 av = ap[q4];
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, bx[4 * q4 + 0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, bx[4 * q4 + 1], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, bx[4 * q4 + 2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, bx[4 * q4 + 3], acc, 0, 0, 0);
-    }
-    return acc;
-}
 
 // Common part of the epilogue: the sum of 2^u over the lane's 16 values.
 __device__ __forceinline__ float chunk_sum(const floatx16 &u) {
@@ -196,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void lse_rows_mfma_kernel(HalfStep h, int
     }
     // Start the first tile's copy, then load the stationary B operands: this
     // lane's half of its row's scaled coordinates.
-    issue_tile<TILE4>(col4, colb, tbeg, lrec[0], lbias[0], wave, lane);
+    issue_tile<TILE4, kWaves, kSub>(col4, colb, tbeg, lrec[0], lbias[0], wave, lane);
     const float scale = (float)h.scale;
     const int64_t i = (int64_t)blockIdx.x * kRowsPerBlock + wave * 32 + li;
     const int64_t ic = i < h.rows ? i : h.rows - 1;
@@ -231,7 +177,8 @@ __global__ __launch_bounds__(kThreads) void lse_rows_mfma_kernel(HalfStep h, int
     for (int t = tbeg; t < tend; ++t) {
         const int b = (t - tbeg) & 1;
         if (t + 1 < tend)
-            issue_tile<TILE4>(col4, colb, t + 1, lrec[b ^ 1], lbias[b ^ 1], wave, lane);
+            issue_tile<TILE4, kWaves, kSub>(col4, colb, t + 1, lrec[b ^ 1], lbias[b ^ 1], wave,
+                                            lane);
 #pragma unroll
         for (int sub = 1; sub < kSub; ++sub) {
             const float Mu_cur = M;

@@ -94,6 +94,28 @@ hipError_t launch_plan_stats(const float *x_rec, const float *y_rec, const float
 size_t plan_stats_scratch_doubles(const Layout &L, int64_t n, int64_t m, int64_t n_pad,
                                   int64_t m_pad);
 
+// Transport application (records from launch_prep_side with kBiasHat of f
+// and g; out_i = sum_j P_ij v_j).
+int transport_value_chunk(int dv);
+size_t transport_scratch_doubles(const Layout &L, int64_t n, int64_t m_pad, int dv);
+hipError_t launch_transport_apply(const Layout &L, const void *xrec, const void *yrec,
+                                  const float *v, int64_t n, int64_t n_pad, int64_t m,
+                                  int64_t m_pad, int dv, double scale, double *part, float *out,
+                                  hipStream_t s);
+// MFMA variant (fp32 records, separate fp32 hat biases); rowsum (nullable)
+// also receives r_i = sum_j P_ij, with rowsum = true in the scratch size.
+size_t transport_mfma_scratch_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum);
+hipError_t launch_transport_apply_mfma(const Layout &L, const void *xrec, const float *xbias,
+                                       const void *yrec, const float *ybias, const float *v,
+                                       int64_t n, int64_t n_pad, int64_t m, int64_t m_pad, int dv,
+                                       double scale, double *part, float *out, float *rowsum,
+                                       hipStream_t s);
+hipError_t launch_values_y1(const float *y, int64_t m, int d, float *v, hipStream_t s);
+// mode 0: out_i = w_i / a_i; mode 1: out_i = 2 (r_i x_i - w_i), where w_i is
+// row i of w (row stride ws >= d) and r_i = r[i], or w[i*ws + d] if r is null.
+hipError_t launch_combine(const float *w, int ws, const float *r, const float *x, const float *a,
+                          int64_t n, int d, int mode, float *out, hipStream_t s);
+
 hipError_t launch_birkhoff4(const float *logits, int64_t batch, float eps, int max_iters, float tol,
                             float *out, int32_t *iters_out, hipStream_t s);
 

@@ -25,6 +25,7 @@ def test_header_declares_expected_functions():
     assert lds.declared_functions() == sorted([
         "ot_status_string", "ot_sinkhorn_solve", "ot_sinkhorn_solve_eps_scaling",
         "ot_plan_stats", "ot_plan_cost", "ot_marginal_error", "ot_birkhoff_project_batched",
+        "ot_transport_apply", "ot_barycentric_map", "ot_cost_gradient_x",
     ])
 
 
@@ -37,6 +38,7 @@ def test_every_declared_function_is_exported(lib):
 def test_header_max_dim_matches_binding():
     text = open(lds._HEADER).read()
     assert f"#define OT_MAX_DIM {lds.OT_MAX_DIM}" in text
+    assert f"#define OT_MAX_VALUE_DIM {lds.OT_MAX_VALUE_DIM}" in text
 
 
 def test_status_strings(lib):
@@ -89,6 +91,40 @@ def test_plan_stats_rejects_invalid(lib):
     assert lib.ot_plan_cost(X, Y, F, G, 10, 12, 3, 0.1, None, None) == INVALID
     assert lib.ot_marginal_error(X, Y, A, B, F, G, 10, 12, 3, 0.1, None, None) == INVALID
     assert lib.ot_marginal_error(X, Y, None, B, F, G, 10, 12, 3, 0.1, MG, None) == INVALID
+
+
+V, OUT = 0x90000000, 0xA0000000
+
+
+def test_transport_apply_rejects_invalid(lib):
+    ta = lib.ot_transport_apply
+    ok = dict(x=X, y=Y, f=F, g=G, n=10, m=12, d=3, eps=0.1, v=V, dv=5, out=OUT)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return ta(a["x"], a["y"], a["f"], a["g"], a["n"], a["m"], a["d"], a["eps"], a["v"],
+                  a["dv"], a["out"], None)
+
+    for kw in [dict(x=None), dict(f=None), dict(g=None), dict(v=None), dict(out=None),
+               dict(n=0), dict(m=-1), dict(d=0), dict(dv=0), dict(eps=0.0), dict(eps=math.nan),
+               dict(out=X), dict(out=V + 8), dict(out=F - 16)]:
+        assert call(**kw) == INVALID, kw
+    assert call(d=lds.OT_MAX_DIM + 1) == UNSUPPORTED
+    assert call(dv=lds.OT_MAX_VALUE_DIM + 1) == UNSUPPORTED
+    assert call(dv=lds.OT_MAX_VALUE_DIM + 1, eps=-1.0) == INVALID
+
+
+def test_map_and_gradient_reject_invalid(lib):
+    bm, gx = lib.ot_barycentric_map, lib.ot_cost_gradient_x
+    assert bm(X, Y, None, F, G, 10, 12, 3, 0.1, OUT, None) == INVALID      # map needs a
+    assert bm(X, Y, A, F, G, 10, 12, 3, 0.1, None, None) == INVALID
+    assert bm(X, Y, A, F, G, 10, 12, 3, 0.1, A, None) == INVALID           # out aliases a
+    assert bm(X, Y, A, F, G, 0, 12, 3, 0.1, OUT, None) == INVALID
+    assert bm(X, Y, A, F, G, 10, 12, 129, 0.1, OUT, None) == UNSUPPORTED
+    assert gx(X, Y, None, G, 10, 12, 3, 0.1, OUT, None) == INVALID
+    assert gx(X, Y, F, G, 10, 12, 3, 0.1, Y + 4, None) == INVALID          # out overlaps y
+    assert gx(X, Y, F, G, 10, 12, 3, -0.1, OUT, None) == INVALID
+    assert gx(X, Y, F, G, 10, 12, 129, 0.1, OUT, None) == UNSUPPORTED
 
 
 def test_birkhoff_rejects_invalid(lib):

@@ -36,6 +36,7 @@ __all__ = [
     "make_logits",
     "geometric_eps_schedule",
     "random_clouds",
+    "random_values",
 ]
 
 
@@ -210,6 +211,12 @@ def random_clouds(n: int, m: int, d: int, seed: int = 0, spread: float = 1.0,
     a = _weights(weights, n, rng)
     b = _weights(weights, m, rng)
     return {"x": _f32(x), "y": _f32(y), "a": a, "b": b}
+
+
+def random_values(count: int, dv: int, seed: int = 0) -> np.ndarray:
+    """Value matrix (count x dv, fp32) for the transport application: N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    return _f32(rng.normal(size=(count, dv)))
 
 
 def make_logits(batch: int, sigmas=(1.0, 10.0), seed: int = 0) -> np.ndarray:
