@@ -31,8 +31,9 @@ if ROOT not in sys.path:
 
 METRIC = "Sinkhorn pair-evals/sec (n·m·iters/s) at n=m=65536 + % of FP32/exp roofline"
 
-# MI355X published peaks used for the roofline fractions.
+# MI355X published peaks used for the roofline fractions (dense).
 PEAK_MFMA_FP32_TFLOPS = 157.3
+PEAK_MFMA_FP16_TFLOPS = 2500.0
 # ALU ceiling of the d < 32 half-step, derived from the chip's issue slots
 # (256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz) and the per-pair-side instruction
 # mix of that kernel: kp fp64 FMAs + 1 fp64 add (the score, formed in fp64),
@@ -43,7 +44,7 @@ PEAK_MFMA_FP32_TFLOPS = 157.3
 ISSUE_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
 EXP_SLOTS = 2.0
 
-HALF_STEP_KERNELS = ("lse_rows_mfma_kernel", "lse_rows_valu_kernel")
+HALF_STEP_KERNELS = ("lse_rows_h3_kernel", "lse_rows_valu_kernel")
 
 
 def parse():
@@ -66,10 +67,14 @@ def alu_peak_pair_sides(d: int) -> float:
     return ISSUE_SLOTS_PER_S / slots
 
 
-def source_digest(files) -> str:
+def source_digest(files):
+    """Digest of the named sources; None if one of them no longer exists."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
+        path = os.path.join(ROOT, f)
+        if not os.path.exists(path):
+            return None
+        with open(path, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -86,7 +91,8 @@ def traffic_for(kernel: str, workload: str):
         return None
     if not rec:
         return None
-    if rec.get("source_digest") != source_digest(rec.get("sources", [])):
+    digest = source_digest(rec.get("sources", []))
+    if digest is None or rec.get("source_digest") != digest:
         return None
     return rec.get("bytes_per_launch")
 
@@ -183,17 +189,30 @@ def run_cloud_workload(name, steps, warmup, torch, lds, with_stats=True):
     }
 
 
+def h3_kp(d: int) -> int:
+    """Coordinates per record of the split-f16 half-step (d padded to 32k)."""
+    return (d + 31) // 32 * 32
+
+
 def roofline_for(r, workload):
     n, m, d = r["n"], r["m"], r["d"]
     launch_s = r["half_step_ms"] / 1e3
     if d >= 32:
-        flops = 2.0 * d * n * m  # algorithmic fp32 MFMA flops per half-step launch
+        # The d >= 32 half-step forms each fp32 dot product as three f16
+        # matrix-core products (hi.hi + lo.hi + hi.lo) over kp = 32*ceil(d/32)
+        # coordinates: 3 * 2 * kp f16 MFMA flops per pair-side, against the
+        # f16 dense peak. The fp32-equivalent rate (2d flops per pair-side)
+        # is printed beside it with the fp32 MFMA peak.
+        kp = h3_kp(d)
+        flops = 6.0 * kp * n * m
         ach = flops / launch_s / 1e12
-        return {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_FP32_TFLOPS,
-                "unit": "TFLOP/s", "frac": ach / PEAK_MFMA_FP32_TFLOPS,
-                "traffic": traffic_for("lse_rows_mfma_kernel", workload),
-                "kernel": "lse_rows_mfma_kernel<64>", "launch_ms": r["half_step_ms"],
-                "work_per_launch": f"{n}*{m} pair-sides x {2 * d} flops"}
+        alg = 2.0 * d * n * m / launch_s / 1e12
+        return {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_FP16_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / PEAK_MFMA_FP16_TFLOPS,
+                "traffic": traffic_for("lse_rows_h3_kernel", workload),
+                "kernel": f"lse_rows_h3_kernel<{kp}>", "launch_ms": r["half_step_ms"],
+                "work_per_launch": f"{n}*{m} pair-sides x {6 * kp} f16 MFMA flops",
+                "fp32_equivalent_tflops": alg, "fp32_mfma_peak": PEAK_MFMA_FP32_TFLOPS}
     flops_per_ps = 2 * d + 3
     ach = flops_per_ps * n * m / launch_s / 1e12
     peak = alu_peak_pair_sides(d) * flops_per_ps / 1e12
@@ -245,6 +264,40 @@ def run_birkhoff(name, torch, lds, reps=5):
             "hbm_gb_per_s": w.batch * (64 + 64 + 4) / (ms / 1e3) / 1e9}
 
 
+def run_transport(name, torch, lds, reps=3):
+    """Transport application P·y (values = the target points) and the
+    x-gradient at the potentials of a short solve of workload ``name``."""
+    from workloads import make_clouds
+
+    c = make_clouds(name)
+    dev = torch.device("cuda:0")
+    x, y, a, b = (torch.from_numpy(c[k]).to(dev) for k in "xyab")
+    n, m, d = c["n"], c["m"], c["d"]
+    eps = c["eps"][-1]
+    f = torch.zeros(n, device=dev)
+    g = torch.zeros(m, device=dev)
+    lds.ot_sinkhorn_solve(x, y, a, b, eps, 5, f, g)
+    out = torch.empty((n, d), device=dev)
+    res = {"name": name, "n": n, "m": m, "d": d, "dv": d}
+    for label, fn in (("apply", lambda: lds.ot_transport_apply(x, y, f, g, eps, y, out)),
+                      ("grad", lambda: lds.ot_cost_gradient_x(x, y, f, g, eps, out))):
+        fn()
+        torch.cuda.synchronize()
+        with Timer(torch) as t:
+            for _ in range(reps):
+                fn()
+        ms = t.ms() / reps
+        res[f"{label}_ms"] = ms
+        res[f"{label}_pairs_per_s"] = n * m / (ms / 1e3)
+    if d >= 32:
+        flops = 2.0 * (d + d) * n * m  # x.y and P.V, fp32 MFMA
+        ach = flops / (res["apply_ms"] / 1e3) / 1e12
+        res["roofline_whole_call"] = {"bound": "mfma", "achieved": ach,
+                                      "peak": PEAK_MFMA_FP32_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": ach / PEAK_MFMA_FP32_TFLOPS}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -291,6 +344,12 @@ def main():
             sec[name] = {"pair_evals_per_s": s["pair_evals_per_s"], "ms_per_step": s["ms_per_step"],
                          "solve_ms": s["solve_ms"], "stats_ms": s["stats_ms"],
                          "roofline": roofline_for(s, name)}
+        for name in ("feature64_64k", "cube_gauss3d_64k"):
+            key = f"transport:{name}"
+            if wanted is not None and key not in wanted:
+                continue
+            print(f"# secondary {key}", file=sys.stderr, flush=True)
+            sec[key] = run_transport(name, torch, lds)
         for name in ("birkhoff4x4_1m_fixed20", "birkhoff4x4_1m"):
             if wanted is not None and name not in wanted:
                 continue

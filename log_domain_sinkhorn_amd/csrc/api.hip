@@ -82,36 +82,92 @@ struct Scratch {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// d >= 32: split-f16 matrix-core half-steps. Per side: column record and row
+// record (4*kp bytes per point each), |p|^2 and the fp32 bias.
+ot_status run_schedule_h3(const float *x, const float *y, const float *a, const float *b,
+                          int64_t n, int64_t m, int32_t d, const double *eps_list, int stages,
+                          int iters, float *f, float *g, hipStream_t s) {
+    const int kp = h3_kp(d);
+    const int64_t n_pad = pad_points(n), m_pad = pad_points(m);
+    size_t part = half_step_partials_h3(n, m_pad);
+    const size_t part2 = half_step_partials_h3(m, n_pad);
+    if (part2 > part)
+        part = part2;
+    const size_t xr = align_up((size_t)n_pad * 4 * kp, 256);
+    const size_t yr = align_up((size_t)m_pad * 4 * kp, 256);
+    const size_t xv = align_up((size_t)n_pad * sizeof(float), 256);
+    const size_t yv = align_up((size_t)m_pad * sizeof(float), 256);
+    const size_t pb = align_up(part * sizeof(Partial), 256);
+    const size_t mb = align_up(h3_maxabs_floats() * sizeof(float), 256);
+    Scratch sc(s);
+    hipError_t e = sc.alloc(2 * xr + 2 * yr + 2 * xv + 2 * yv + pb + mb);
+    if (e != hipSuccess)
+        return map_error(e);
+    char *p = static_cast<char *>(sc.ptr);
+    void *xcol = p, *xrow = p + xr;
+    p += 2 * xr;
+    void *ycol = p, *yrow = p + yr;
+    p += 2 * yr;
+    float *xnrm = reinterpret_cast<float *>(p), *xbias = reinterpret_cast<float *>(p + xv);
+    p += 2 * xv;
+    float *ynrm = reinterpret_cast<float *>(p), *ybias = reinterpret_cast<float *>(p + yv);
+    p += 2 * yv;
+    Partial *partials = reinterpret_cast<Partial *>(p);
+    float *maxabs = reinterpret_cast<float *>(p + pb);
+
+    if ((e = launch_maxabs(x, n * d, y, m * d, maxabs, s)) != hipSuccess)
+        return map_error(e);
+    for (int st = 0; st < stages; ++st) {
+        const double eps = eps_list[st];
+        const double scale = 2.0 * kLog2e / eps;
+        const double hat_scale = kLog2e / eps;
+        if ((e = launch_prep_h3(x, nullptr, n, n_pad, d, kp, scale, hat_scale, kBiasZero, maxabs,
+                                0, xcol, xrow, xnrm, xbias, s)) != hipSuccess)
+            return map_error(e);
+        if ((e = launch_prep_h3(y, g, m, m_pad, d, kp, scale, hat_scale, kBiasHat, maxabs, 1, ycol,
+                                yrow, ynrm, ybias, s)) != hipSuccess)
+            return map_error(e);
+        HalfStep hf{xrow, xbias, a, ycol, ybias, 1, 0, f, n, m_pad, scale, eps * kLn2,
+                    partials, n_pad, xnrm};
+        HalfStep hg{yrow, ybias, b, xcol, xbias, 1, 0, g, m, n_pad, scale, eps * kLn2,
+                    partials, m_pad, ynrm};
+        for (int it = 0; it < iters; ++it) {
+            if ((e = launch_half_step_h3(hf, kp, s)) != hipSuccess)
+                return map_error(e);
+            if ((e = launch_half_step_h3(hg, kp, s)) != hipSuccess)
+                return map_error(e);
+        }
+    }
+    return OT_SUCCESS;
+}
+
+// The whole schedule: stages of eps, each warm-started from the previous
+// stage's potentials; d < 32 on the VALU kernels (fp64 records with the bias
+// in the record), d >= 32 on the split-f16 matrix-core kernels.
 ot_status run_schedule(const float *x, const float *y, const float *a, const float *b, int64_t n,
                        int64_t m, int32_t d, const double *eps_list, int stages, int iters,
                        float *f, float *g, hipStream_t s) {
+    if (d >= 32)
+        return run_schedule_h3(x, y, a, b, n, m, d, eps_list, stages, iters, f, g, s);
     const Layout L = choose_layout(d);
     const int64_t n_pad = pad_points(n), m_pad = pad_points(m);
-    size_t part = L.mfma ? half_step_partials_mfma(n, m_pad) : half_step_partials(L, n, m_pad);
-    const size_t part2 =
-        L.mfma ? half_step_partials_mfma(m, n_pad) : half_step_partials(L, m, n_pad);
+    size_t part = half_step_partials(L, n, m_pad);
+    const size_t part2 = half_step_partials(L, m, n_pad);
     if (part2 > part)
         part = part2;
     const size_t xb = align_up((size_t)n_pad * L.record_bytes(), 256);
     const size_t yb = align_up((size_t)m_pad * L.record_bytes(), 256);
     const size_t pb = align_up(part * sizeof(Partial), 256);
-    // MFMA layout: biases in separate contiguous fp32 arrays.
-    const size_t xbb = L.mfma ? align_up((size_t)n_pad * sizeof(float), 256) : 0;
-    const size_t ybb = L.mfma ? align_up((size_t)m_pad * sizeof(float), 256) : 0;
     Scratch sc(s);
-    hipError_t e = sc.alloc(xb + yb + pb + xbb + ybb);
+    hipError_t e = sc.alloc(xb + yb + pb);
     if (e != hipSuccess)
         return map_error(e);
     char *base = static_cast<char *>(sc.ptr);
     void *xrec = base;
     void *yrec = base + xb;
     Partial *partials = reinterpret_cast<Partial *>(base + xb + yb);
-    void *xbias = L.mfma ? static_cast<void *>(base + xb + yb + pb) : xrec;
-    void *ybias = L.mfma ? static_cast<void *>(base + xb + yb + pb + xbb) : yrec;
-    const int bstride = L.mfma ? 1 : L.rs;
-    const int boff = L.mfma ? 0 : L.kp;
 
-    if ((e = launch_prep_side(x, nullptr, n, n_pad, L, 0.0, kBiasZero, xrec, xbias, bstride, boff,
+    if ((e = launch_prep_side(x, nullptr, n, n_pad, L, 0.0, kBiasZero, xrec, xrec, L.rs, L.kp,
                               s)) != hipSuccess)
         return map_error(e);
     for (int st = 0; st < stages; ++st) {
@@ -119,19 +175,17 @@ ot_status run_schedule(const float *x, const float *y, const float *a, const flo
         const double hat_scale = kLog2e / eps;
         // Column bias of the first f update, from the caller's (or the
         // previous stage's) g at this stage's eps.
-        if ((e = launch_prep_side(y, g, m, m_pad, L, hat_scale, kBiasHat, yrec, ybias, bstride,
-                                  boff, s)) != hipSuccess)
+        if ((e = launch_prep_side(y, g, m, m_pad, L, hat_scale, kBiasHat, yrec, yrec, L.rs, L.kp,
+                                  s)) != hipSuccess)
             return map_error(e);
-        HalfStep hf{xrec, xbias, a, yrec, ybias, bstride, boff, f, n, m_pad,
-                    2.0 * kLog2e / eps, eps * kLn2, partials, n_pad};
-        HalfStep hg{yrec, ybias, b, xrec, xbias, bstride, boff, g, m, n_pad,
-                    2.0 * kLog2e / eps, eps * kLn2, partials, m_pad};
+        HalfStep hf{xrec, xrec, a, yrec, yrec, L.rs, L.kp, f, n, m_pad,
+                    2.0 * kLog2e / eps, eps * kLn2, partials, n_pad, nullptr};
+        HalfStep hg{yrec, yrec, b, xrec, xrec, L.rs, L.kp, g, m, n_pad,
+                    2.0 * kLog2e / eps, eps * kLn2, partials, m_pad, nullptr};
         for (int it = 0; it < iters; ++it) {
-            e = L.mfma ? launch_half_step_mfma(hf, L, s) : launch_half_step_valu(hf, L, s);
-            if (e != hipSuccess)
+            if ((e = launch_half_step_valu(hf, L, s)) != hipSuccess)
                 return map_error(e);
-            e = L.mfma ? launch_half_step_mfma(hg, L, s) : launch_half_step_valu(hg, L, s);
-            if (e != hipSuccess)
+            if ((e = launch_half_step_valu(hg, L, s)) != hipSuccess)
                 return map_error(e);
         }
     }

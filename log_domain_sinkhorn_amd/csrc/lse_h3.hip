@@ -1,0 +1,403 @@
+// Log-domain Sinkhorn half-step for feature dimension d >= 32 with the dot
+// products on gfx950's f16 matrix cores, as three split products accumulated
+// in fp32.
+//
+// The update is the one of the other half-step kernels ("FlashSinkhorn:
+// IO-Aware Entropic Optimal Transport on GPU", Methodik sections 1-2):
+// s_ij = (2 log2(e)/eps) p_i.q_j + qhat_j, an online base-2 log-sum-exp over
+// j, phat_i = log2 w_i - lse_i. Only the way p_i.q_j is formed differs.
+//
+// Split products. Each fp32 coordinate v is written as hi + lo with
+// hi = f16(v) and lo = f16(v - hi), so v - hi - lo is below 2^-22 |v|. Then
+//   P.Q ~ Ph.Qh + Ph.Ql + Pl.Qh          (Pl.Ql, below 2^-22 |P||Q|, dropped)
+// with every f16 x f16 product exact. The split loses about 2^-22 |P||Q|;
+// the matrix core's aligned sums (below) lose about 2^-21 of the partial sum
+// per instruction, comparable to fp32 accumulation over d terms. A tile of
+// 32 columns x 32 rows takes 3*KP/16 v_mfma_f32_32x32x16_f16 (32 cycles each)
+// instead of KP/2 v_mfma_f32_32x32x2f32 (64 cycles each): 2.7x fewer matrix
+// cycles. On gfx950, f16 MFMAs also execute concurrently with vector-ALU
+// work from the same SIMD (measured: an FMA stream hides completely under an
+// f16 MFMA stream, an exp2 stream mostly), which fp32 MFMAs do not, so the
+// exp2/add epilogue of the log-sum-exp largely overlaps the products.
+//
+// f16 range. To keep hi and lo inside f16's range, the column side stores
+// (2 log2(e)/eps) q 2^-e and the row side p 2^e with one power of two e per
+// direction, chosen so that both sides' largest magnitudes meet at
+// sqrt((2 log2(e)/eps) max|p| max|q|); the product is unchanged. This needs
+// (2 log2(e)/eps) max|p_k| max|q_k| < 2^31 (beyond it fp32 scores would carry
+// no fractional bits either).
+//
+// The column bias qhat_j and the row's running maximum M enter through one
+// fp32 MFMA at the end of the chain (k-slot 0: bias_j x 1, k-slot 1:
+// 1 x -M_i), so they keep full fp32 precision.
+//
+// Layout. Column records: 2*KP halves (hi then lo) in 16-byte chunks, chunk q
+// of point j stored at position q ^ (j & SW), so the 16-byte operand reads of
+// consecutive points fall in distinct LDS banks. Row records: hi then lo,
+// unswizzled (read once per workgroup). Biases and norms are fp32 arrays.
+// Workgroups of 8 waves own 256 rows and stream 128-column tiles through
+// double-buffered LDS with gfx950's direct global->LDS loads, as the fp32
+// kernel does; the lazy shared running maximum and the epilogue are the same.
+#include "mfma_common.h"
+
+#include <math.h>
+
+namespace otsk {
+
+namespace {
+
+using namespace mfma;
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerBlock = 32 * kWaves;
+constexpr int kTileCols = 128;
+constexpr int kSub = kTileCols / 32;
+static_assert(kSub <= kWaves, "one wave copies each subtile's biases");
+constexpr int kBiasSlots = 2 * kTileCols;
+constexpr int kTargetBlocks = 1024;
+
+// Swizzle mask of a record of RC 16-byte chunks (RC a multiple of 8).
+__host__ __device__ constexpr int swizzle_mask(int rc) { return rc % 16 == 0 ? 15 : 7; }
+
+__device__ __forceinline__ half8 as_half8(float4 v) { return __builtin_bit_cast(half8, v); }
+
+// u[j][i] = s_ij - Mu_i for subtile `sub` of the tile in `rec` / `bias`.
+//
+// Order of the chain. The f16 MFMA adds its 16 products and the accumulator
+// in one aligned sum whose error is about 2^-21 of the largest term
+// (measured on gfx950; a lone product is exact), so the accumulator should be
+// small while the products go in: first the lo corrections (2^-11 of the
+// rest), then the hi x hi products onto them, and the bias and -M last,
+// through the fp32 MFMA, whose sum is rounded like fp32 arithmetic.
+template <int KP>
+__device__ __forceinline__ floatx16 score_h3(const float4 *rec, const float *bias, int sub,
+                                             int lane, int li, int hl, const half8 (&bh)[KP / 16],
+                                             const half8 (&bl)[KP / 16], float Mu) {
+    constexpr int RC = KP / 4;
+    constexpr int SW = swizzle_mask(RC);
+    floatx16 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
+                    0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const int j = sub * 32 + li;
+    const float4 *ap = rec + j * RC;
+    const int sw = j & SW;
+    half8 qh[KP / 16];
+#pragma unroll
+    for (int c = 0; c < KP / 16; ++c) {
+        qh[c] = as_half8(ap[(2 * c + hl) ^ sw]);
+        const half8 ql = as_half8(ap[(KP / 8 + 2 * c + hl) ^ sw]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ql, bh[c], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qh[c], bl[c], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < KP / 16; ++c)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qh[c], bh[c], acc, 0, 0, 0);
+    const float a0 = bias[sub * 64 + lane];
+    const float b0 = hl ? -Mu : 1.f;
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc, 0, 0, 0);
+}
+
+template <int KP>
+__global__ __launch_bounds__(kThreads) void lse_rows_h3_kernel(HalfStep h, int tiles_per_split,
+                                                               int ntiles) {
+    constexpr int RC = KP / 4;
+    constexpr int TILE16 = kTileCols * RC;
+    static_assert(KP % 32 == 0, "records are whole groups of 8 chunks");
+    static_assert(TILE16 % 64 == 0, "tiles are whole 64-lane chunks");
+    __shared__ float4 lrec[2][TILE16];
+    __shared__ float lbias[2][kBiasSlots];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int hl = lane >> 5;
+    const int li = lane & 31;
+    const int split = blockIdx.y;
+    const int tbeg = split * tiles_per_split;
+    const int tend = min(tbeg + tiles_per_split, ntiles);
+    const float4 *col4 = static_cast<const float4 *>(h.col_rec);
+    const float *colb = static_cast<const float *>(h.col_bias);
+
+    for (int k = tid; k < 2 * kBiasSlots; k += kThreads) {
+        const int e = k % kBiasSlots;
+        if ((e / 32) & 1)
+            lbias[k / kBiasSlots][e] = 1.f;
+    }
+    issue_tile<TILE16, kWaves, kSub>(col4, colb, tbeg, lrec[0], lbias[0], wave, lane);
+    // Stationary B operands: this lane's k-halves of its row's hi and lo parts.
+    const int64_t i = (int64_t)blockIdx.x * kRowsPerBlock + wave * 32 + li;
+    const int64_t ic = i < h.rows ? i : h.rows - 1;
+    half8 bh[KP / 16], bl[KP / 16];
+    {
+        const float4 *rr = static_cast<const float4 *>(h.row_rec) + ic * RC;
+#pragma unroll
+        for (int c = 0; c < KP / 16; ++c) {
+            bh[c] = as_half8(rr[2 * c + hl]);
+            bl[c] = as_half8(rr[KP / 8 + 2 * c + hl]);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    float M = 0.f;
+    float S = 0.f;
+    float Mu_prev = M;
+    floatx16 acc_prev = score_h3<KP>(lrec[0], lbias[0], 0, lane, li, hl, bh, bl, Mu_prev);
+    for (int t = tbeg; t < tend; ++t) {
+        const int b = (t - tbeg) & 1;
+        if (t + 1 < tend)
+            issue_tile<TILE16, kWaves, kSub>(col4, colb, t + 1, lrec[b ^ 1], lbias[b ^ 1], wave,
+                                             lane);
+#pragma unroll
+        for (int sub = 1; sub < kSub; ++sub) {
+            const float Mu_cur = M;
+            const floatx16 acc_cur = score_h3<KP>(lrec[b], lbias[b], sub, lane, li, hl, bh, bl,
+                                                  Mu_cur);
+            const float c = chunk_sum(acc_prev);
+            fold(acc_prev, Mu_prev, c, M, S);
+            pin(M, S);
+            acc_prev = acc_cur;
+            Mu_prev = Mu_cur;
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        // First subtile of the next tile (on the last iteration: the idle
+        // buffer, never folded).
+        const float Mu_cur = M;
+        const floatx16 acc_cur =
+            score_h3<KP>(lrec[b ^ 1], lbias[b ^ 1], 0, lane, li, hl, bh, bl, Mu_cur);
+        const float c = chunk_sum(acc_prev);
+        fold(acc_prev, Mu_prev, c, M, S);
+        pin(M, S);
+        acc_prev = acc_cur;
+        Mu_prev = Mu_cur;
+    }
+
+    const float So = __shfl_xor(S, 32);
+    const float Sm = hl == 0 ? S + So : So + S;
+    if (hl == 0 && i < h.rows) {
+        if (gridDim.y == 1) {
+            const float lse = M + hw_log2(Sm);
+            const float hat = log2f(h.row_w[i]) - lse;
+            static_cast<float *>(h.row_bias)[i] = hat;
+            h.pot_out[i] = fmaf((float)h.eps_ln2, hat, h.row_nrm[i]);
+        } else {
+            h.partials[(int64_t)split * h.rows_pad + i] = Partial{(double)M, Sm, 0.f};
+        }
+    }
+}
+
+// Combine the per-split (M, S) pairs of each row in split order.
+__global__ __launch_bounds__(256) void lse_merge_h3_kernel(HalfStep h, int nsplit) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= h.rows)
+        return;
+    double M = h.partials[i].m;
+    for (int s = 1; s < nsplit; ++s)
+        M = fmax(M, h.partials[(int64_t)s * h.rows_pad + i].m);
+    float S = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+        const Partial p = h.partials[(int64_t)s * h.rows_pad + i];
+        S = fmaf(p.s, hw_exp2((float)(p.m - M)), S);
+    }
+    const float lse = (float)M + hw_log2(S);
+    const float hat = log2f(h.row_w[i]) - lse;
+    static_cast<float *>(h.row_bias)[i] = hat;
+    h.pot_out[i] = fmaf((float)h.eps_ln2, hat, h.row_nrm[i]);
+}
+
+// ---------------------------------------------------------------------------
+// Records.
+// ---------------------------------------------------------------------------
+
+// Largest |coordinate| of x (blockIdx.y == 0) or y (1), one value per block.
+__global__ __launch_bounds__(256) void maxabs_kernel(const float *__restrict__ x, int64_t nx,
+                                                     const float *__restrict__ y, int64_t ny,
+                                                     float *__restrict__ part) {
+    __shared__ float red[4];
+    const float *p = blockIdx.y ? y : x;
+    const int64_t cnt = blockIdx.y ? ny : nx;
+    float mx = 0.f;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < cnt;
+         e += (int64_t)gridDim.x * 256)
+        mx = fmaxf(mx, fabsf(p[e]));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        part[blockIdx.y * gridDim.x + blockIdx.x] =
+            fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__global__ __launch_bounds__(64) void maxabs_final_kernel(const float *__restrict__ part, int nb,
+                                                          float *__restrict__ out) {
+    const int side = threadIdx.x >> 5;  // lanes 0-31: x, 32-63: y
+    float mx = 0.f;
+    for (int k = threadIdx.x & 31; k < nb; k += 32)
+        mx = fmaxf(mx, part[side * nb + k]);
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1)
+        mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((threadIdx.x & 31) == 0)
+        out[side] = mx;
+}
+
+// Power of two e with (scale * b_own) 2^-e ~ b_other 2^e; 0 for empty data.
+__device__ __forceinline__ int balance_exp(double scale, double b_own, double b_other) {
+    if (!(b_own > 0.0) || !(b_other > 0.0))
+        return 0;
+    double r = 0.5 * log2(scale * b_own / b_other);
+    r = r < -100.0 ? -100.0 : (r > 100.0 ? 100.0 : r);
+    return (int)rint(r);
+}
+
+// hi = f16(v), lo = f16(v - hi), each rounded once to nearest from an fp32
+// value. The empty asm statements keep the compiler from fusing the product,
+// the difference and the conversion into mixed-precision FMAs (v_fma_mix*),
+// whose f16 results lose the subnormal lo parts of small coordinates.
+__device__ __forceinline__ _Float16 split_hi(float v, _Float16 &lo) {
+    asm volatile("" : "+v"(v));
+    const _Float16 hi = (_Float16)v;
+    float r = v - (float)hi;
+    asm volatile("" : "+v"(r));
+    lo = (_Float16)r;
+    return hi;
+}
+
+__device__ __forceinline__ float4 pack8(const _Float16 (&v)[8]) {
+    half8 h;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        h[r] = v[r];
+    return __builtin_bit_cast(float4, h);
+}
+
+// One side's records at one eps: column record (scaled, split, swizzled), row
+// record (split), |p|^2 and the bias (zero, hat of pot, or padding).
+__global__ __launch_bounds__(256) void prep_h3_kernel(
+    const float *__restrict__ pts, const float *__restrict__ pot, int64_t count, int64_t padded,
+    int d, int kp, double scale, double hat_scale, int bias_mode, const float *__restrict__ maxabs,
+    int own, float4 *__restrict__ colrec, float4 *__restrict__ rowrec, float *__restrict__ nrm_out,
+    float *__restrict__ bias) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= padded)
+        return;
+    const double bo = maxabs[own], bt = maxabs[1 - own];
+    const float cf = (float)ldexp(scale, -balance_exp(scale, bo, bt));
+    const float rf = (float)ldexp(1.0, balance_exp(scale, bt, bo));
+    const int rc = kp / 4;
+    const int hc = kp / 8;
+    const int sw = (int)(i & swizzle_mask(rc));
+    const bool real = i < count;
+    double nrm = 0.0;
+    for (int q = 0; q < hc; ++q) {
+        _Float16 ch[8], cl[8], rh[8], rl[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int k = 8 * q + r;
+            const float v = (real && k < d) ? pts[i * d + k] : 0.f;
+            nrm = fma((double)v, (double)v, nrm);
+            ch[r] = split_hi(v * cf, cl[r]);
+            rh[r] = split_hi(v * rf, rl[r]);
+        }
+        colrec[i * rc + (q ^ sw)] = pack8(ch);
+        colrec[i * rc + ((hc + q) ^ sw)] = pack8(cl);
+        rowrec[i * rc + q] = pack8(rh);
+        rowrec[i * rc + hc + q] = pack8(rl);
+    }
+    nrm_out[i] = (float)nrm;
+    float bv = kPadBias;
+    if (real)
+        bv = bias_mode == kBiasHat ? (float)(((double)pot[i] - nrm) * hat_scale)
+                                   : (bias_mode == kBiasRaw ? pot[i] : 0.f);
+    bias[i] = bv;
+}
+
+struct H3Plan {
+    int ntiles;
+    int tiles_per_split;
+    int nsplit;
+    int64_t row_blocks;
+};
+
+H3Plan plan_h3(int64_t rows, int64_t cols_pad) {
+    H3Plan p;
+    p.ntiles = (int)(cols_pad / kTileCols);
+    p.row_blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    int64_t want = (kTargetBlocks + p.row_blocks - 1) / p.row_blocks;
+    if (want > p.ntiles)
+        want = p.ntiles;
+    if (want > 65535)
+        want = 65535;
+    if (want < 1)
+        want = 1;
+    p.tiles_per_split = (int)((p.ntiles + want - 1) / want);
+    p.nsplit = (p.ntiles + p.tiles_per_split - 1) / p.tiles_per_split;
+    return p;
+}
+
+template <int KP>
+hipError_t launch_h3_kp(const HalfStep &h, const H3Plan &p, hipStream_t s) {
+    dim3 grid((unsigned)p.row_blocks, (unsigned)p.nsplit);
+    hipLaunchKernelGGL((lse_rows_h3_kernel<KP>), grid, dim3(kThreads), 0, s, h, p.tiles_per_split,
+                       p.ntiles);
+    return hipGetLastError();
+}
+
+constexpr int kMaxabsBlocks = 256;
+
+}  // namespace
+
+int h3_kp(int d) { return (d + 31) / 32 * 32; }
+
+size_t h3_maxabs_floats() { return 2 * kMaxabsBlocks + 2; }
+
+hipError_t launch_maxabs(const float *x, int64_t nx, const float *y, int64_t ny, float *scratch,
+                         hipStream_t s) {
+    hipLaunchKernelGGL(maxabs_kernel, dim3(kMaxabsBlocks, 2), dim3(256), 0, s, x, nx, y, ny,
+                       scratch + 2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(maxabs_final_kernel, dim3(1), dim3(64), 0, s, scratch + 2, kMaxabsBlocks,
+                       scratch);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep_h3(const float *pts, const float *pot, int64_t count, int64_t padded, int d,
+                          int kp, double scale, double hat_scale, int bias_mode,
+                          const float *maxabs, int own, void *colrec, void *rowrec, float *nrm,
+                          float *bias, hipStream_t s) {
+    const unsigned blocks = (unsigned)((padded + 255) / 256);
+    hipLaunchKernelGGL(prep_h3_kernel, dim3(blocks), dim3(256), 0, s, pts, pot, count, padded, d,
+                       kp, scale, hat_scale, bias_mode, maxabs, own,
+                       static_cast<float4 *>(colrec), static_cast<float4 *>(rowrec), nrm, bias);
+    return hipGetLastError();
+}
+
+size_t half_step_partials_h3(int64_t rows, int64_t cols_pad) {
+    const H3Plan p = plan_h3(rows, cols_pad);
+    return p.nsplit > 1 ? (size_t)p.nsplit * (size_t)pad_points(rows) : 0;
+}
+
+hipError_t launch_half_step_h3(const HalfStep &h, int kp, hipStream_t s) {
+    const H3Plan p = plan_h3(h.rows, h.cols_pad);
+    hipError_t e;
+    switch (kp) {
+    case 32: e = launch_h3_kp<32>(h, p, s); break;
+    case 64: e = launch_h3_kp<64>(h, p, s); break;
+    case 96: e = launch_h3_kp<96>(h, p, s); break;
+    case 128: e = launch_h3_kp<128>(h, p, s); break;
+    default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess || p.nsplit <= 1)
+        return e;
+    hipLaunchKernelGGL(lse_merge_h3_kernel, dim3((unsigned)((h.rows + 255) / 256)), dim3(256), 0,
+                       s, h, p.nsplit);
+    return hipGetLastError();
+}
+
+}  // namespace otsk

@@ -1,7 +1,8 @@
-// Device helpers shared by the fp32 MFMA kernels (the half-step and the
+// Device helpers shared by the MFMA kernels (the half-steps and the
 // transport application): tile copies with gfx950's direct global->LDS
-// loads, and the 32x32 score tile with the bias and a per-row offset folded
-// into one extra v_mfma_f32_32x32x2f32.
+// loads, the 32x32 score tile with the bias and a per-row offset folded into
+// one extra v_mfma_f32_32x32x2f32, and the lazy online log-sum-exp epilogue
+// over the 16 accumulator values a lane holds.
 #pragma once
 
 #include "ot_internal.h"
@@ -10,6 +11,7 @@ namespace otsk {
 namespace mfma {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -64,6 +66,50 @@ __device__ __forceinline__ floatx16 score_tile(const float4 *rec, const float *b
     return acc;
 }
 
+// Common part of the epilogue: the sum of 2^u over the lane's 16 values.
+__device__ __forceinline__ float chunk_sum(const floatx16 &u) {
+    float c0 = hw_exp2(u[0]), c1 = hw_exp2(u[1]);
+#pragma unroll
+    for (int v = 2; v < 16; v += 2) {
+        c0 += hw_exp2(u[v]);
+        c1 += hw_exp2(u[v + 1]);
+    }
+    return c0 + c1;
+}
+
+// Fold a subtile (values u relative to Mu, sum c) into the row's (M, S).
+// Lanes l and l^32 hold the same row and keep the same M.
+__device__ __forceinline__ void fold(const floatx16 &u, float Mu, float c, float &M, float &S) {
+    const bool need = !(c <= 0x1p16f) || !(S + c >= 0x1p-64f) || Mu != M;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+        // Rare (wave-uniform): move M to the larger of this subtile's row
+        // maximum and the mass already accumulated, rescale, recompute c.
+        float mh = u[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v)
+            mh = fmaxf(mh, u[v]);
+        mh = fmaxf(mh + Mu, M + hw_log2(S));
+        const float Mn = fmaxf(mh, __shfl_xor(mh, 32));
+        // S is 0 or >= 2^-64 (the common path only adds when S + c >= 2^-64)
+        // and Mn >= M + log2 S, so the factor stays below 2^64; S = 0 is kept
+        // apart because M may move down by ~1e30 past a padding-only chunk.
+        S = S > 0.f ? S * hw_exp2(M - Mn) : 0.f;
+        const float off = Mn - Mu;
+        float c0 = 0.f, c1 = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; v += 2) {
+            c0 += hw_exp2(u[v] - off);
+            c1 += hw_exp2(u[v + 1] - off);
+        }
+        c = c0 + c1;
+        M = Mn;
+    }
+    S += c;
+}
+
+// Keep the running (M, S) computed here: the fold above it may not be moved
+// past this point (in particular not past the tile barrier that follows).
+__device__ __forceinline__ void pin(float &M, float &S) { asm volatile("" : "+v"(M), "+v"(S)); }
 
 }  // namespace mfma
 }  // namespace otsk

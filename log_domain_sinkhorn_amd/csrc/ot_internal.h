@@ -72,6 +72,7 @@ struct HalfStep {
     double eps_ln2;         // eps*ln(2)
     Partial *partials;      // split-column scratch, >= nsplit * rows_pad entries
     int64_t rows_pad;
+    const float *row_nrm;   // |p_i|^2 of the rows (split-f16 kernel only)
 };
 
 // Launch helpers (each returns hipSuccess or the first HIP error).
@@ -81,9 +82,7 @@ hipError_t launch_prep_side(const float *pts, const float *pot, int64_t count, i
                             const Layout &L, double hat_scale, int bias_mode, void *rec,
                             void *bias, int bias_stride, int bias_off, hipStream_t s);
 hipError_t launch_half_step_valu(const HalfStep &h, const Layout &L, hipStream_t s);
-hipError_t launch_half_step_mfma(const HalfStep &h, const Layout &L, hipStream_t s);
 size_t half_step_partials(const Layout &L, int64_t rows, int64_t cols_pad);
-size_t half_step_partials_mfma(int64_t rows, int64_t cols_pad);
 hipError_t launch_merge(const HalfStep &h, const Layout &L, int nsplit, hipStream_t s);
 
 // x_rec / y_rec: records whose bias slot holds the raw potential (f or g).
@@ -115,6 +114,21 @@ hipError_t launch_values_y1(const float *y, int64_t m, int d, float *v, hipStrea
 // row i of w (row stride ws >= d) and r_i = r[i], or w[i*ws + d] if r is null.
 hipError_t launch_combine(const float *w, int ws, const float *r, const float *x, const float *a,
                           int64_t n, int d, int mode, float *out, hipStream_t s);
+
+// Half-step with split-f16 matrix-core products (d >= 32): records from
+// launch_prep_h3 (column record, row record, |p|^2, fp32 bias per side) after
+// launch_maxabs has written max|x| and max|y| to maxabs[0..1] (scratch of
+// h3_maxabs_floats() floats).
+int h3_kp(int d);
+size_t h3_maxabs_floats();
+hipError_t launch_maxabs(const float *x, int64_t nx, const float *y, int64_t ny, float *scratch,
+                         hipStream_t s);
+hipError_t launch_prep_h3(const float *pts, const float *pot, int64_t count, int64_t padded, int d,
+                          int kp, double scale, double hat_scale, int bias_mode,
+                          const float *maxabs, int own, void *colrec, void *rowrec, float *nrm,
+                          float *bias, hipStream_t s);
+size_t half_step_partials_h3(int64_t rows, int64_t cols_pad);
+hipError_t launch_half_step_h3(const HalfStep &h, int kp, hipStream_t s);
 
 hipError_t launch_birkhoff4(const float *logits, int64_t batch, float eps, int max_iters, float tol,
                             float *out, int32_t *iters_out, hipStream_t s);

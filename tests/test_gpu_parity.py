@@ -104,6 +104,35 @@ def test_shapes(n, m, d):
     _check_solve(c, eps, 10, f"shape {n}x{m}x{d}")
 
 
+# d >= 32 runs on split-f16 matrix-core products (three f16 products per fp32
+# product, fp32 accumulation). The split itself keeps ~22 bits of each
+# coordinate; the matrix core's aligned sums lose about 2^-21 of the largest
+# product per instruction (measured), comparable to fp32 accumulation. These
+# cases use N(0, I) clouds (coordinates up to ~4.5, so products up to ~20 and
+# many coordinates small enough that their lo parts are f16 subnormals), at
+# several eps; one half-step is held to the same bound as the other paths.
+TOL_SPLIT_HALF = TOL_HALF
+
+
+@pytest.mark.parametrize("d,eps_factor", [(32, 0.5), (64, 0.5), (64, 0.1), (128, 0.1), (96, 1.0)])
+def test_split_f16_half_step_on_unit_gaussians(d, eps_factor):
+    c = random_clouds(1024, 1536, d, seed=d, spread=1.0)
+    eps = eps_factor * d ** 0.5
+    fo, go = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, 5)
+    g32 = go.astype(np.float32)
+    f1, g1 = gpu_solve(c, eps, 1, g0=g32)
+    f_ref = oracle.half_update(c["x"], c["y"], c["a"], g32, eps)
+    g_ref = oracle.half_update(c["y"], c["x"], c["b"], f1, eps)
+    ef, eg = rel_inf(f1, f_ref), rel_inf(g1, g_ref)
+    print(f"d={d} eps={eps:.3g}: one half-step rel err f {ef:.2e} g {eg:.2e}", flush=True)
+    assert ef <= TOL_SPLIT_HALF and eg <= TOL_SPLIT_HALF
+
+
+def test_split_f16_long_solve_on_unit_gaussians():
+    c = random_clouds(700, 900, 64, seed=3, spread=1.0)
+    _check_solve(c, 0.25 * 8.0, 60, "d=64 N(0,I) 60 iterations")
+
+
 def test_iters_zero_leaves_potentials():
     c = random_clouds(100, 80, 3, seed=1)
     f0 = np.linspace(-1, 1, 100).astype(np.float32)
