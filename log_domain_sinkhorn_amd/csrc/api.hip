@@ -207,6 +207,49 @@ ot_status check_solve_outputs(const float *x, const float *y, const float *a, co
     return OT_SUCCESS;
 }
 
+// d >= 32: plan statistics on split-f16 records with the hat biases of f
+// and g (the records of the solver at this eps).
+ot_status plan_stats_h3(const float *x, const float *y, const float *a, const float *b,
+                        const float *f, const float *g, int64_t n, int64_t m, int32_t d,
+                        float eps, double *cost, double *marg, hipStream_t s) {
+    const int kp = h3_kp(d);
+    const int64_t n_pad = pad_points(n), m_pad = pad_points(m);
+    const size_t xr = align_up((size_t)n_pad * 4 * kp, 256);
+    const size_t yr = align_up((size_t)m_pad * 4 * kp, 256);
+    const size_t xv = align_up((size_t)n_pad * sizeof(float), 256);
+    const size_t yv = align_up((size_t)m_pad * sizeof(float), 256);
+    const size_t mb = align_up(h3_maxabs_floats() * sizeof(float), 256);
+    const size_t db = plan_stats_h3_scratch_doubles(n, m, n_pad, m_pad) * sizeof(double);
+    Scratch sc(s);
+    hipError_t e = sc.alloc(2 * xr + 2 * yr + 2 * xv + 2 * yv + mb + db);
+    if (e != hipSuccess)
+        return map_error(e);
+    char *p = static_cast<char *>(sc.ptr);
+    void *xcol = p, *xrow = p + xr;
+    p += 2 * xr;
+    void *ycol = p, *yrow = p + yr;
+    p += 2 * yr;
+    float *xnrm = reinterpret_cast<float *>(p), *xhat = reinterpret_cast<float *>(p + xv);
+    p += 2 * xv;
+    float *ynrm = reinterpret_cast<float *>(p), *yhat = reinterpret_cast<float *>(p + yv);
+    p += 2 * yv;
+    float *maxabs = reinterpret_cast<float *>(p);
+    double *dsc = reinterpret_cast<double *>(p + mb);
+    const double scale = 2.0 * kLog2e / (double)eps;
+    const double hat_scale = kLog2e / (double)eps;
+    if ((e = launch_maxabs(x, n * d, y, m * d, maxabs, s)) != hipSuccess)
+        return map_error(e);
+    if ((e = launch_prep_h3(x, f, n, n_pad, d, kp, scale, hat_scale, kBiasHat, maxabs, 0, xcol,
+                            xrow, xnrm, xhat, s)) != hipSuccess)
+        return map_error(e);
+    if ((e = launch_prep_h3(y, g, m, m_pad, d, kp, scale, hat_scale, kBiasHat, maxabs, 1, ycol,
+                            yrow, ynrm, yhat, s)) != hipSuccess)
+        return map_error(e);
+    e = launch_plan_stats_h3(kp, xrow, xcol, xhat, xnrm, yrow, ycol, yhat, ynrm, a, b, n, m, n_pad,
+                             m_pad, scale, cost, marg, dsc, s);
+    return map_error(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -274,6 +317,8 @@ ot_status ot_plan_stats(const float *x, const float *y, const float *a, const fl
     if (st != OT_SUCCESS)
         return st;
     hipStream_t s = (hipStream_t)stream;
+    if (d >= 32)
+        return plan_stats_h3(x, y, a, b, f, g, n, m, d, eps, cost, marg, s);
     // The statistics passes read fp32 records (raw potentials in the bias slot).
     Layout L = choose_layout(d);
     L.f64 = false;

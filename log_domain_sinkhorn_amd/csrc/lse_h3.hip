@@ -316,6 +316,127 @@ __global__ __launch_bounds__(256) void prep_h3_kernel(
     bias[i] = bv;
 }
 
+// ---------------------------------------------------------------------------
+// Plan statistics on the same records: one pass over the columns for each row
+// i gives r_i = sum_j P_ij and (COST) c_i = sum_j P_ij C_ij, with
+// log2 P_ij = (2 log2(e)/eps) p_i.q_j + qhat_j + phat_i from the split-f16
+// chain plus one fp32 MFMA (k-slot 0: qhat_j x 1, k-slot 1: 1 x phat_i), and
+// C_ij = |p_i|^2 + |q_j|^2 - 2 p_i.q_j from the chain's dot product before the
+// bias. Sums are fp32 within a tile of 128 columns and fp64 across tiles; the
+// two lane halves (disjoint columns of one row) are added at the end.
+// ---------------------------------------------------------------------------
+template <int KP, bool COST>
+__global__ __launch_bounds__(kThreads) void plan_rows_h3_kernel(
+    const float4 *__restrict__ row_rec, const float *__restrict__ row_hat,
+    const float *__restrict__ row_nrm, const float4 *__restrict__ col4,
+    const float *__restrict__ colb, const float *__restrict__ col_nrm, int64_t rows,
+    int64_t rows_pad, int tiles_per_split, int ntiles, float inv_scale,
+    double2 *__restrict__ part) {
+    constexpr int RC = KP / 4;
+    constexpr int TILE16 = kTileCols * RC;
+    __shared__ float4 lrec[2][TILE16];
+    __shared__ float lbias[2][kBiasSlots];
+    __shared__ __attribute__((aligned(16))) float lnrm[2][kTileCols];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int hl = lane >> 5;
+    const int li = lane & 31;
+    const int split = blockIdx.y;
+    const int tbeg = split * tiles_per_split;
+    const int tend = min(tbeg + tiles_per_split, ntiles);
+
+    for (int k = tid; k < 2 * kBiasSlots; k += kThreads) {
+        const int e = k % kBiasSlots;
+        if ((e / 32) & 1)
+            lbias[k / kBiasSlots][e] = 1.f;
+    }
+    // Column norms of a tile: waves 0 and 1, one dword per lane.
+    auto issue_norms = [&](int t, float *dst) {
+        if (COST && wave < kTileCols / 64)
+            __builtin_amdgcn_global_load_lds(col_nrm + (int64_t)t * kTileCols + wave * 64 + lane,
+                                             (lds_void *)(dst + wave * 64), 4, 0, 0);
+    };
+    issue_tile<TILE16, kWaves, kSub>(col4, colb, tbeg, lrec[0], lbias[0], wave, lane);
+    issue_norms(tbeg, lnrm[0]);
+    const int64_t i = (int64_t)blockIdx.x * kRowsPerBlock + wave * 32 + li;
+    const int64_t ic = i < rows ? i : rows - 1;
+    half8 bh[KP / 16], bl[KP / 16];
+    {
+        const float4 *rr = row_rec + ic * RC;
+#pragma unroll
+        for (int c = 0; c < KP / 16; ++c) {
+            bh[c] = as_half8(rr[2 * c + hl]);
+            bl[c] = as_half8(rr[KP / 8 + 2 * c + hl]);
+        }
+    }
+    // With Mu = -phat_i the bias MFMA adds qhat_j + phat_i.
+    const float Mu = -row_hat[ic];
+    const float nx = COST ? row_nrm[ic] : 0.f;
+    const float m2 = -2.f * inv_scale;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    double rsum = 0.0, csum = 0.0;
+    for (int t = tbeg; t < tend; ++t) {
+        const int b = (t - tbeg) & 1;
+        if (t + 1 < tend) {
+            issue_tile<TILE16, kWaves, kSub>(col4, colb, t + 1, lrec[b ^ 1], lbias[b ^ 1], wave,
+                                             lane);
+            issue_norms(t + 1, lnrm[b ^ 1]);
+        }
+        float rs = 0.f, cs = 0.f;
+#pragma unroll
+        for (int sub = 0; sub < kSub; ++sub) {
+            constexpr int SW = swizzle_mask(RC);
+            const int j = sub * 32 + li;
+            const float4 *ap = lrec[b] + j * RC;
+            const int sw = j & SW;
+            floatx16 dot = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
+                            0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            half8 qh[KP / 16];
+#pragma unroll
+            for (int c = 0; c < KP / 16; ++c) {
+                qh[c] = as_half8(ap[(2 * c + hl) ^ sw]);
+                const half8 ql = as_half8(ap[(KP / 8 + 2 * c + hl) ^ sw]);
+                dot = __builtin_amdgcn_mfma_f32_32x32x16_f16(ql, bh[c], dot, 0, 0, 0);
+                dot = __builtin_amdgcn_mfma_f32_32x32x16_f16(qh[c], bl[c], dot, 0, 0, 0);
+            }
+#pragma unroll
+            for (int c = 0; c < KP / 16; ++c)
+                dot = __builtin_amdgcn_mfma_f32_32x32x16_f16(qh[c], bh[c], dot, 0, 0, 0);
+            const float a0 = lbias[b][sub * 64 + lane];
+            const float b0 = hl ? -Mu : 1.f;
+            const floatx16 u = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, dot, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float4 ny = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (COST)
+                    ny = *reinterpret_cast<const float4 *>(&lnrm[b][sub * 32 + 8 * q + 4 * hl]);
+                const float nyv[4] = {ny.x, ny.y, ny.z, ny.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float pr = hw_exp2(u[4 * q + r]);
+                    rs += pr;
+                    if (COST) {
+                        const float cij = fmaf(dot[4 * q + r], m2, nx + nyv[r]);
+                        cs = fmaf(pr, cij, cs);
+                    }
+                }
+            }
+        }
+        rsum += (double)rs;
+        csum += (double)cs;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+    const double ro = __shfl_xor(rsum, 32);
+    const double co = __shfl_xor(csum, 32);
+    if (hl == 0 && i < rows)
+        part[(int64_t)split * rows_pad + i] = make_double2(rsum + ro, csum + co);
+}
+
 struct H3Plan {
     int ntiles;
     int tiles_per_split;
@@ -375,6 +496,40 @@ hipError_t launch_prep_h3(const float *pts, const float *pot, int64_t count, int
     hipLaunchKernelGGL(prep_h3_kernel, dim3(blocks), dim3(256), 0, s, pts, pot, count, padded, d,
                        kp, scale, hat_scale, bias_mode, maxabs, own,
                        static_cast<float4 *>(colrec), static_cast<float4 *>(rowrec), nrm, bias);
+    return hipGetLastError();
+}
+
+int plan_pass_h3_splits(int64_t rows, int64_t cols_pad) { return plan_h3(rows, cols_pad).nsplit; }
+
+hipError_t launch_plan_pass_h3(int kp, bool cost, const void *row_rec, const float *row_hat,
+                               const float *row_nrm, const void *col_rec, const float *col_hat,
+                               const float *col_nrm, int64_t rows, int64_t rows_pad,
+                               int64_t cols_pad, double scale, double2 *part, hipStream_t s) {
+    const H3Plan p = plan_h3(rows, cols_pad);
+    dim3 grid((unsigned)p.row_blocks, (unsigned)p.nsplit);
+    const float4 *rr = static_cast<const float4 *>(row_rec);
+    const float4 *cr = static_cast<const float4 *>(col_rec);
+    const float inv = (float)(1.0 / scale);
+#define OTSK_PR(KPV)                                                                           \
+    case KPV:                                                                                  \
+        if (cost)                                                                              \
+            hipLaunchKernelGGL((plan_rows_h3_kernel<KPV, true>), grid, dim3(kThreads), 0, s,  \
+                               rr, row_hat, row_nrm, cr, col_hat, col_nrm, rows, rows_pad,     \
+                               p.tiles_per_split, p.ntiles, inv, part);                        \
+        else                                                                                   \
+            hipLaunchKernelGGL((plan_rows_h3_kernel<KPV, false>), grid, dim3(kThreads), 0, s, \
+                               rr, row_hat, row_nrm, cr, col_hat, col_nrm, rows, rows_pad,     \
+                               p.tiles_per_split, p.ntiles, inv, part);                        \
+        break;
+    switch (kp) {
+        OTSK_PR(32)
+        OTSK_PR(64)
+        OTSK_PR(96)
+        OTSK_PR(128)
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef OTSK_PR
     return hipGetLastError();
 }
 
