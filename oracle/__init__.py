@@ -25,6 +25,11 @@ Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``
 * ``transport_apply``, ``barycentric_map``, ``grad_x``: pinned (n = 1 closed
   form, product-coupling limit, eps -> 0 permutation limit, finite
   differences of the converged dual value, marginal sums).
+* ``birkhoff4_newton``: pinned (same limit as long Sinkhorn-Knopp runs,
+  cross-ratio invariant, doubly stochastic, constant logits need no step,
+  quadratic convergence).
+* ``birkhoff4_backward``: pinned (central finite differences of <G, P(L)>
+  with P from Sinkhorn-Knopp, zero row and column sums of dl/dL).
 """
 from __future__ import annotations
 
@@ -82,6 +87,9 @@ def _load():
                                          ctypes.c_double, _dp, _i32p]
         lib.oracle_birkhoff4_replay.argtypes = [_dp, ctypes.c_int64, ctypes.c_double, _i32p,
                                                 _dp, _dp]
+        lib.oracle_birkhoff4_newton.argtypes = [_dp, ctypes.c_int64, ctypes.c_double, ctypes.c_int,
+                                                ctypes.c_double, _dp, _i32p]
+        lib.oracle_birkhoff4_backward.argtypes = [_dp, _dp, ctypes.c_int64, ctypes.c_double, _dp]
         _lib = lib
         return lib
 
@@ -228,3 +236,29 @@ def birkhoff4_replay(logits, iters, eps: float = 1.0):
     err = np.empty(B)
     _load().oracle_birkhoff4_replay(_ptr(L), B, float(eps), _ptr(it, _i32p), _ptr(P), _ptr(err))
     return P.reshape(B, 4, 4), err
+
+
+def birkhoff4_newton(logits, eps: float = 1.0, max_iters: int = 50, tol: float = 1e-12):
+    """Projection by Newton's method on the 3-variable dual (Birkhoff page,
+    section 2.1), from g = 0 with a backtracking line search; stops before a
+    step once the worst column-sum error is <= tol (tol < 0: exactly
+    max_iters steps). Returns (P, steps)."""
+    L = _d(logits).reshape(-1, 16)
+    B = L.shape[0]
+    P = np.empty((B, 16))
+    it = np.empty(B, dtype=np.int32)
+    _load().oracle_birkhoff4_newton(_ptr(L), B, float(eps), int(max_iters), float(tol), _ptr(P),
+                                    _ptr(it, _i32p))
+    return P.reshape(B, 4, 4), it
+
+
+def birkhoff4_backward(P, grad_P, eps: float = 1.0) -> np.ndarray:
+    """dl/dL for the projection P of L and dl/dP = grad_P, by implicit
+    differentiation at the solution (Birkhoff page, section 2.2)."""
+    Pd = _d(P).reshape(-1, 16)
+    G = _d(grad_P).reshape(-1, 16)
+    if Pd.shape != G.shape:
+        raise ValueError("shape mismatch")
+    out = np.empty_like(Pd)
+    _load().oracle_birkhoff4_backward(_ptr(Pd), _ptr(G), Pd.shape[0], float(eps), _ptr(out))
+    return out.reshape(-1, 4, 4)

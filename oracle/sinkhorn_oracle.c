@@ -19,7 +19,11 @@
  *    para Hiper-conexiones ...", section 2 and its French twin): projecting a
  *    4x4 matrix onto the doubly-stochastic matrices is entropic OT with unit
  *    marginals, iterated by Sinkhorn-Knopp; section 2.1 subtracts the maximum
- *    before exponentiating; section 1 names 20 fixed iterations.
+ *    before exponentiating; section 1 names 20 fixed iterations. Section 2.1
+ *    also solves the dual by Newton's method in the 3 free variables left
+ *    after removing the shift, with closed-form gradient and Hessian;
+ *    section 2.2 differentiates the projection implicitly, with the matrix of
+ *    the last Newton step.
  *
  * Convention (the pages put log b inside the log-sum-exp; here eps*log a sits
  * outside it, which gives the same plan with f' = f + eps log a and
@@ -284,5 +288,174 @@ void oracle_birkhoff4_replay(const double *L, int64_t B, double eps,
         double e = birk_plan(Lb, eps, f, g, P + 16 * bi);
         if (err)
             err[bi] = e;
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* 4x4 projection by Newton's method on the dual, and its backward.         */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * Semi-dual of the 4x4 problem (a = b = 1, cost -L): for column potentials
+ * g (g[3] = 0 removes the shift (f + c, g - c)), the row potentials are
+ * f_i(g) = -eps LSE_j((g_j + L_ij)/eps), P_ij = exp((f_i + g_j + L_ij)/eps)
+ * has unit row sums, and the concave objective
+ *     F(g) = sum_i f_i(g) + sum_j g_j
+ * has gradient dF/dg_j = 1 - c_j (c_j the column sums of P) and Hessian
+ *     d2F/dg_j dg_k = -(c_j delta_jk - sum_i P_ij P_ik) / eps.
+ * Row softmax with the row maximum subtracted first.
+ */
+static double birk_rows(const double L[16], double eps, const double g[4], double P[16],
+                        double *mag)
+{
+    double F = g[0] + g[1] + g[2] + g[3];
+    double m = fabs(g[0]) + fabs(g[1]) + fabs(g[2]) + fabs(g[3]);
+    for (int i = 0; i < 4; ++i) {
+        double v[4];
+        for (int j = 0; j < 4; ++j)
+            v[j] = (g[j] + L[4 * i + j]) / eps;
+        double mx = v[0];
+        for (int j = 1; j < 4; ++j)
+            if (v[j] > mx)
+                mx = v[j];
+        double s = 0.0;
+        for (int j = 0; j < 4; ++j)
+            s += exp(v[j] - mx);
+        for (int j = 0; j < 4; ++j)
+            P[4 * i + j] = exp(v[j] - mx) / s;
+        F -= eps * (mx + log(s));
+        m += fabs(eps * (mx + log(s)));
+    }
+    if (mag)
+        *mag = m;
+    return F;
+}
+
+/* Solve the symmetric positive definite 3x3 system A x = r (Cholesky). */
+static void spd3_solve(const double A[9], const double r[3], double x[3])
+{
+    double l00 = sqrt(A[0]);
+    double l10 = A[3] / l00, l20 = A[6] / l00;
+    double l11 = sqrt(A[4] - l10 * l10);
+    double l21 = (A[7] - l20 * l10) / l11;
+    double l22 = sqrt(A[8] - l20 * l20 - l21 * l21);
+    double y0 = r[0] / l00;
+    double y1 = (r[1] - l10 * y0) / l11;
+    double y2 = (r[2] - l20 * y0 - l21 * y1) / l22;
+    x[2] = y2 / l22;
+    x[1] = (y1 - l21 * x[2]) / l11;
+    x[0] = (y0 - l10 * x[1] - l20 * x[2]) / l00;
+}
+
+/* -H restricted to the free coordinates 0..2: (c_j delta_jk - sum_i P_ij P_ik)/eps. */
+static void birk_neg_hessian(const double P[16], double eps, double A[9])
+{
+    for (int j = 0; j < 3; ++j)
+        for (int k = 0; k < 3; ++k) {
+            double s = 0.0, c = 0.0;
+            for (int i = 0; i < 4; ++i) {
+                s += P[4 * i + j] * P[4 * i + k];
+                c += P[4 * i + j];
+            }
+            A[3 * j + k] = ((j == k ? c : 0.0) - s) / eps;
+        }
+}
+
+/*
+ * Newton's method on F from g = 0, with a backtracking (Armijo) line search:
+ * the step length halves until F rises by at least 1e-4 of the linear
+ * prediction, less the rounding of F itself (1e-13 of the magnitude of its
+ * terms), so that steps below the resolution of F are accepted as they are.
+ * Before each step the plan of the current g is formed; with tol >= 0 the
+ * loop stops when its worst column-sum error (rows are exact) is <= tol,
+ * else after max_iters steps; tol < 0 runs exactly max_iters steps.
+ * iters_out (nullable) gets the number of Newton steps taken; P the plan.
+ */
+void oracle_birkhoff4_newton(const double *L, int64_t B, double eps, int max_iters,
+                             double tol, double *P, int32_t *iters_out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t bi = 0; bi < B; ++bi) {
+        const double *Lb = L + 16 * bi;
+        double g[4] = {0, 0, 0, 0}, Pc[16];
+        int k = 0;
+        for (;;) {
+            double mag;
+            double F = birk_rows(Lb, eps, g, Pc, &mag);
+            double grad[3], err = 0.0;
+            for (int j = 0; j < 4; ++j) {
+                double c = Pc[j] + Pc[4 + j] + Pc[8 + j] + Pc[12 + j];
+                if (fabs(c - 1.0) > err)
+                    err = fabs(c - 1.0);
+                if (j < 3)
+                    grad[j] = 1.0 - c;
+            }
+            if ((tol >= 0.0 && err <= tol) || k >= max_iters)
+                break;
+            double A[9], step[3];
+            birk_neg_hessian(Pc, eps, A);
+            spd3_solve(A, grad, step); /* ascent direction: (-H)^-1 grad */
+            double slope = grad[0] * step[0] + grad[1] * step[1] + grad[2] * step[2];
+            double t = 1.0;
+            for (int ls = 0; ls < 60; ++ls) {
+                double gt[4] = {g[0] + t * step[0], g[1] + t * step[1], g[2] + t * step[2], 0.0};
+                double tmp[16];
+                if (birk_rows(Lb, eps, gt, tmp, NULL) >= F + 1e-4 * t * slope - 1e-13 * mag)
+                    break;
+                t *= 0.5;
+            }
+            for (int j = 0; j < 3; ++j)
+                g[j] += t * step[j];
+            ++k;
+        }
+        for (int e = 0; e < 16; ++e)
+            P[16 * bi + e] = Pc[e];
+        if (iters_out)
+            iters_out[bi] = k;
+    }
+}
+
+/*
+ * Backward of the projection by implicit differentiation. With P the
+ * projection of L, G = dl/dP and r_i = sum_j P_ij G_ij:
+ *   direct part      dl/dL_ij |g fixed = P_ij (G_ij - r_i) / eps,
+ *   through g        dl/dg_j = sum_i P_ij (G_ij - r_i) / eps   (j = 0..2),
+ *   and the optimality 1 - c(g, L) = 0 gives dg = H^-1 (dc/dL) dL, so
+ *   dl/dL_il = P_il (G_il - r_i + lam_l - (P lam)_i) / eps,
+ * with -H lam = -dl/dg, i.e. lam = H^-1 dl/dg on coordinates 0..2, lam_3 = 0,
+ * and H the Hessian of F at the solution (the matrix of the last Newton
+ * step). gradL (B x 16) receives dl/dL.
+ */
+void oracle_birkhoff4_backward(const double *P, const double *G, int64_t B, double eps,
+                               double *gradL)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t bi = 0; bi < B; ++bi) {
+        const double *Pb = P + 16 * bi, *Gb = G + 16 * bi;
+        double r[4];
+        for (int i = 0; i < 4; ++i) {
+            r[i] = 0.0;
+            for (int j = 0; j < 4; ++j)
+                r[i] += Pb[4 * i + j] * Gb[4 * i + j];
+        }
+        double w[3];
+        for (int j = 0; j < 3; ++j) {
+            w[j] = 0.0;
+            for (int i = 0; i < 4; ++i)
+                w[j] += Pb[4 * i + j] * (Gb[4 * i + j] - r[i]) / eps;
+        }
+        /* lam = H^-1 w = -(-H)^-1 w */
+        double A[9], mlam[3];
+        birk_neg_hessian(Pb, eps, A);
+        spd3_solve(A, w, mlam);
+        double lam[4] = {-mlam[0], -mlam[1], -mlam[2], 0.0};
+        for (int i = 0; i < 4; ++i) {
+            double pl = 0.0;
+            for (int l = 0; l < 4; ++l)
+                pl += Pb[4 * i + l] * lam[l];
+            for (int l = 0; l < 4; ++l)
+                gradL[16 * bi + 4 * i + l] =
+                    Pb[4 * i + l] * (Gb[4 * i + l] - r[i] + lam[l] - pl) / eps;
+        }
     }
 }

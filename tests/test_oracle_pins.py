@@ -428,6 +428,104 @@ def test_birkhoff_fixed20_sigma_split():
 
 
 # --------------------------------------------------------------------------- #
+# 4x4 projection by Newton's method on the dual, and its backward             #
+# (Birkhoff page, sections 2.1 and 2.2)                                        #
+# --------------------------------------------------------------------------- #
+
+def test_newton_limit_matches_long_sinkhorn():
+    # Sinkhorn's theorem: one doubly-stochastic matrix of the form
+    # diag(u) exp(L/eps) diag(v); Sinkhorn-Knopp (a different algorithm)
+    # reaches it after enough iterations.
+    L = make_logits(64, (1.0, 2.0), seed=40)
+    for eps in (1.0, 0.5):
+        Pn, it = oracle.birkhoff4_newton(L, eps, 100, 1e-13)
+        Ps, its = oracle.birkhoff4(L, eps, 1000000, 1e-13)
+        assert np.all(it < 100) and np.all(its < 1000000)
+        np.testing.assert_allclose(Pn, Ps, atol=1e-10)
+
+
+def test_newton_plan_structure_and_marginals():
+    L = make_logits(256, (1.0, 10.0), seed=41).astype(np.float64)
+    P, it = oracle.birkhoff4_newton(L, 1.0, 100, 1e-12)
+    assert np.all(it < 100)
+    np.testing.assert_allclose(P.sum(axis=2), 1.0, atol=1e-13)   # rows exact by construction
+    np.testing.assert_allclose(P.sum(axis=1), 1.0, atol=1e-12)   # columns to tol
+    # every plan is diag(u) exp(L) diag(v): cross ratios are those of exp(L)
+    for (i, k), (j, l) in [((0, 1), (0, 2)), ((2, 3), (1, 3)), ((0, 3), (1, 2))]:
+        lhs = np.log(P[:, i, j]) + np.log(P[:, k, l]) - np.log(P[:, i, l]) - np.log(P[:, k, j])
+        rhs = L[:, i, j] + L[:, k, l] - L[:, i, l] - L[:, k, j]
+        assert np.all(np.abs(lhs - rhs) <= 1e-8 * (1 + np.abs(rhs)))
+
+
+def test_newton_constant_and_circulant_need_no_step():
+    # Constant or circulant logits: the first row softmax (g = 0) already has
+    # unit column sums, so no Newton step is taken.
+    c = np.array([0.3, -1.2, 2.0, 0.7])
+    circ = np.array([[c[(j - i) % 4] for j in range(4)] for i in range(4)])
+    L = np.stack([np.full((4, 4), -3.0), circ])
+    P, it = oracle.birkhoff4_newton(L, 1.0, 50, 1e-13)
+    assert list(it) == [0, 0]
+    np.testing.assert_allclose(P[0], 0.25, rtol=1e-14)
+    K = np.exp(circ)
+    np.testing.assert_allclose(P[1], K / K.sum(axis=1, keepdims=True), rtol=1e-13)
+
+
+def test_newton_converges_quadratically():
+    # Quadratic convergence at the end: the step that reaches 1e-12 starts
+    # from an error below 1e-5 (a linearly converging method with the
+    # observed early contraction, ~0.4 per step, would need ~1e-12 there).
+    # Large-magnitude logits (N(0, 10^2)) converge in few steps where 20
+    # Sinkhorn-Knopp iterations do not.
+    L = make_logits(512, (1.0, 10.0), seed=42)
+    P, it12 = oracle.birkhoff4_newton(L, 1.0, 200, 1e-12)
+    assert np.max(it12) <= 40 and np.median(it12[256:]) <= 12
+    for k in range(0, 512, 8):
+        if it12[k] == 0:
+            continue
+        Pk, _ = oracle.birkhoff4_newton(L[k:k + 1], 1.0, int(it12[k]) - 1, -1.0)
+        assert np.abs(Pk.sum(1) - 1).max() <= 1e-5
+    P20, _ = oracle.birkhoff4(L[256:], 1.0, 20, -1.0)   # columns exact after its g step
+    err20 = np.abs(P20.sum(2) - 1).max(1)
+    assert np.median(err20) > 1e-6 and np.median(it12[256:]) < 20
+
+
+def _loss_of_logits(L, G, eps):
+    P, it = oracle.birkhoff4(L, eps, 200000, 1e-15)
+    return float((P * G).sum())
+
+
+@pytest.mark.parametrize("eps,sigma", [(1.0, 1.0), (0.5, 2.0), (1.0, 4.0)])
+def test_backward_matches_finite_differences(eps, sigma):
+    rng = np.random.default_rng(43)
+    L = rng.normal(0.0, sigma, size=(1, 4, 4))
+    G = rng.normal(size=(1, 4, 4))
+    P, _ = oracle.birkhoff4_newton(L, eps, 100, 1e-14)
+    grad = oracle.birkhoff4_backward(P, G, eps)[0]
+    h = 1e-5
+    fd = np.empty((4, 4))
+    for i in range(4):
+        for j in range(4):
+            Lp, Lm = L.copy(), L.copy()
+            Lp[0, i, j] += h
+            Lm[0, i, j] -= h
+            fd[i, j] = (_loss_of_logits(Lp, G, eps) - _loss_of_logits(Lm, G, eps)) / (2 * h)
+    np.testing.assert_allclose(grad, fd, atol=1e-7 * (1 + np.abs(fd).max()))
+
+
+def test_backward_row_and_column_sums_vanish():
+    # Adding a constant to a row or a column of L leaves the projection
+    # unchanged, so dl/dL has zero row and column sums.
+    L = make_logits(128, (1.0, 5.0), seed=44)
+    rng = np.random.default_rng(45)
+    G = rng.normal(size=L.shape)
+    P, _ = oracle.birkhoff4_newton(L, 1.0, 100, 1e-14)
+    gL = oracle.birkhoff4_backward(P, G, 1.0)
+    scale = np.abs(gL).max(axis=(1, 2))
+    assert np.all(np.abs(gL.sum(axis=2)).max(axis=1) <= 1e-10 * (1 + scale))
+    assert np.all(np.abs(gL.sum(axis=1)).max(axis=1) <= 1e-9 * (1 + scale))
+
+
+# --------------------------------------------------------------------------- #
 # Transport application (FlashSinkhorn page, Methodik section 3)               #
 # --------------------------------------------------------------------------- #
 
