@@ -264,6 +264,37 @@ def run_birkhoff(name, torch, lds, reps=5):
             "hbm_gb_per_s": w.batch * (64 + 64 + 4) / (ms / 1e3) / 1e9}
 
 
+def run_birkhoff_newton(name, torch, lds, reps=5):
+    """Newton forward (tol 1e-6, cap 50 steps) and the implicit backward on the
+    batch of ``name``; the backward is HBM-bound (plan and dl/dP in, dl/dL
+    out: 192 bytes per matrix)."""
+    from workloads import BIRKHOFF_WORKLOADS, make_logits
+
+    w = BIRKHOFF_WORKLOADS[name]
+    L = torch.from_numpy(make_logits(w.batch, w.sigmas, seed=0)).to("cuda:0")
+    out = torch.empty_like(L)
+    grad = torch.randn(L.shape, generator=torch.Generator().manual_seed(1)).to(L.device)
+    gl = torch.empty_like(L)
+    it = torch.empty(w.batch, dtype=torch.int32, device=L.device)
+    lds.ot_birkhoff_project_newton_batched(L, w.eps, 50, 1e-6, out, it)
+    lds.ot_birkhoff_projection_backward_batched(out, grad, w.eps, gl)
+    torch.cuda.synchronize()
+    with Timer(torch) as tf:
+        for _ in range(reps):
+            lds.ot_birkhoff_project_newton_batched(L, w.eps, 50, 1e-6, out, it)
+    with Timer(torch) as tb:
+        for _ in range(reps):
+            lds.ot_birkhoff_projection_backward_batched(out, grad, w.eps, gl)
+    fms, bms = tf.ms() / reps, tb.ms() / reps
+    steps = it.to(torch.int64)
+    return {"name": f"{name}:newton", "batch": w.batch, "tol": 1e-6, "max_steps": 50,
+            "forward_ms": fms, "backward_ms": bms,
+            "forward_matrices_per_s": w.batch / (fms / 1e3),
+            "forward_backward_matrices_per_s": w.batch / ((fms + bms) / 1e3),
+            "mean_steps": float(steps.float().mean().item()), "max_steps_taken": int(steps.max()),
+            "backward_hbm_gb_per_s": w.batch * 192 / (bms / 1e3) / 1e9}
+
+
 def run_transport(name, torch, lds, reps=3):
     """Transport application P·y (values = the target points) and the
     x-gradient at the potentials of a short solve of workload ``name``."""
@@ -355,6 +386,9 @@ def main():
                 continue
             print(f"# secondary {name}", file=sys.stderr, flush=True)
             sec[name] = run_birkhoff(name, torch, lds)
+        if wanted is None or "birkhoff4x4_1m:newton" in wanted:
+            print("# secondary birkhoff4x4_1m:newton", file=sys.stderr, flush=True)
+            sec["birkhoff4x4_1m:newton"] = run_birkhoff_newton("birkhoff4x4_1m", torch, lds)
         out["secondary"] = sec
     print(json.dumps(out))
 

@@ -208,6 +208,63 @@ ot_status ot_birkhoff_project_batched(const float *logits, int64_t batch,
                                       float *out, int32_t *iters_out,
                                       void *stream);
 
+/*
+ * ot_birkhoff_project_newton_batched -- the same projection as
+ * ot_birkhoff_project_batched, computed by Newton's method on the dual (page
+ * "Aceleración de la Proyección de Birkhoff ...", section 2.1): after fixing
+ * g_4 = 0 (the dual is invariant under (f + c, g - c)) the row potentials are
+ * eliminated, f_i(g) = -eps*LSE_j((g_j + L_ij)/eps), and the concave
+ * F(g) = sum_i f_i(g) + sum_j g_j of the 3 free g_j is maximised with its
+ * closed-form gradient 1 - c_j (c_j = column sums of the plan) and Hessian
+ * -(c_j delta_jk - sum_i P_ij P_ik)/eps, each step halved until F rises by
+ * 1e-4 of the linear prediction (less the rounding of F). The plan written
+ * is the row softmax of the final g: rows sum to 1 up to rounding.
+ *
+ *   logits    [batch*16]  row-major 4x4 matrices L (fp32, 16-byte aligned)
+ *   batch     >= 0        (0 is a no-op)
+ *   eps       > 0 and finite
+ *   max_iters >= 0        cap on Newton steps (0 returns the row softmax of L/eps)
+ *   tol       < 0: take exactly max_iters steps;
+ *             >= 0: stop before a step once the plan, as written in fp32, has
+ *             every row and column sum within tol of 1. NaN is invalid.
+ *   out       [batch*16]  result; may alias logits exactly (in place)
+ *   iters_out [batch]     nullable; Newton steps each matrix took (int32)
+ *
+ * Errors: as ot_birkhoff_project_batched.
+ */
+ot_status ot_birkhoff_project_newton_batched(const float *logits, int64_t batch,
+                                             float eps, int32_t max_iters,
+                                             float tol, float *out,
+                                             int32_t *iters_out, void *stream);
+
+/*
+ * ot_birkhoff_projection_backward_batched -- dl/dL of the projection by
+ * implicit differentiation at the solution (page "Aceleración de la
+ * Proyección de Birkhoff ...", section 2.2): with P the projection of L,
+ * G = dl/dP and r_i = sum_j P_ij G_ij,
+ *
+ *   A lam = -w,  w_j = sum_i P_ij (G_ij - r_i),  A = diag(c) - P^T P
+ *                (coordinates j, k < 3, lam_4 = 0; A is -eps times the
+ *                Hessian of the last Newton step, recomputed from P),
+ *   dl/dL_ij = P_ij (G_ij - r_i + lam_j - sum_k P_ik lam_k) / eps.
+ *
+ * Exact at a doubly-stochastic P; no forward iterate is stored or replayed.
+ *
+ *   plan        [batch*16]  the forward's output (fp32, 16-byte aligned)
+ *   grad_plan   [batch*16]  dl/dP (fp32, 16-byte aligned)
+ *   batch       >= 0
+ *   eps         > 0 and finite, the forward's eps
+ *   grad_logits [batch*16]  dl/dL; may alias plan or grad_plan exactly
+ *
+ * Errors: INVALID_VALUE (null pointers, batch < 0, eps <= 0 or not finite,
+ * misaligned pointers, partial overlaps), LAUNCH_FAILURE.
+ */
+ot_status ot_birkhoff_projection_backward_batched(const float *plan,
+                                                  const float *grad_plan,
+                                                  int64_t batch, float eps,
+                                                  float *grad_logits,
+                                                  void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,6 +36,8 @@ __all__ = [
     "ot_barycentric_map",
     "ot_cost_gradient_x",
     "ot_birkhoff_project_batched",
+    "ot_birkhoff_project_newton_batched",
+    "ot_birkhoff_projection_backward_batched",
     "OT_MAX_DIM",
     "OT_MAX_VALUE_DIM",
 ]
@@ -74,6 +76,9 @@ _SIGNATURES = {
     "ot_barycentric_map": ([_p, _p, _p, _p, _p, _i64, _i64, _i32, _f32, _p, _p], ctypes.c_int),
     "ot_cost_gradient_x": ([_p, _p, _p, _p, _i64, _i64, _i32, _f32, _p, _p], ctypes.c_int),
     "ot_birkhoff_project_batched": ([_p, _i64, _f32, _i32, _f32, _p, _p, _p], ctypes.c_int),
+    "ot_birkhoff_project_newton_batched": ([_p, _i64, _f32, _i32, _f32, _p, _p, _p],
+                                           ctypes.c_int),
+    "ot_birkhoff_projection_backward_batched": ([_p, _p, _i64, _f32, _p, _p], ctypes.c_int),
 }
 
 
@@ -294,3 +299,31 @@ def ot_birkhoff_project_batched(logits, eps: float, max_iters: int, tol: float, 
         _dev_tensor(iters_out, "iters_out", "i32", (batch,))
     _call("ot_birkhoff_project_batched", _ptr(logits), batch, float(eps), int(max_iters),
           float(tol), _ptr(out), _ptr(iters_out), _stream_of(logits, stream))
+
+
+def ot_birkhoff_project_newton_batched(logits, eps: float, max_iters: int, tol: float, out,
+                                       iters_out=None, stream=None) -> None:
+    """Newton's method on the 3-variable dual; same arguments as
+    :func:`ot_birkhoff_project_batched` (``iters_out`` gets Newton steps)."""
+    _dev_tensor(logits, "logits", "f32")
+    if logits.dim() != 3 or tuple(logits.shape[1:]) != (4, 4):
+        raise ValueError("logits must be (batch, 4, 4)")
+    batch = logits.shape[0]
+    _dev_tensor(out, "out", "f32", (batch, 4, 4))
+    if iters_out is not None:
+        _dev_tensor(iters_out, "iters_out", "i32", (batch,))
+    _call("ot_birkhoff_project_newton_batched", _ptr(logits), batch, float(eps), int(max_iters),
+          float(tol), _ptr(out), _ptr(iters_out), _stream_of(logits, stream))
+
+
+def ot_birkhoff_projection_backward_batched(plan, grad_plan, eps: float, grad_logits,
+                                            stream=None) -> None:
+    """dl/dL (batch, 4, 4) from the projection ``plan`` and dl/dP ``grad_plan``."""
+    _dev_tensor(plan, "plan", "f32")
+    if plan.dim() != 3 or tuple(plan.shape[1:]) != (4, 4):
+        raise ValueError("plan must be (batch, 4, 4)")
+    batch = plan.shape[0]
+    _dev_tensor(grad_plan, "grad_plan", "f32", (batch, 4, 4))
+    _dev_tensor(grad_logits, "grad_logits", "f32", (batch, 4, 4))
+    _call("ot_birkhoff_projection_backward_batched", _ptr(plan), _ptr(grad_plan), batch,
+          float(eps), _ptr(grad_logits), _stream_of(plan, stream))

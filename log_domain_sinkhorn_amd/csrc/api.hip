@@ -508,4 +508,40 @@ ot_status ot_birkhoff_project_batched(const float *logits, int64_t batch, float 
                                       (hipStream_t)stream));
 }
 
+ot_status ot_birkhoff_project_newton_batched(const float *logits, int64_t batch, float eps,
+                                             int32_t max_iters, float tol, float *out,
+                                             int32_t *iters_out, void *stream) {
+    if (!logits || !out || batch < 0 || !finite_pos(eps) || max_iters < 0 || isnan(tol))
+        return OT_ERROR_INVALID_VALUE;
+    if (((uintptr_t)logits & 15) || ((uintptr_t)out & 15))
+        return OT_ERROR_INVALID_VALUE;
+    const size_t bytes = (size_t)batch * 16 * sizeof(float);
+    if (logits != out && overlaps(logits, bytes, out, bytes))
+        return OT_ERROR_INVALID_VALUE;
+    if (iters_out && (overlaps(iters_out, (size_t)batch * 4, out, bytes) ||
+                      overlaps(iters_out, (size_t)batch * 4, logits, bytes)))
+        return OT_ERROR_INVALID_VALUE;
+    if (batch == 0)
+        return OT_SUCCESS;
+    return map_error(launch_birkhoff4_newton(logits, batch, eps, max_iters, tol, out, iters_out,
+                                             (hipStream_t)stream));
+}
+
+ot_status ot_birkhoff_projection_backward_batched(const float *plan, const float *grad_plan,
+                                                  int64_t batch, float eps, float *grad_logits,
+                                                  void *stream) {
+    if (!plan || !grad_plan || !grad_logits || batch < 0 || !finite_pos(eps))
+        return OT_ERROR_INVALID_VALUE;
+    if (((uintptr_t)plan & 15) || ((uintptr_t)grad_plan & 15) || ((uintptr_t)grad_logits & 15))
+        return OT_ERROR_INVALID_VALUE;
+    const size_t bytes = (size_t)batch * 16 * sizeof(float);
+    if ((grad_logits != plan && overlaps(grad_logits, bytes, plan, bytes)) ||
+        (grad_logits != grad_plan && overlaps(grad_logits, bytes, grad_plan, bytes)))
+        return OT_ERROR_INVALID_VALUE;
+    if (batch == 0)
+        return OT_SUCCESS;
+    return map_error(launch_birkhoff4_backward(plan, grad_plan, batch, eps, grad_logits,
+                                               (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -152,4 +152,271 @@ hipError_t launch_birkhoff4(const float *logits, int64_t batch, float eps, int m
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Newton's method on the dual ("Aceleración de la Proyección de Birkhoff ...",
+// section 2.1) and the implicit-differentiation backward (section 2.2).
+//
+// Semi-dual in base 2, with l_ij = L_ij log2(e)/eps and column potentials g
+// (g_3 = 0 removes the shift (f + c, g - c); 3 free variables):
+//   f_i(g) = -log2 sum_j 2^(g_j + l_ij),  P_ij = 2^(f_i + g_j + l_ij),
+//   F(g)   = sum_i f_i(g) + sum_j g_j   (concave),
+//   dF/dg_j = 1 - c_j,   d2F/dg_j dg_k = -ln2 (c_j delta_jk - sum_i P_ij P_ik),
+// c_j the column sums (rows sum to 1 by construction). Each step solves the
+// 3x3 system by Cholesky and backtracks (halving) until F rises by 1e-4 of
+// the linear prediction, less the rounding of F. One matrix per lane; the
+// exponents g_j + l_ij, the row maxima, F and the Hessian are fp64 (fp64
+// VALU issues at the fp32 rate on gfx950) and 2^x is v_exp_f32 of the
+// max-subtracted exponent, so P carries fp32 rounding only, not the rounding
+// of exponents of size |l| (up to ~60 for N(0, 10^2) logits).
+// ---------------------------------------------------------------------------
+namespace {
+
+// Longest Newton move per step in any dual coordinate (log2 units). Only a
+// guard against overflow of g: a nearly flat direction (a column with almost
+// no mass) asks for a long move, and the line search, not a short cap, has to
+// find how much of it to take (a cap of 32..256 made such matrices oscillate
+// between the cap's ends).
+constexpr double kMaxStep = 1e4;
+// Halvings of the line search (2^-60 of a 1e4 move is below fp64 resolution
+// of g).
+constexpr int kLineSearch = 60;
+
+// Row softmax of t_ij = g_j + l_ij: P (fp32, rows as written), returns F.
+__device__ __forceinline__ double newton_rows(const double l[4][4], const double g[4],
+                                              float P[4][4], double &mag) {
+    double F = g[0] + g[1] + g[2];
+    mag = fabs(g[0]) + fabs(g[1]) + fabs(g[2]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        double t[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            t[j] = g[j] + l[i][j];
+        const double m = fmax(fmax(t[0], t[1]), fmax(t[2], t[3]));
+        float e[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            e[j] = hw_exp2((float)(t[j] - m));
+        const float sum = (e[0] + e[1]) + (e[2] + e[3]);
+        const float inv = 1.f / sum;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            P[i][j] = e[j] * inv;
+        const double fi = -(m + (double)hw_log2(sum));
+        F += fi;
+        mag += fabs(fi);
+    }
+    return F;
+}
+
+// F only (line-search trials).
+__device__ __forceinline__ double newton_objective(const double l[4][4], const double g[4]) {
+    double F = g[0] + g[1] + g[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        double t[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            t[j] = g[j] + l[i][j];
+        const double m = fmax(fmax(t[0], t[1]), fmax(t[2], t[3]));
+        const float sum = (hw_exp2((float)(t[0] - m)) + hw_exp2((float)(t[1] - m))) +
+                          (hw_exp2((float)(t[2] - m)) + hw_exp2((float)(t[3] - m)));
+        F -= m + (double)hw_log2(sum);
+    }
+    return F;
+}
+
+// A = diag(c) - P^T P on the free coordinates 0..2 (fp64), A symmetric.
+__device__ __forceinline__ void gram3(const float P[4][4], double A[3][3], double c[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        c[j] = ((double)P[0][j] + (double)P[1][j]) + ((double)P[2][j] + (double)P[3][j]);
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int k = 0; k <= j; ++k) {
+            double s = 0.0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s = fma((double)P[i][j], (double)P[i][k], s);
+            A[j][k] = (j == k ? c[j] : 0.0) - s;
+            A[k][j] = A[j][k];
+        }
+}
+
+// Solve A x = r for symmetric positive (semi)definite A by Cholesky. A is
+// formed from an fp32 plan, so its entries carry ~1e-7 of rounding and a
+// column with no mass (its entries below fp32's range) makes it singular;
+// pivots are floored at 1e-13 of the largest diagonal entry, which keeps the
+// solve finite and leaves well-conditioned systems untouched.
+__device__ __forceinline__ void chol3_solve(const double A[3][3], const double r[3],
+                                            double x[3]) {
+    const double floor_ = 1e-300 + 1e-13 * fmax(fmax(A[0][0], A[1][1]), A[2][2]);
+    const double l00 = sqrt(fmax(A[0][0], floor_));
+    const double l10 = A[1][0] / l00, l20 = A[2][0] / l00;
+    const double l11 = sqrt(fmax(A[1][1] - l10 * l10, floor_));
+    const double l21 = (A[2][1] - l20 * l10) / l11;
+    const double l22 = sqrt(fmax(A[2][2] - l20 * l20 - l21 * l21, floor_));
+    const double y0 = r[0] / l00;
+    const double y1 = (r[1] - l10 * y0) / l11;
+    const double y2 = (r[2] - l20 * y0 - l21 * y1) / l22;
+    x[2] = y2 / l22;
+    x[1] = (y1 - l21 * x[2]) / l11;
+    x[0] = (y0 - l10 * x[1] - l20 * x[2]) / l00;
+}
+
+__global__ __launch_bounds__(256) void birkhoff4_newton_kernel(const float *logits,
+                                                               int64_t batch, double scale,
+                                                               int max_iters, float tol,
+                                                               float *out, int32_t *iters_out) {
+    const int64_t bi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (bi >= batch)
+        return;
+    const float4 *src = reinterpret_cast<const float4 *>(logits) + 4 * bi;
+    double l[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float4 v = src[r];
+        l[r][0] = v.x * scale;
+        l[r][1] = v.y * scale;
+        l[r][2] = v.z * scale;
+        l[r][3] = v.w * scale;
+    }
+    double g[4] = {0.0, 0.0, 0.0, 0.0};
+    float P[4][4];
+    int k = 0;
+    for (;;) {
+        double mag;
+        const double F = newton_rows(l, g, P, mag);
+        if ((tol >= 0.f && plan_error(P) <= tol) || k >= max_iters)
+            break;
+        double A[3][3], c[4];
+        gram3(P, A, c);
+        const double grad[3] = {1.0 - c[0], 1.0 - c[1], 1.0 - c[2]};
+        double step[3];
+        chol3_solve(A, grad, step);
+        // (ln2 A)^-1 grad, at most kMaxStep log2 units in any coordinate.
+        double len = 0.0;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            step[j] *= 1.4426950408889634;
+            len = fmax(len, fabs(step[j]));
+        }
+        const double shrink = len > kMaxStep ? kMaxStep / len : 1.0;
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            step[j] *= shrink;
+        const double slope = grad[0] * step[0] + grad[1] * step[1] + grad[2] * step[2];
+        // F carries ~1e-7 of rounding per row from the fp32 log2 / exp2.
+        const double slack = 4e-6 + 1e-12 * mag;
+        double t = 1.0;
+        bool accepted = false;
+        for (int ls = 0; ls < kLineSearch; ++ls) {
+            const double gt[4] = {g[0] + t * step[0], g[1] + t * step[1], g[2] + t * step[2],
+                                  0.0};
+            if (newton_objective(l, gt) >= F + 1e-4 * t * slope - slack) {
+                accepted = true;
+                break;
+            }
+            t *= 0.5;
+        }
+        // No acceptable step: the plan is as close as fp32 allows; stop here.
+        if (!accepted)
+            break;
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            g[j] += t * step[j];
+        ++k;
+    }
+    float4 *dst = reinterpret_cast<float4 *>(out) + 4 * bi;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        dst[r] = make_float4(P[r][0], P[r][1], P[r][2], P[r][3]);
+    if (iters_out)
+        iters_out[bi] = k;
+}
+
+// dl/dL from the projection P and dl/dP = G by the implicit function theorem
+// at the solution (section 2.2), in fp64 (the kernel is bound by its 192
+// bytes of HBM traffic per matrix, and the 3x3 system is ill-conditioned for
+// near-permutation plans):
+//   r_i = sum_j P_ij G_ij,  w_j = sum_i P_ij (G_ij - r_i)  (j = 0..2),
+//   A lam = -w (A = diag(c) - P^T P, the last Newton step's matrix), lam_3 = 0,
+//   dl/dL_il = P_il (G_il - r_i + lam_l - sum_j P_ij lam_j) / eps.
+__global__ __launch_bounds__(256) void birkhoff4_backward_kernel(const float *plan,
+                                                                 const float *grad_plan,
+                                                                 int64_t batch, double inv_eps,
+                                                                 float *grad_logits) {
+    const int64_t bi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (bi >= batch)
+        return;
+    const float4 *ps = reinterpret_cast<const float4 *>(plan) + 4 * bi;
+    const float4 *gs = reinterpret_cast<const float4 *>(grad_plan) + 4 * bi;
+    float P[4][4];
+    double G[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float4 p = ps[r], q = gs[r];
+        P[r][0] = p.x, P[r][1] = p.y, P[r][2] = p.z, P[r][3] = p.w;
+        G[r][0] = q.x, G[r][1] = q.y, G[r][2] = q.z, G[r][3] = q.w;
+    }
+    double rr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        double s = 0.0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            s = fma((double)P[i][j], G[i][j], s);
+        rr[i] = s;
+    }
+    double w[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        double s = 0.0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            s = fma((double)P[i][j], G[i][j] - rr[i], s);
+        w[j] = -s;
+    }
+    double A[3][3], c[4], lam3[3];
+    gram3(P, A, c);
+    chol3_solve(A, w, lam3);
+    const double lam[4] = {lam3[0], lam3[1], lam3[2], 0.0};
+    float4 *dst = reinterpret_cast<float4 *>(grad_logits) + 4 * bi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        double pl = 0.0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            pl = fma((double)P[i][j], lam[j], pl);
+        float o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            o[j] = (float)((double)P[i][j] * (G[i][j] - rr[i] + lam[j] - pl) * inv_eps);
+        dst[i] = make_float4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_birkhoff4_newton(const float *logits, int64_t batch, float eps, int max_iters,
+                                   float tol, float *out, int32_t *iters_out, hipStream_t s) {
+    if (batch == 0)
+        return hipSuccess;
+    const unsigned blocks = (unsigned)((batch + 255) / 256);
+    hipLaunchKernelGGL(birkhoff4_newton_kernel, dim3(blocks), dim3(256), 0, s, logits, batch,
+                       kLog2e / (double)eps, max_iters, tol, out, iters_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_birkhoff4_backward(const float *plan, const float *grad_plan, int64_t batch,
+                                     float eps, float *grad_logits, hipStream_t s) {
+    if (batch == 0)
+        return hipSuccess;
+    const unsigned blocks = (unsigned)((batch + 255) / 256);
+    hipLaunchKernelGGL(birkhoff4_backward_kernel, dim3(blocks), dim3(256), 0, s, plan, grad_plan,
+                       batch, 1.0 / (double)eps, grad_logits);
+    return hipGetLastError();
+}
+
 }  // namespace otsk

@@ -148,6 +148,10 @@ hipError_t launch_half_step_h3(const HalfStep &h, int kp, hipStream_t s);
 
 hipError_t launch_birkhoff4(const float *logits, int64_t batch, float eps, int max_iters, float tol,
                             float *out, int32_t *iters_out, hipStream_t s);
+hipError_t launch_birkhoff4_newton(const float *logits, int64_t batch, float eps, int max_iters,
+                                   float tol, float *out, int32_t *iters_out, hipStream_t s);
+hipError_t launch_birkhoff4_backward(const float *plan, const float *grad_plan, int64_t batch,
+                                     float eps, float *grad_logits, hipStream_t s);
 
 // bias_mode values of launch_prep_side
 enum { kBiasZero = 0, kBiasHat = 1, kBiasRaw = 2 };

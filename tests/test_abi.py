@@ -26,6 +26,7 @@ def test_header_declares_expected_functions():
         "ot_status_string", "ot_sinkhorn_solve", "ot_sinkhorn_solve_eps_scaling",
         "ot_plan_stats", "ot_plan_cost", "ot_marginal_error", "ot_birkhoff_project_batched",
         "ot_transport_apply", "ot_barycentric_map", "ot_cost_gradient_x",
+        "ot_birkhoff_project_newton_batched", "ot_birkhoff_projection_backward_batched",
     ])
 
 
@@ -140,6 +141,34 @@ def test_birkhoff_rejects_invalid(lib):
     assert bp(X, 4, 1.0, 20, -1.0, F, X + 16, None) == INVALID            # counts overlap
     # batch == 0 is a valid no-op that never touches the device
     assert bp(X, 0, 1.0, 20, -1.0, F, None, None) == 0
+
+
+def test_birkhoff_newton_rejects_invalid(lib):
+    bn = lib.ot_birkhoff_project_newton_batched
+    assert bn(None, 4, 1.0, 20, 1e-6, F, None, None) == INVALID
+    assert bn(X, 4, 1.0, 20, 1e-6, None, None, None) == INVALID
+    assert bn(X, -2, 1.0, 20, 1e-6, F, None, None) == INVALID
+    assert bn(X, 4, math.inf, 20, 1e-6, F, None, None) == INVALID
+    assert bn(X, 4, 1.0, -1, 1e-6, F, None, None) == INVALID
+    assert bn(X, 4, 1.0, 20, math.nan, F, None, None) == INVALID
+    assert bn(X + 8, 4, 1.0, 20, 1e-6, F, None, None) == INVALID
+    assert bn(X, 4, 1.0, 20, 1e-6, X + 32, None, None) == INVALID
+    assert bn(X, 4, 1.0, 20, 1e-6, F, F + 4, None) == INVALID
+    assert bn(X, 0, 1.0, 20, 1e-6, F, None, None) == 0
+
+
+def test_birkhoff_backward_rejects_invalid(lib):
+    bw = lib.ot_birkhoff_projection_backward_batched
+    assert bw(None, G, 4, 1.0, F, None) == INVALID
+    assert bw(X, None, 4, 1.0, F, None) == INVALID
+    assert bw(X, G, 4, 1.0, None, None) == INVALID
+    assert bw(X, G, -1, 1.0, F, None) == INVALID
+    assert bw(X, G, 4, 0.0, F, None) == INVALID
+    assert bw(X + 4, G, 4, 1.0, F, None) == INVALID
+    assert bw(X, G, 4, 1.0, X + 16, None) == INVALID      # partial overlap with plan
+    assert bw(X, G, 4, 1.0, G - 16, None) == INVALID      # partial overlap with grad_plan
+    assert bw(X, G, 0, 1.0, F, None) == 0
+    assert bw(X, G, 0, 1.0, X, None) == 0                 # exact aliasing is allowed
 
 
 def test_solve_zero_iters_is_a_host_noop(lib):
