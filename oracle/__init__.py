@@ -25,6 +25,9 @@ Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``
 * ``transport_apply``, ``barycentric_map``, ``grad_x``: pinned (n = 1 closed
   form, product-coupling limit, eps -> 0 permutation limit, finite
   differences of the converged dual value, marginal sums).
+* ``sinkhorn_cosine``, ``plan_stats_cosine``: pinned (scale and rotation
+  invariance, the unit-sphere identity with the squared Euclidean cost at
+  twice the eps, n = 1 closed form, marginal invariants, cost range).
 * ``birkhoff4_newton``: pinned (same limit as long Sinkhorn-Knopp runs,
   cross-ratio invariant, doubly stochastic, constant logits need no step,
   quadratic convergence).
@@ -80,6 +83,12 @@ def _load():
         lib.oracle_plan_stats.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int64,
                                           ctypes.c_int64, ctypes.c_int, ctypes.c_double,
                                           _dp, _dp, _dp, _dp]
+        lib.oracle_sinkhorn_kind.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int, ctypes.c_double, ctypes.c_int, _dp,
+                                             _dp, ctypes.c_int]
+        lib.oracle_plan_stats_kind.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int64,
+                                               ctypes.c_int64, ctypes.c_int, ctypes.c_double,
+                                               _dp, _dp, _dp, _dp, ctypes.c_int]
         lib.oracle_transport_apply.argtypes = [_dp, _dp, _dp, _dp, ctypes.c_int64, ctypes.c_int64,
                                                ctypes.c_int, ctypes.c_double, _dp, ctypes.c_int,
                                                _dp]
@@ -262,3 +271,33 @@ def birkhoff4_backward(P, grad_P, eps: float = 1.0) -> np.ndarray:
     out = np.empty_like(Pd)
     _load().oracle_birkhoff4_backward(_ptr(Pd), _ptr(G), Pd.shape[0], float(eps), _ptr(out))
     return out.reshape(-1, 4, 4)
+
+
+def sinkhorn_cosine(x, y, a, b, eps: float, iters: int, f0=None, g0=None):
+    """:func:`sinkhorn` with the cosine cost C_ij = 1 - x_i.y_j / (|x_i| |y_j|)
+    (FlashSinkhorn page, significance section)."""
+    x, y = _points(x, "x"), _points(y, "y")
+    a, b = _d(a), _d(b)
+    n, m, d = x.shape[0], y.shape[0], x.shape[1]
+    if y.shape[1] != d or a.shape != (n,) or b.shape != (m,):
+        raise ValueError("shape mismatch")
+    f = np.zeros(n) if f0 is None else _d(f0).copy()
+    g = np.zeros(m) if g0 is None else _d(g0).copy()
+    _load().oracle_sinkhorn_kind(_ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps),
+                                 int(iters), _ptr(f), _ptr(g), 1)
+    return f, g
+
+
+def plan_stats_cosine(x, y, a, b, f, g, eps: float) -> dict:
+    """:func:`plan_stats` with the cosine cost."""
+    x, y = _points(x, "x"), _points(y, "y")
+    a, b, f, g = _d(a), _d(b), _d(f), _d(g)
+    n, m, d = x.shape[0], y.shape[0], x.shape[1]
+    cost = np.zeros(1)
+    marg = np.zeros(2)
+    rs = np.empty(n)
+    cs = np.empty(m)
+    _load().oracle_plan_stats_kind(_ptr(x), _ptr(y), _ptr(a), _ptr(b), _ptr(f), _ptr(g), n, m,
+                                   d, float(eps), _ptr(cost), _ptr(marg), _ptr(rs), _ptr(cs), 1)
+    return {"cost": float(cost[0]), "marg_row": float(marg[0]), "marg_col": float(marg[1]),
+            "marg": float(marg[0] + marg[1]), "rowsum": rs, "colsum": cs}

@@ -66,16 +66,39 @@ static double sq_dist(const double *p, const double *q, int d)
 }
 
 /*
+ * Cosine cost ("FlashSinkhorn ...", significance section: the method applies
+ * to the squared Euclidean cost and to the cosine distance after
+ * normalisation): C = 1 - p.q / (|p| |q|), from its definition. Undefined
+ * for a zero vector (NaN here).
+ */
+static double cos_dist(const double *p, const double *q, int d)
+{
+    double pq = 0.0, pp = 0.0, qq = 0.0;
+    for (int k = 0; k < d; ++k) {
+        pq += p[k] * q[k];
+        pp += p[k] * p[k];
+        qq += q[k] * q[k];
+    }
+    return 1.0 - pq / (sqrt(pp) * sqrt(qq));
+}
+
+/* Cost kinds: 0 squared Euclidean, 1 cosine. */
+static double cost_of(const double *p, const double *q, int d, int kind)
+{
+    return kind == 1 ? cos_dist(p, q, d) : sq_dist(p, q, d);
+}
+
+/*
  * One half-step for the side whose points are P (np x d, weights w):
  *   out_i = eps*log w_i - eps*LSE_j((other_j - C(P_i, Q_j))/eps)
  * over all nq points Q_j with potentials other_j.  rows == NULL updates every
  * i in [0, np) and writes out[i]; otherwise it updates rows[r] for
  * r in [0, nrows) and writes out[r].
  */
-void oracle_half_update(const double *P, const double *Q, const double *w,
-                        const double *other, int64_t np, int64_t nq, int d,
-                        double eps, const int64_t *rows, int64_t nrows,
-                        double *out)
+static void half_update_kind(const double *P, const double *Q, const double *w,
+                             const double *other, int64_t np, int64_t nq, int d,
+                             double eps, const int64_t *rows, int64_t nrows,
+                             double *out, int kind)
 {
     int64_t count = rows ? nrows : np;
 #pragma omp parallel for schedule(dynamic, 16)
@@ -84,30 +107,45 @@ void oracle_half_update(const double *P, const double *Q, const double *w,
         const double *pi = P + i * (int64_t)d;
         double mx = -INFINITY;
         for (int64_t j = 0; j < nq; ++j) {
-            double v = (other[j] - sq_dist(pi, Q + j * (int64_t)d, d)) / eps;
+            double v = (other[j] - cost_of(pi, Q + j * (int64_t)d, d, kind)) / eps;
             if (v > mx)
                 mx = v;
         }
         double s = 0.0;
         for (int64_t j = 0; j < nq; ++j) {
-            double v = (other[j] - sq_dist(pi, Q + j * (int64_t)d, d)) / eps;
+            double v = (other[j] - cost_of(pi, Q + j * (int64_t)d, d, kind)) / eps;
             s += exp(v - mx);
         }
         out[r] = eps * log(w[i]) - eps * (mx + log(s));
     }
 }
 
+void oracle_half_update(const double *P, const double *Q, const double *w,
+                        const double *other, int64_t np, int64_t nq, int d,
+                        double eps, const int64_t *rows, int64_t nrows,
+                        double *out)
+{
+    half_update_kind(P, Q, w, other, np, nq, d, eps, rows, nrows, out, 0);
+}
+
 /*
  * iters alternating iterations at one eps, in place on f (n) and g (m).
  */
+void oracle_sinkhorn_kind(const double *x, const double *y, const double *a,
+                          const double *b, int64_t n, int64_t m, int d, double eps,
+                          int iters, double *f, double *g, int kind)
+{
+    for (int k = 0; k < iters; ++k) {
+        half_update_kind(x, y, a, g, n, m, d, eps, NULL, 0, f, kind);
+        half_update_kind(y, x, b, f, m, n, d, eps, NULL, 0, g, kind);
+    }
+}
+
 void oracle_sinkhorn(const double *x, const double *y, const double *a,
                      const double *b, int64_t n, int64_t m, int d, double eps,
                      int iters, double *f, double *g)
 {
-    for (int k = 0; k < iters; ++k) {
-        oracle_half_update(x, y, a, g, n, m, d, eps, NULL, 0, f);
-        oracle_half_update(y, x, b, f, m, n, d, eps, NULL, 0, g);
-    }
+    oracle_sinkhorn_kind(x, y, a, b, n, m, d, eps, iters, f, g, 0);
 }
 
 /*
@@ -118,10 +156,10 @@ void oracle_sinkhorn(const double *x, const double *y, const double *a,
  * rowsum / colsum may be NULL.  Per-row and per-column partials are added in
  * index order.
  */
-void oracle_plan_stats(const double *x, const double *y, const double *a,
-                       const double *b, const double *f, const double *g,
-                       int64_t n, int64_t m, int d, double eps, double *cost,
-                       double *marg, double *rowsum, double *colsum)
+void oracle_plan_stats_kind(const double *x, const double *y, const double *a,
+                            const double *b, const double *f, const double *g,
+                            int64_t n, int64_t m, int d, double eps, double *cost,
+                            double *marg, double *rowsum, double *colsum, int kind)
 {
     double *rs = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
     double *rc = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
@@ -130,7 +168,7 @@ void oracle_plan_stats(const double *x, const double *y, const double *a,
     for (int64_t i = 0; i < n; ++i) {
         double s = 0.0, c = 0.0;
         for (int64_t j = 0; j < m; ++j) {
-            double cij = sq_dist(x + i * (int64_t)d, y + j * (int64_t)d, d);
+            double cij = cost_of(x + i * (int64_t)d, y + j * (int64_t)d, d, kind);
             double p = exp((f[i] + g[j] - cij) / eps);
             s += p;
             c += p * cij;
@@ -142,7 +180,7 @@ void oracle_plan_stats(const double *x, const double *y, const double *a,
     for (int64_t j = 0; j < m; ++j) {
         double s = 0.0;
         for (int64_t i = 0; i < n; ++i) {
-            double cij = sq_dist(x + i * (int64_t)d, y + j * (int64_t)d, d);
+            double cij = cost_of(x + i * (int64_t)d, y + j * (int64_t)d, d, kind);
             s += exp((f[i] + g[j] - cij) / eps);
         }
         cs[j] = s;
@@ -165,6 +203,14 @@ void oracle_plan_stats(const double *x, const double *y, const double *a,
     free(rs);
     free(rc);
     free(cs);
+}
+
+void oracle_plan_stats(const double *x, const double *y, const double *a,
+                       const double *b, const double *f, const double *g,
+                       int64_t n, int64_t m, int d, double eps, double *cost,
+                       double *marg, double *rowsum, double *colsum)
+{
+    oracle_plan_stats_kind(x, y, a, b, f, g, n, m, d, eps, cost, marg, rowsum, colsum, 0);
 }
 
 /*

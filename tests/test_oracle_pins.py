@@ -428,6 +428,70 @@ def test_birkhoff_fixed20_sigma_split():
 
 
 # --------------------------------------------------------------------------- #
+# Cosine cost (FlashSinkhorn page, significance section)                       #
+# --------------------------------------------------------------------------- #
+
+def _cos_cost(x, y):
+    x = np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    return 1.0 - (x @ y.T) / (np.linalg.norm(x, axis=1)[:, None] * np.linalg.norm(y, axis=1)[None])
+
+
+def test_cosine_first_half_step_matches_scipy():
+    c = random_clouds(31, 44, 5, seed=60)
+    eps = 0.07
+    g0 = np.random.default_rng(61).normal(0, 0.1, size=44)
+    f, _ = oracle.sinkhorn_cosine(c["x"], c["y"], c["a"], c["b"], eps, 1, g0=g0)
+    # after one iteration f is the half-step from g0 (the g half-step follows)
+    ref = eps * np.log(c["a"].astype(np.float64)) - eps * logsumexp(
+        (g0[None, :] - _cos_cost(c["x"], c["y"])) / eps, axis=1)
+    np.testing.assert_allclose(f, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_cosine_unit_sphere_equals_half_sqeuclid_at_twice_eps():
+    # On unit vectors 1 - cos = |x - y|^2 / 2, so the cosine problem at eps is
+    # the squared Euclidean one at 2 eps with potentials doubled.
+    c = random_clouds(40, 35, 6, seed=62)
+    xs = c["x"] / np.linalg.norm(c["x"].astype(np.float64), axis=1, keepdims=True)
+    ys = c["y"] / np.linalg.norm(c["y"].astype(np.float64), axis=1, keepdims=True)
+    eps = 0.05
+    fc, gc = oracle.sinkhorn_cosine(xs, ys, c["a"], c["b"], eps, 30)
+    fq, gq = oracle.sinkhorn(xs, ys, c["a"], c["b"], 2 * eps, 30)
+    np.testing.assert_allclose(fc, fq / 2, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(gc, gq / 2, rtol=1e-11, atol=1e-12)
+    sc = oracle.plan_stats_cosine(xs, ys, c["a"], c["b"], fc, gc, eps)
+    sq = oracle.plan_stats(xs, ys, c["a"], c["b"], fq, gq, 2 * eps)
+    assert sc["cost"] == pytest.approx(sq["cost"] / 2, rel=1e-11)
+    assert sc["marg"] == pytest.approx(sq["marg"], rel=1e-8, abs=1e-14)
+
+
+def test_cosine_scale_and_rotation_invariance():
+    c = random_clouds(25, 30, 4, seed=63)
+    rng = np.random.default_rng(64)
+    Q, _ = np.linalg.qr(rng.normal(size=(4, 4)))
+    sx = rng.uniform(0.1, 10.0, size=(25, 1))
+    sy = rng.uniform(0.1, 10.0, size=(30, 1))
+    f0, g0 = oracle.sinkhorn_cosine(c["x"], c["y"], c["a"], c["b"], 0.1, 20)
+    f1, g1 = oracle.sinkhorn_cosine((c["x"] * sx) @ Q, (c["y"] * sy) @ Q, c["a"], c["b"], 0.1, 20)
+    np.testing.assert_allclose(f1, f0, rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(g1, g0, rtol=1e-10, atol=1e-11)
+
+
+def test_cosine_single_source_and_cost_range():
+    rng = np.random.default_rng(65)
+    x = rng.normal(size=(1, 8))
+    y = rng.normal(size=(50, 8))
+    b = rng.dirichlet(np.ones(50))
+    a = np.array([b.sum()])
+    f, g = oracle.sinkhorn_cosine(x, y, a, b, 0.3, 2)
+    st = oracle.plan_stats_cosine(x, y, a, b, f, g, 0.3)
+    C = _cos_cost(x, y)[0]
+    assert st["cost"] == pytest.approx(float(b @ C), rel=1e-12)   # P_1j = b_j
+    assert st["marg"] < 1e-12
+    assert np.all(C >= 0) and np.all(C <= 2)
+
+
+# --------------------------------------------------------------------------- #
 # 4x4 projection by Newton's method on the dual, and its backward             #
 # (Birkhoff page, sections 2.1 and 2.2)                                        #
 # --------------------------------------------------------------------------- #
