@@ -209,6 +209,30 @@ ot_status ot_birkhoff_project_batched(const float *logits, int64_t batch,
                                       void *stream);
 
 /*
+ * ot_sinkhorn_solve_cosine -- ot_sinkhorn_solve with the cosine cost
+ * C_ij = 1 - x_i.y_j / (|x_i| |y_j|) (page "FlashSinkhorn ...", significance
+ * section: the method covers the cosine distance after normalisation).
+ * Computed as the squared Euclidean problem on x/|x|, y/|y| at 2*eps (on
+ * unit vectors 1 - cos = |x - y|^2 / 2), with the potentials halved on the
+ * way out and g doubled on the way in. Arguments, warm start and errors as
+ * ot_sinkhorn_solve; every x_i and y_j must be nonzero (not checked).
+ */
+ot_status ot_sinkhorn_solve_cosine(const float *x, const float *y, const float *a,
+                                   const float *b, int64_t n, int64_t m, int32_t d,
+                                   float eps, int32_t iters, float *f, float *g,
+                                   void *stream);
+
+/*
+ * ot_plan_stats_cosine -- ot_plan_stats for the cosine cost: cost =
+ * sum_ij P_ij (1 - cos(x_i, y_j)) and the marginal L1 errors of
+ * P_ij = exp((f_i + g_j - C_ij)/eps). Arguments and errors as ot_plan_stats.
+ */
+ot_status ot_plan_stats_cosine(const float *x, const float *y, const float *a,
+                               const float *b, const float *f, const float *g,
+                               int64_t n, int64_t m, int32_t d, float eps,
+                               double *cost, double *marg, void *stream);
+
+/*
  * ot_birkhoff_project_newton_batched -- the same projection as
  * ot_birkhoff_project_batched, computed by Newton's method on the dual (page
  * "Aceleración de la Proyección de Birkhoff ...", section 2.1): after fixing

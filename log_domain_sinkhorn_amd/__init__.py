@@ -32,6 +32,8 @@ __all__ = [
     "ot_plan_stats",
     "ot_plan_cost",
     "ot_marginal_error",
+    "ot_sinkhorn_solve_cosine",
+    "ot_plan_stats_cosine",
     "ot_transport_apply",
     "ot_barycentric_map",
     "ot_cost_gradient_x",
@@ -71,6 +73,10 @@ _SIGNATURES = {
     "ot_plan_stats": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _f32, _p, _p, _p], ctypes.c_int),
     "ot_plan_cost": ([_p, _p, _p, _p, _i64, _i64, _i32, _f32, _p, _p], ctypes.c_int),
     "ot_marginal_error": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _f32, _p, _p], ctypes.c_int),
+    "ot_sinkhorn_solve_cosine": ([_p, _p, _p, _p, _i64, _i64, _i32, _f32, _i32, _p, _p, _p],
+                                 ctypes.c_int),
+    "ot_plan_stats_cosine": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _f32, _p, _p, _p],
+                             ctypes.c_int),
     "ot_transport_apply": ([_p, _p, _p, _p, _i64, _i64, _i32, _f32, _p, _i32, _p, _p],
                            ctypes.c_int),
     "ot_barycentric_map": ([_p, _p, _p, _p, _p, _i64, _i64, _i32, _f32, _p, _p], ctypes.c_int),
@@ -249,6 +255,35 @@ def ot_marginal_error(x, y, a, b, f, g, eps: float, marg, stream=None) -> None:
     _dev_tensor(marg, "marg", "f64", (2,))
     _call("ot_marginal_error", _ptr(x), _ptr(y), _ptr(a), _ptr(b), _ptr(f), _ptr(g), n, m, d,
           float(eps), _ptr(marg), _stream_of(x, stream))
+
+
+def ot_sinkhorn_solve_cosine(x, y, a, b, eps: float, iters: int, f, g, stream=None) -> None:
+    """:func:`ot_sinkhorn_solve` with the cosine cost 1 - cos(x_i, y_j)."""
+    n, m, d = _clouds(x, y)
+    _dev_tensor(a, "a", "f32", (n,))
+    _dev_tensor(b, "b", "f32", (m,))
+    _dev_tensor(f, "f", "f32", (n,))
+    _dev_tensor(g, "g", "f32", (m,))
+    _call("ot_sinkhorn_solve_cosine", _ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps),
+          int(iters), _ptr(f), _ptr(g), _stream_of(x, stream))
+
+
+def ot_plan_stats_cosine(x, y, a, b, f, g, eps: float, cost=None, marg=None,
+                         stream=None) -> None:
+    """:func:`ot_plan_stats` with the cosine cost."""
+    n, m, d = _clouds(x, y)
+    if a is not None:
+        _dev_tensor(a, "a", "f32", (n,))
+    if b is not None:
+        _dev_tensor(b, "b", "f32", (m,))
+    _dev_tensor(f, "f", "f32", (n,))
+    _dev_tensor(g, "g", "f32", (m,))
+    if cost is not None:
+        _dev_tensor(cost, "cost", "f64", (1,))
+    if marg is not None:
+        _dev_tensor(marg, "marg", "f64", (2,))
+    _call("ot_plan_stats_cosine", _ptr(x), _ptr(y), _ptr(a), _ptr(b), _ptr(f), _ptr(g), n, m, d,
+          float(eps), _ptr(cost), _ptr(marg), _stream_of(x, stream))
 
 
 def ot_transport_apply(x, y, f, g, eps: float, v, out, stream=None) -> None:

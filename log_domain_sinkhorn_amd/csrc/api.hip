@@ -508,6 +508,83 @@ ot_status ot_birkhoff_project_batched(const float *logits, int64_t batch, float 
                                       (hipStream_t)stream));
 }
 
+ot_status ot_sinkhorn_solve_cosine(const float *x, const float *y, const float *a, const float *b,
+                                   int64_t n, int64_t m, int32_t d, float eps, int32_t iters,
+                                   float *f, float *g, void *stream) {
+    ot_status st = check_clouds(x, y, n, m, d, eps);
+    if (st == OT_SUCCESS && iters < 0)
+        st = OT_ERROR_INVALID_VALUE;
+    if (st == OT_SUCCESS)
+        st = check_solve_outputs(x, y, a, b, n, m, d, f, g);
+    if (st == OT_SUCCESS)
+        st = check_supported(n, m, d);
+    if (st == OT_SUCCESS && !isfinite(2.0f * eps))
+        st = OT_ERROR_NOT_SUPPORTED;
+    if (st != OT_SUCCESS || iters == 0)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    const size_t xb = align_up((size_t)n * d * sizeof(float), 256);
+    const size_t yb = align_up((size_t)m * d * sizeof(float), 256);
+    const size_t fb = align_up((size_t)n * sizeof(float), 256);
+    const size_t gb = align_up((size_t)m * sizeof(float), 256);
+    Scratch sc(s);
+    hipError_t e = sc.alloc(xb + yb + fb + gb);
+    if (e != hipSuccess)
+        return map_error(e);
+    char *p = static_cast<char *>(sc.ptr);
+    float *xn = reinterpret_cast<float *>(p), *yn = reinterpret_cast<float *>(p + xb);
+    float *f2 = reinterpret_cast<float *>(p + xb + yb);
+    float *g2 = reinterpret_cast<float *>(p + xb + yb + fb);
+    if ((e = launch_normalize(x, n, d, xn, s)) != hipSuccess ||
+        (e = launch_normalize(y, m, d, yn, s)) != hipSuccess ||
+        (e = launch_scale(g, m, 2.f, g2, s)) != hipSuccess)
+        return map_error(e);
+    const double e2 = 2.0 * (double)eps;
+    st = run_schedule(xn, yn, a, b, n, m, d, &e2, 1, iters, f2, g2, s);
+    if (st != OT_SUCCESS)
+        return st;
+    if ((e = launch_scale(f2, n, 0.5f, f, s)) != hipSuccess ||
+        (e = launch_scale(g2, m, 0.5f, g, s)) != hipSuccess)
+        return map_error(e);
+    return OT_SUCCESS;
+}
+
+ot_status ot_plan_stats_cosine(const float *x, const float *y, const float *a, const float *b,
+                               const float *f, const float *g, int64_t n, int64_t m, int32_t d,
+                               float eps, double *cost, double *marg, void *stream) {
+    ot_status st = check_clouds(x, y, n, m, d, eps);
+    if (st == OT_SUCCESS && (!f || !g || (!cost && !marg) || (marg && (!a || !b))))
+        st = OT_ERROR_INVALID_VALUE;
+    if (st == OT_SUCCESS)
+        st = check_supported(n, m, d);
+    if (st == OT_SUCCESS && !isfinite(2.0f * eps))
+        st = OT_ERROR_NOT_SUPPORTED;
+    if (st != OT_SUCCESS)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    const size_t xb = align_up((size_t)n * d * sizeof(float), 256);
+    const size_t yb = align_up((size_t)m * d * sizeof(float), 256);
+    const size_t fb = align_up((size_t)n * sizeof(float), 256);
+    const size_t gb = align_up((size_t)m * sizeof(float), 256);
+    Scratch sc(s);
+    hipError_t e = sc.alloc(xb + yb + fb + gb);
+    if (e != hipSuccess)
+        return map_error(e);
+    char *p = static_cast<char *>(sc.ptr);
+    float *xn = reinterpret_cast<float *>(p), *yn = reinterpret_cast<float *>(p + xb);
+    float *f2 = reinterpret_cast<float *>(p + xb + yb);
+    float *g2 = reinterpret_cast<float *>(p + xb + yb + fb);
+    if ((e = launch_normalize(x, n, d, xn, s)) != hipSuccess ||
+        (e = launch_normalize(y, m, d, yn, s)) != hipSuccess ||
+        (e = launch_scale(f, n, 2.f, f2, s)) != hipSuccess ||
+        (e = launch_scale(g, m, 2.f, g2, s)) != hipSuccess)
+        return map_error(e);
+    st = ot_plan_stats(xn, yn, a, b, f2, g2, n, m, d, 2.0f * eps, cost, marg, stream);
+    if (st != OT_SUCCESS || !cost)
+        return st;
+    return map_error(launch_scale_double(cost, 0.5, s));
+}
+
 ot_status ot_birkhoff_project_newton_batched(const float *logits, int64_t batch, float eps,
                                              int32_t max_iters, float tol, float *out,
                                              int32_t *iters_out, void *stream) {

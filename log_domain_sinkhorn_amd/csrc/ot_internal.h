@@ -146,6 +146,11 @@ hipError_t launch_plan_stats_h3(int kp, const void *xrow, const void *xcol, cons
                                 double *scratch, hipStream_t s);
 hipError_t launch_half_step_h3(const HalfStep &h, int kp, hipStream_t s);
 
+// Cosine cost: normalised copies of the points, scaled potentials.
+hipError_t launch_normalize(const float *pts, int64_t count, int d, float *out, hipStream_t s);
+hipError_t launch_scale(const float *in, int64_t count, float factor, float *out, hipStream_t s);
+hipError_t launch_scale_double(double *v, double factor, hipStream_t s);
+
 hipError_t launch_birkhoff4(const float *logits, int64_t batch, float eps, int max_iters, float tol,
                             float *out, int32_t *iters_out, hipStream_t s);
 hipError_t launch_birkhoff4_newton(const float *logits, int64_t batch, float eps, int max_iters,

@@ -27,6 +27,7 @@ def test_header_declares_expected_functions():
         "ot_plan_stats", "ot_plan_cost", "ot_marginal_error", "ot_birkhoff_project_batched",
         "ot_transport_apply", "ot_barycentric_map", "ot_cost_gradient_x",
         "ot_birkhoff_project_newton_batched", "ot_birkhoff_projection_backward_batched",
+        "ot_sinkhorn_solve_cosine", "ot_plan_stats_cosine",
     ])
 
 
@@ -169,6 +170,20 @@ def test_birkhoff_backward_rejects_invalid(lib):
     assert bw(X, G, 4, 1.0, G - 16, None) == INVALID      # partial overlap with grad_plan
     assert bw(X, G, 0, 1.0, F, None) == 0
     assert bw(X, G, 0, 1.0, X, None) == 0                 # exact aliasing is allowed
+
+
+def test_cosine_entries_reject_invalid(lib):
+    sc, pc = lib.ot_sinkhorn_solve_cosine, lib.ot_plan_stats_cosine
+    assert sc(None, Y, A, B, 10, 12, 3, 0.1, 5, F, G, None) == INVALID
+    assert sc(X, Y, A, B, 10, 12, 3, 0.0, 5, F, G, None) == INVALID
+    assert sc(X, Y, A, B, 10, 12, 3, 0.1, -1, F, G, None) == INVALID
+    assert sc(X, Y, A, B, 10, 12, 3, 0.1, 5, A, G, None) == INVALID    # f aliases a
+    assert sc(X, Y, A, B, 10, 12, 129, 0.1, 5, F, G, None) == UNSUPPORTED
+    assert sc(X, Y, A, B, 10, 12, 3, 3e38, 5, F, G, None) == UNSUPPORTED  # 2 eps overflows
+    assert sc(X, Y, A, B, 10, 12, 3, 0.1, 0, F, G, None) == 0           # host no-op
+    assert pc(X, Y, A, B, F, G, 10, 12, 3, 0.1, None, None, None) == INVALID
+    assert pc(X, Y, None, B, F, G, 10, 12, 3, 0.1, None, MG, None) == INVALID
+    assert pc(X, Y, A, B, F, G, 10, 12, 200, 0.1, C, None, None) == UNSUPPORTED
 
 
 def test_solve_zero_iters_is_a_host_noop(lib):
