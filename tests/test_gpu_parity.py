@@ -104,6 +104,27 @@ def test_shapes(n, m, d):
     _check_solve(c, eps, 10, f"shape {n}x{m}x{d}")
 
 
+STATS_SHAPES = [(1, 300, 64), (300, 1, 64), (129, 257, 33), (600, 200, 96), (257, 300, 128),
+                (1, 1, 40), (300, 500, 31)]
+
+
+@pytest.mark.parametrize("n,m,d", STATS_SHAPES)
+def test_plan_stats_shapes(n, m, d):
+    # Plan statistics on the same fp32 (f, g) as the oracle: the kernels alone.
+    c = random_clouds(n, m, d, seed=n + 5 * m + d, spread=1.0 / np.sqrt(d))
+    eps = 0.3
+    fo, go = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, 6)
+    f, g = fo.astype(np.float32), go.astype(np.float32)
+    st = gpu_plan_stats(c, f, g, eps)
+    sk = oracle.plan_stats(c["x"], c["y"], c["a"], c["b"], f, g, eps)
+    ec = abs(st["cost"] - sk["cost"]) / abs(sk["cost"])
+    print(f"stats {n}x{m}x{d}: cost rel {ec:.1e}; marg {st['marg_row']:.3e}/{st['marg_col']:.3e} "
+          f"vs {sk['marg_row']:.3e}/{sk['marg_col']:.3e}", flush=True)
+    assert ec <= TOL_COST
+    assert abs(st["marg_row"] - sk["marg_row"]) <= TOL_MARG
+    assert abs(st["marg_col"] - sk["marg_col"]) <= TOL_MARG
+
+
 # d >= 32 runs on split-f16 matrix-core products (three f16 products per fp32
 # product, fp32 accumulation). The split itself keeps ~22 bits of each
 # coordinate; the matrix core's aligned sums lose about 2^-21 of the largest
