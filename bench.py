@@ -321,11 +321,16 @@ def run_transport(name, torch, lds, reps=3):
         res[f"{label}_ms"] = ms
         res[f"{label}_pairs_per_s"] = n * m / (ms / 1e3)
     if d >= 32:
-        flops = 2.0 * (d + d) * n * m  # x.y and P.V, fp32 MFMA
-        ach = flops / (res["apply_ms"] / 1e3) / 1e12
-        res["roofline_whole_call"] = {"bound": "mfma", "achieved": ach,
-                                      "peak": PEAK_MFMA_FP32_TFLOPS, "unit": "TFLOP/s",
-                                      "frac": ach / PEAK_MFMA_FP32_TFLOPS}
+        # Matrix-pipe time per 32x32 subtile and wave: the split-f16 score
+        # (3*kp/16 f16 MFMAs of 32 cycles + one fp32 MFMA of 64) and P.V
+        # (16 fp32 MFMAs of 64 cycles per 32 value channels), at 2.4 GHz on
+        # 1024 SIMDs; frac = that time / the measured call.
+        kp = h3_kp(d)
+        cycles = 3 * kp // 16 * 32 + 64 + 16 * 64 * ((d + 31) // 32)
+        model_ms = (n / 32) * (m / 32) * cycles / (1024 * 2.4e9) * 1e3
+        res["roofline_whole_call"] = {"bound": "mfma", "model_ms": model_ms,
+                                      "frac": model_ms / res["apply_ms"],
+                                      "model": f"{cycles} matrix-pipe cycles per 32x32 subtile"}
     return res
 
 

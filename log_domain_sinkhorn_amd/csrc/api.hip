@@ -359,47 +359,68 @@ ot_status ot_marginal_error(const float *x, const float *y, const float *a, cons
 }
 
 // out_i = sum_j P_ij v_j: records with hat biases of f and g, then the
-// VALU (d < 32) or MFMA (d >= 32) streaming kernel. rowsum (MFMA path only,
-// nullable) also receives r_i = sum_j P_ij.
+// VALU (d < 32) or matrix-core (d >= 32, split-f16 records) streaming
+// kernel. rowsum (matrix-core path only, nullable) also receives
+// r_i = sum_j P_ij.
 static ot_status transport_apply_impl(const float *x, const float *y, const float *f,
                                       const float *g, int64_t n, int64_t m, int32_t d, float eps,
                                       const float *v, int32_t dv, float *out, float *rowsum,
                                       hipStream_t s) {
-    const Layout L = choose_layout(d);
-    if (rowsum && !L.mfma)
-        return OT_ERROR_INVALID_VALUE;
     const int64_t n_pad = pad_points(n), m_pad = pad_points(m);
+    const double hat_scale = kLog2e / (double)eps;
+    const double scale = 2.0 * kLog2e / (double)eps;
+    hipError_t e;
+    if (d >= 32) {
+        const int kp = h3_kp(d);
+        const size_t xr = align_up((size_t)n_pad * 4 * kp, 256);
+        const size_t yr = align_up((size_t)m_pad * 4 * kp, 256);
+        const size_t xv = align_up((size_t)n_pad * sizeof(float), 256);
+        const size_t yv = align_up((size_t)m_pad * sizeof(float), 256);
+        const size_t mb = align_up(h3_maxabs_floats() * sizeof(float), 256);
+        const size_t pd = transport_mfma_scratch_doubles(n, m_pad, dv, rowsum != nullptr);
+        Scratch sc(s);
+        if ((e = sc.alloc(2 * xr + 2 * yr + 2 * xv + 2 * yv + mb + pd * sizeof(double))) !=
+            hipSuccess)
+            return map_error(e);
+        char *p = static_cast<char *>(sc.ptr);
+        void *xcol = p, *xrow = p + xr;
+        p += 2 * xr;
+        void *ycol = p, *yrow = p + yr;
+        p += 2 * yr;
+        float *xnrm = reinterpret_cast<float *>(p), *xhat = reinterpret_cast<float *>(p + xv);
+        p += 2 * xv;
+        float *ynrm = reinterpret_cast<float *>(p), *yhat = reinterpret_cast<float *>(p + yv);
+        p += 2 * yv;
+        float *maxabs = reinterpret_cast<float *>(p);
+        double *part = reinterpret_cast<double *>(p + mb);
+        if ((e = launch_maxabs(x, n * d, y, m * d, maxabs, s)) != hipSuccess ||
+            (e = launch_prep_h3(x, f, n, n_pad, d, kp, scale, hat_scale, kBiasHat, maxabs, 0, xcol,
+                                xrow, xnrm, xhat, s)) != hipSuccess ||
+            (e = launch_prep_h3(y, g, m, m_pad, d, kp, scale, hat_scale, kBiasHat, maxabs, 1, ycol,
+                                yrow, ynrm, yhat, s)) != hipSuccess)
+            return map_error(e);
+        return map_error(launch_transport_apply_mfma(kp, xrow, xhat, ycol, yhat, v, n, n_pad, m,
+                                                     m_pad, dv, part, out, rowsum, s));
+    }
+    if (rowsum)
+        return OT_ERROR_INVALID_VALUE;
+    const Layout L = choose_layout(d);
     const size_t xb = align_up((size_t)n_pad * L.record_bytes(), 256);
     const size_t yb = align_up((size_t)m_pad * L.record_bytes(), 256);
-    const size_t xbb = L.mfma ? align_up((size_t)n_pad * sizeof(float), 256) : 0;
-    const size_t ybb = L.mfma ? align_up((size_t)m_pad * sizeof(float), 256) : 0;
-    const size_t pd = L.mfma ? transport_mfma_scratch_doubles(n, m_pad, dv, rowsum != nullptr)
-                             : transport_scratch_doubles(L, n, m_pad, dv);
+    const size_t pd = transport_scratch_doubles(L, n, m_pad, dv);
     Scratch sc(s);
-    hipError_t e = sc.alloc(xb + yb + xbb + ybb + pd * sizeof(double));
-    if (e != hipSuccess)
+    if ((e = sc.alloc(xb + yb + pd * sizeof(double))) != hipSuccess)
         return map_error(e);
     char *base = static_cast<char *>(sc.ptr);
     void *xrec = base, *yrec = base + xb;
-    void *xbias = L.mfma ? static_cast<void *>(base + xb + yb) : xrec;
-    void *ybias = L.mfma ? static_cast<void *>(base + xb + yb + xbb) : yrec;
-    double *part = reinterpret_cast<double *>(base + xb + yb + xbb + ybb);
-    const int bstride = L.mfma ? 1 : L.rs;
-    const int boff = L.mfma ? 0 : L.kp;
-    const double hat_scale = kLog2e / (double)eps;
-    if ((e = launch_prep_side(x, f, n, n_pad, L, hat_scale, kBiasHat, xrec, xbias, bstride, boff,
+    double *part = reinterpret_cast<double *>(base + xb + yb);
+    if ((e = launch_prep_side(x, f, n, n_pad, L, hat_scale, kBiasHat, xrec, xrec, L.rs, L.kp,
                               s)) != hipSuccess)
         return map_error(e);
-    if ((e = launch_prep_side(y, g, m, m_pad, L, hat_scale, kBiasHat, yrec, ybias, bstride, boff,
+    if ((e = launch_prep_side(y, g, m, m_pad, L, hat_scale, kBiasHat, yrec, yrec, L.rs, L.kp,
                               s)) != hipSuccess)
         return map_error(e);
-    const double scale = 2.0 * kLog2e / (double)eps;
-    if (L.mfma)
-        e = launch_transport_apply_mfma(L, xrec, static_cast<const float *>(xbias), yrec,
-                                        static_cast<const float *>(ybias), v, n, n_pad, m, m_pad,
-                                        dv, scale, part, out, rowsum, s);
-    else
-        e = launch_transport_apply(L, xrec, yrec, v, n, n_pad, m, m_pad, dv, scale, part, out, s);
+    e = launch_transport_apply(L, xrec, yrec, v, n, n_pad, m, m_pad, dv, scale, part, out, s);
     return map_error(e);
 }
 

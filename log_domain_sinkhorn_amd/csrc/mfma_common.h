@@ -1,8 +1,8 @@
-// Device helpers shared by the MFMA kernels (the half-steps and the
-// transport application): tile copies with gfx950's direct global->LDS
-// loads, the 32x32 score tile with the bias and a per-row offset folded into
-// one extra v_mfma_f32_32x32x2f32, and the lazy online log-sum-exp epilogue
-// over the 16 accumulator values a lane holds.
+// Device helpers shared by the matrix-core kernels (the half-steps, the plan
+// statistics and the transport application): tile copies with gfx950's
+// direct global->LDS loads, the 32x32 split-f16 score tile with the bias and
+// a per-row offset folded into one extra v_mfma_f32_32x32x2f32, and the lazy
+// online log-sum-exp epilogue over the 16 accumulator values a lane holds.
 #pragma once
 
 #include "ot_internal.h"
@@ -41,29 +41,51 @@ __device__ __forceinline__ void issue_tile(const float4 *__restrict__ col4,
     }
 }
 
-// u[j][i] = s_ij - Mu_i for the 32 columns of subtile `sub`: the extra MFMA
-// (bias and -Mu) on a zero accumulator, then KP/2 MFMAs over k.
+// ---------------------------------------------------------------------------
+// Split-f16 score tile. Each fp32 coordinate is hi + lo, hi = f16(v),
+// lo = f16(v - hi); the column record holds the 2*KP halves of
+// (2 log2(e)/eps) q 2^-e (hi chunks then lo chunks, 16-byte chunk q of point
+// j stored at q ^ (j & SW)), the row side holds p 2^e's hi and lo parts as
+// the stationary B operands. p.q ~ ph.qh + pl.qh + ph.ql.
+// ---------------------------------------------------------------------------
+// Swizzle mask of a record of RC 16-byte chunks (RC a multiple of 8).
+__host__ __device__ constexpr int swizzle_mask(int rc) { return rc % 16 == 0 ? 15 : 7; }
+
+__device__ __forceinline__ half8 as_half8(float4 v) { return __builtin_bit_cast(half8, v); }
+
+// u[j][i] = s_ij - Mu_i for subtile `sub` of the tile in `rec` / `bias`.
+//
+// Order of the chain. The f16 MFMA adds its 16 products and the accumulator
+// in one aligned sum whose error is about 2^-21 of the largest term
+// (measured on gfx950; a lone product is exact), so the accumulator should be
+// small while the products go in: first the lo corrections (2^-11 of the
+// rest), then the hi x hi products onto them, and the bias and -M last,
+// through the fp32 MFMA, whose sum is rounded like fp32 arithmetic.
 template <int KP>
-__device__ __forceinline__ floatx16 score_tile(const float4 *rec, const float *bias, int sub,
-                                               int lane, int li, int hl, const float (&bx)[KP / 2],
-                                               float Mu) {
-    constexpr int RS4 = (KP + 4) / 4;
-    constexpr int KH = KP / 2;
-    const floatx16 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
-                           0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ floatx16 score_h3(const float4 *rec, const float *bias, int sub,
+                                             int lane, int li, int hl, const half8 (&bh)[KP / 16],
+                                             const half8 (&bl)[KP / 16], float Mu) {
+    constexpr int RC = KP / 4;
+    constexpr int SW = swizzle_mask(RC);
+    floatx16 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
+                    0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const int j = sub * 32 + li;
+    const float4 *ap = rec + j * RC;
+    const int sw = j & SW;
+    half8 qh[KP / 16];
+#pragma unroll
+    for (int c = 0; c < KP / 16; ++c) {
+        qh[c] = as_half8(ap[(2 * c + hl) ^ sw]);
+        const half8 ql = as_half8(ap[(KP / 8 + 2 * c + hl) ^ sw]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ql, bh[c], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qh[c], bl[c], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < KP / 16; ++c)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qh[c], bh[c], acc, 0, 0, 0);
     const float a0 = bias[sub * 64 + lane];
     const float b0 = hl ? -Mu : 1.f;
-    floatx16 acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, zero, 0, 0, 0);
-    const float4 *ap = rec + (sub * 32 + li) * RS4 + hl * (KH / 4);
-#pragma unroll
-    for (int q4 = 0; q4 < KH / 4; ++q4) {
-        const float4 av = ap[q4];
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, bx[4 * q4 + 0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, bx[4 * q4 + 1], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, bx[4 * q4 + 2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, bx[4 * q4 + 3], acc, 0, 0, 0);
-    }
-    return acc;
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc, 0, 0, 0);
 }
 
 // Common part of the epilogue: the sum of 2^u over the lane's 16 values.

@@ -101,14 +101,15 @@ hipError_t launch_transport_apply(const Layout &L, const void *xrec, const void 
                                   const float *v, int64_t n, int64_t n_pad, int64_t m,
                                   int64_t m_pad, int dv, double scale, double *part, float *out,
                                   hipStream_t s);
-// MFMA variant (fp32 records, separate fp32 hat biases); rowsum (nullable)
-// also receives r_i = sum_j P_ij, with rowsum = true in the scratch size.
+// Matrix-core variant on split-f16 records (launch_prep_h3 with the hat
+// biases of f and g): x's row records and y's column records; rowsum
+// (nullable) also receives r_i = sum_j P_ij, with rowsum = true in the
+// scratch size.
 size_t transport_mfma_scratch_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum);
-hipError_t launch_transport_apply_mfma(const Layout &L, const void *xrec, const float *xbias,
-                                       const void *yrec, const float *ybias, const float *v,
+hipError_t launch_transport_apply_mfma(int kp, const void *xrow, const float *xhat,
+                                       const void *ycol, const float *yhat, const float *v,
                                        int64_t n, int64_t n_pad, int64_t m, int64_t m_pad, int dv,
-                                       double scale, double *part, float *out, float *rowsum,
-                                       hipStream_t s);
+                                       double *part, float *out, float *rowsum, hipStream_t s);
 hipError_t launch_values_y1(const float *y, int64_t m, int d, float *v, hipStream_t s);
 // mode 0: out_i = w_i / a_i; mode 1: out_i = 2 (r_i x_i - w_i), where w_i is
 // row i of w (row stride ws >= d) and r_i = r[i], or w[i*ws + d] if r is null.

@@ -1,16 +1,16 @@
-// Transport application on the fp32 matrix cores (feature dimension d >= 32):
+// Transport application on the matrix cores (feature dimension d >= 32):
 // out_i = sum_j P_ij v_j with P_ij = exp((f_i + g_j - C_ij)/eps), P never
 // stored ("FlashSinkhorn: IO-Aware Entropic Optimal Transport on GPU",
 // Methodik section 3: applying the plan is an attention-like weighted
 // average over the streamed tiles).
 //
 // Per wave (32 rows) and 32-column subtile:
-//  1. one chain of KP/2 + 1 v_mfma_f32_32x32x2f32 gives log2 P_ij as
-//     D[j][i] (the bias MFMA adds ghat_j and fhat_i), j on the per-lane
-//     register axis: lane l holds row i = l % 32 and the 16 columns
-//     j = 8*(v/4) + 4*(l/32) + v%4 of its registers v;
+//  1. the split-f16 score chain of the half-step kernel (3*KP/16 f16 MFMAs
+//     and one fp32 MFMA that adds ghat_j and fhat_i) gives log2 P_ij as
+//     D[j][i], j on the per-lane register axis: lane l holds row i = l % 32
+//     and the 16 columns j = 8*(v/4) + 4*(l/32) + v%4 of its registers v;
 //  2. 16 v_exp_f32 turn them into P;
-//  3. 16 MFMAs per 32 value channels accumulate O^T[k][i] += V[j][k] P_ij:
+//  3. 16 fp32 MFMAs per 32 value channels accumulate O^T[k][i] += V[j][k] P_ij:
 //     register v of every lane is exactly the B operand of one MFMA (its two
 //     k-slots are the j's of the two lane halves), and the A operand is the
 //     matching value row read from LDS, so P never leaves the VGPRs.
@@ -40,14 +40,12 @@ constexpr int kTargetBlocks = 1024;
 
 template <int KP, int NVB, bool RSUM>
 __global__ __launch_bounds__(kThreads) void transport_mfma_kernel(
-    const float *__restrict__ row_rec, const float *__restrict__ row_bias,
+    const float4 *__restrict__ row_rec, const float *__restrict__ row_bias,
     const float4 *__restrict__ col4, const float *__restrict__ colb, const float *__restrict__ v,
-    int64_t m, int dv, int k0, int64_t rows, int64_t rows_pad, float scale, int tiles_per_split,
+    int64_t m, int dv, int k0, int64_t rows, int64_t rows_pad, int tiles_per_split,
     int ntiles, double *__restrict__ part, double *__restrict__ rpart) {
-    constexpr int RS = KP + 4;
-    constexpr int RS4 = RS / 4;
-    constexpr int TILE4 = kTileCols * RS4;
-    constexpr int KH = KP / 2;
+    constexpr int RC = KP / 4;
+    constexpr int TILE4 = kTileCols * RC;
     constexpr int VC = 32 * NVB;                  // value channels per pass
     constexpr int VST = VC + 4;                   // LDS row stride of the values
     constexpr int VPT = kTileCols * VC / kThreads; // values staged per thread per tile
@@ -95,16 +93,13 @@ __global__ __launch_bounds__(kThreads) void transport_mfma_kernel(
 
     const int64_t i = (int64_t)blockIdx.x * kRowsPerBlock + wave * 32 + li;
     const int64_t ic = i < rows ? i : rows - 1;
-    float bx[KH];
+    half8 bh[KP / 16], bl[KP / 16];
     {
-        const float4 *p = reinterpret_cast<const float4 *>(row_rec + ic * RS + hl * KH);
+        const float4 *rr = row_rec + ic * RC;
 #pragma unroll
-        for (int q = 0; q < KH / 4; ++q) {
-            const float4 w = p[q];
-            bx[4 * q + 0] = w.x * scale;
-            bx[4 * q + 1] = w.y * scale;
-            bx[4 * q + 2] = w.z * scale;
-            bx[4 * q + 3] = w.w * scale;
+        for (int c = 0; c < KP / 16; ++c) {
+            bh[c] = as_half8(rr[2 * c + hl]);
+            bl[c] = as_half8(rr[KP / 8 + 2 * c + hl]);
         }
     }
     // The bias MFMA adds ghat_j x 1 + 1 x (-Mu): Mu = -fhat_i puts fhat_i in.
@@ -130,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void transport_mfma_kernel(
         }
 #pragma unroll
         for (int sub = 0; sub < kSub; ++sub) {
-            floatx16 pr = score_tile<KP>(lrec[b], lbias[b], sub, lane, li, hl, bx, Mu);
+            floatx16 pr = score_h3<KP>(lrec[b], lbias[b], sub, lane, li, hl, bh, bl, Mu);
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 pr[r] = hw_exp2(pr[r]);
@@ -215,37 +210,34 @@ MPlan plan_tm(int64_t rows, int64_t cols_pad) {
 int value_blocks(int dv) { return dv <= 32 ? 1 : 2; }
 
 template <int KP, int NVB>
-hipError_t launch_tm(const float *xrec, const float *xbias, const float4 *col4, const float *colb,
+hipError_t launch_tm(const float4 *xrec, const float *xbias, const float4 *col4, const float *colb,
                      const float *v, int64_t m, int dv, int k0, int64_t n, int64_t n_pad,
-                     float scale, const MPlan &p, double *part, double *rpart, hipStream_t s) {
+                     const MPlan &p, double *part, double *rpart, hipStream_t s) {
     dim3 grid((unsigned)p.row_blocks, (unsigned)p.nsplit);
     if (rpart)
         hipLaunchKernelGGL((transport_mfma_kernel<KP, NVB, true>), grid, dim3(kThreads), 0, s,
-                           xrec, xbias, col4, colb, v, m, dv, k0, n, n_pad, scale,
-                           p.tiles_per_split, p.ntiles, part, rpart);
+                           xrec, xbias, col4, colb, v, m, dv, k0, n, n_pad, p.tiles_per_split,
+                           p.ntiles, part, rpart);
     else
         hipLaunchKernelGGL((transport_mfma_kernel<KP, NVB, false>), grid, dim3(kThreads), 0, s,
-                           xrec, xbias, col4, colb, v, m, dv, k0, n, n_pad, scale,
-                           p.tiles_per_split, p.ntiles, part, rpart);
+                           xrec, xbias, col4, colb, v, m, dv, k0, n, n_pad, p.tiles_per_split,
+                           p.ntiles, part, rpart);
     return hipGetLastError();
 }
 
 template <int NVB>
-hipError_t launch_tm_kp(int kp, const float *xrec, const float *xbias, const float4 *col4,
+hipError_t launch_tm_kp(int kp, const float4 *xrec, const float *xbias, const float4 *col4,
                         const float *colb, const float *v, int64_t m, int dv, int k0, int64_t n,
-                        int64_t n_pad, float scale, const MPlan &p, double *part, double *rpart,
+                        int64_t n_pad, const MPlan &p, double *part, double *rpart,
                         hipStream_t s) {
 #define OTSK_TM(KPV)                                                                           \
     case KPV:                                                                                  \
-        return launch_tm<KPV, NVB>(xrec, xbias, col4, colb, v, m, dv, k0, n, n_pad, scale, p,  \
-                                   part, rpart, s);
+        return launch_tm<KPV, NVB>(xrec, xbias, col4, colb, v, m, dv, k0, n, n_pad, p, part,   \
+                                   rpart, s);
     switch (kp) {
         OTSK_TM(32)
-        OTSK_TM(48)
         OTSK_TM(64)
-        OTSK_TM(80)
         OTSK_TM(96)
-        OTSK_TM(112)
         OTSK_TM(128)
     default:
         return hipErrorInvalidValue;
@@ -261,24 +253,25 @@ size_t transport_mfma_scratch_doubles(int64_t n, int64_t m_pad, int dv, bool row
     return (size_t)p.nsplit * (size_t)pad_points(n) * per_row;
 }
 
-hipError_t launch_transport_apply_mfma(const Layout &L, const void *xrec, const float *xbias,
-                                       const void *yrec, const float *ybias, const float *v,
+hipError_t launch_transport_apply_mfma(int kp, const void *xrow, const float *xhat,
+                                       const void *ycol, const float *yhat, const float *v,
                                        int64_t n, int64_t n_pad, int64_t m, int64_t m_pad, int dv,
-                                       double scale, double *part, float *out, float *rowsum,
-                                       hipStream_t s) {
+                                       double *part, float *out, float *rowsum, hipStream_t s) {
     const MPlan p = plan_tm(n, m_pad);
     const int nvb = value_blocks(dv);
     const int vc = 32 * nvb;
-    const float *xr = static_cast<const float *>(xrec);
-    const float4 *col4 = static_cast<const float4 *>(yrec);
+    const float4 *xr = static_cast<const float4 *>(xrow);
+    const float4 *col4 = static_cast<const float4 *>(ycol);
+    const float *xbias = xhat;
+    const float *ybias = yhat;
     // Row-sum partials follow the value partials in the scratch.
     double *rpart = rowsum ? part + (size_t)p.nsplit * (size_t)n_pad * (size_t)vc : nullptr;
     for (int k0 = 0; k0 < dv; k0 += vc) {
         double *rp = k0 == 0 ? rpart : nullptr;
-        hipError_t e = nvb == 1 ? launch_tm_kp<1>(L.kp, xr, xbias, col4, ybias, v, m, dv, k0, n,
-                                                  n_pad, (float)scale, p, part, rp, s)
-                                : launch_tm_kp<2>(L.kp, xr, xbias, col4, ybias, v, m, dv, k0, n,
-                                                  n_pad, (float)scale, p, part, rp, s);
+        hipError_t e = nvb == 1 ? launch_tm_kp<1>(kp, xr, xbias, col4, ybias, v, m, dv, k0, n,
+                                                  n_pad, p, part, rp, s)
+                                : launch_tm_kp<2>(kp, xr, xbias, col4, ybias, v, m, dv, k0, n,
+                                                  n_pad, p, part, rp, s);
         if (e != hipSuccess)
             return e;
         const int64_t total = n * vc;
