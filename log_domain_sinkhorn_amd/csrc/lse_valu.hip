@@ -278,47 +278,53 @@ __global__ __launch_bounds__(256) void lse_rows_valu_kernel(HalfStep h, int tile
     }
 }
 
-// Combine the per-split (M, S) pairs of each row in split order. F64 selects
-// the record element type the bias is written into.
-template <bool F64>
+// Combine the per-split (M, S) pairs of each row: one wave per row, lane s
+// takes splits s, s + 64, ...; the maximum and the rescaled sum are reduced
+// across the wave in a fixed butterfly order (bitwise reproducible). A
+// thread-per-row loop over the splits is bound by the latency of its
+// dependent loads (25 us for 64 splits of 16384 rows); this takes one
+// round of loads.
+__device__ __forceinline__ double wave_max(double v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v = fmax(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v += __shfl_xor(v, o);
+    return v;
+}
+
 __global__ __launch_bounds__(256) void lse_merge_kernel(HalfStep h, int nsplit, int kp, int rs) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     if (i >= h.rows)
-        return;
-    double M = h.partials[i].m;
-    for (int s = 1; s < nsplit; ++s)
+        return;  // whole waves only
+    double M = -INFINITY;
+    for (int s = lane; s < nsplit; s += 64)
         M = fmax(M, h.partials[(int64_t)s * h.rows_pad + i].m);
+    M = wave_max(M);
     float S = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
+    for (int s = lane; s < nsplit; s += 64) {
         const Partial p = h.partials[(int64_t)s * h.rows_pad + i];
         S = fmaf(p.s, hw_exp2((float)(p.m - M)), S);
     }
-    if (F64) {
+    S = wave_sum(S);
+    if (lane == 0) {
         const double *p = static_cast<const double *>(h.row_rec) + i * rs;
         double q = 0.0;
         for (int k = 0; k < kp; ++k)
             q = fma(p[k], p[k], q);
         finish_row_f64(h, kp, rs, i, M, S, q);
-    } else {
-        const float *p = static_cast<const float *>(h.row_rec) + i * rs;
-        float q = 0.f;
-        for (int k = 0; k < kp; ++k)
-            q = fmaf(p[k], p[k], q);
-        const float lse = (float)M + hw_log2(S);
-        const float hat = log2f(h.row_w[i]) - lse;
-        static_cast<float *>(h.row_bias)[i * h.bias_stride + h.bias_off] = hat;
-        h.pot_out[i] = fmaf((float)h.eps_ln2, hat, q);
     }
 }
 
 hipError_t launch_merge(const HalfStep &h, const Layout &L, int nsplit, hipStream_t s) {
-    const unsigned blocks = (unsigned)((h.rows + 255) / 256);
-    if (L.f64)
-        hipLaunchKernelGGL(lse_merge_kernel<true>, dim3(blocks), dim3(256), 0, s, h, nsplit, L.kp,
-                           L.rs);
-    else
-        hipLaunchKernelGGL(lse_merge_kernel<false>, dim3(blocks), dim3(256), 0, s, h, nsplit,
-                           L.kp, L.rs);
+    const unsigned blocks = (unsigned)((h.rows + 3) / 4);
+    hipLaunchKernelGGL(lse_merge_kernel, dim3(blocks), dim3(256), 0, s, h, nsplit, L.kp, L.rs);
     return hipGetLastError();
 }
 
