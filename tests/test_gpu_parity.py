@@ -163,6 +163,28 @@ def test_iters_zero_leaves_potentials():
     np.testing.assert_array_equal(g, g0)
 
 
+def test_eps_scaling_schedule_d64():
+    # The split-f16 records are rebuilt per stage (their scale is 2 log2(e)/eps).
+    from workloads import geometric_eps_schedule
+    c = make_clouds("feature64_64k", n=1200, m=1700)
+    eps_list = geometric_eps_schedule(2.0, 0.05, 5)
+    f, g = gpu_solve_schedule(c, eps_list[0], eps_list[-1], len(eps_list), 15)
+    fo, go = oracle.sinkhorn_schedule(c["x"], c["y"], c["a"], c["b"], eps_list, 15)
+    ef, eg = rel_inf(f, fo, eps_list[-1]), rel_inf(g, go, eps_list[-1])
+    print(f"d=64 schedule: rel err f {ef:.2e} g {eg:.2e}", flush=True)
+    assert ef <= TOL_POT and eg <= TOL_POT
+    _check_stats(c, f, g, fo, go, eps_list[-1], "d=64 schedule")
+
+
+def test_warm_start_d64():
+    c = random_clouds(600, 900, 64, seed=8, spread=0.2)
+    eps = 0.1
+    f1, g1 = gpu_solve(c, eps, 4)
+    f2, g2 = gpu_solve(c, eps, 6, g0=g1)
+    fo, go = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, 10)
+    assert rel_inf(f2, fo, eps) <= TOL_POT and rel_inf(g2, go, eps) <= TOL_POT
+
+
 def test_warm_start_continues_the_iteration():
     c = random_clouds(700, 900, 3, seed=2)
     eps = 0.2
