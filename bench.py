@@ -323,10 +323,11 @@ def run_transport(name, torch, lds, reps=3):
     if d >= 32:
         # Matrix-pipe time per 32x32 subtile and wave: the split-f16 score
         # (3*kp/16 f16 MFMAs of 32 cycles + one fp32 MFMA of 64) and P.V
-        # (16 fp32 MFMAs of 64 cycles per 32 value channels), at 2.4 GHz on
-        # 1024 SIMDs; frac = that time / the measured call.
+        # (12 bf16 MFMAs of 32 cycles per 32 value channels: 2 column chunks
+        # x 6 split products), at 2.4 GHz on 1024 SIMDs; frac = that time /
+        # the measured call.
         kp = h3_kp(d)
-        cycles = 3 * kp // 16 * 32 + 64 + 16 * 64 * ((d + 31) // 32)
+        cycles = 3 * kp // 16 * 32 + 64 + 12 * 32 * ((d + 31) // 32)
         model_ms = (n / 32) * (m / 32) * cycles / (1024 * 2.4e9) * 1e3
         res["roofline_whole_call"] = {"bound": "mfma", "model_ms": model_ms,
                                       "frac": model_ms / res["apply_ms"],
