@@ -43,6 +43,10 @@ PEAK_MFMA_FP16_TFLOPS = 2500.0
 # FMA streams do not overlap).
 ISSUE_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
 EXP_SLOTS = 2.0
+# One 4x4 Sinkhorn-Knopp iteration of the Birkhoff kernel: 8 max-subtracted
+# log-sum-exps of 4 terms (32 exp2 + 8 log2 at two slots each, ~60 other VALU
+# instructions, plus the bookkeeping of the loop) ~ 192 issue slots.
+BIRKHOFF_SLOTS_PER_ITER = 192.0
 
 HALF_STEP_KERNELS = ("lse_rows_h3_kernel", "lse_rows_valu_kernel")
 
@@ -261,7 +265,13 @@ def run_birkhoff(name, torch, lds, reps=5):
             "useful_matrix_iters_per_s": useful / (ms / 1e3),
             "issued_matrix_iters_per_s": issued / (ms / 1e3),
             "mean_iters": useful / w.batch,
-            "hbm_gb_per_s": w.batch * (64 + 64 + 4) / (ms / 1e3) / 1e9}
+            "hbm_gb_per_s": w.batch * (64 + 64 + 4) / (ms / 1e3) / 1e9,
+            # Iterations issued (a wave runs until its slowest lane stops)
+            # against the issue-slot ceiling of the kernel's loop body.
+            "roofline": {"bound": "alu", "achieved": issued / (ms / 1e3),
+                         "peak": ISSUE_SLOTS_PER_S / BIRKHOFF_SLOTS_PER_ITER,
+                         "unit": "matrix-iterations/s",
+                         "frac": issued / (ms / 1e3) / (ISSUE_SLOTS_PER_S / BIRKHOFF_SLOTS_PER_ITER)}}
 
 
 def run_birkhoff_newton(name, torch, lds, reps=5):

@@ -33,8 +33,11 @@
  *  - Arguments are validated on the host before anything is enqueued; an
  *    invalid call returns OT_ERROR_INVALID_VALUE and enqueues nothing.
  *  - Preconditions that are NOT checked (checking would need a device read):
- *    finite inputs, a_i > 0, b_j > 0. Violations give NaN or inf results,
- *    not an error code.
+ *    finite inputs, a_i > 0, b_j > 0, and for d >= 32 the range of the
+ *    split-f16 matrix-core products, (2 log2(e)/eps) * max_ik |x_ik| *
+ *    max_jk |y_jk| < 2^30 (with x and y replaced by their unit-normalised
+ *    rows and eps by 2 eps in the cosine calls). Violations give NaN or inf
+ *    results, not an error code.
  *  - Outputs must not alias inputs unless a call says otherwise.
  *  - Calls are stateless; concurrent calls on different streams are safe.
  */

@@ -22,10 +22,12 @@
 //
 // f16 range. To keep hi and lo inside f16's range, the column side stores
 // (2 log2(e)/eps) q 2^-e and the row side p 2^e with one power of two e per
-// direction, chosen so that both sides' largest magnitudes meet at
-// sqrt((2 log2(e)/eps) max|p| max|q|); the product is unchanged. This needs
-// (2 log2(e)/eps) max|p_k| max|q_k| < 2^31 (beyond it fp32 scores would carry
-// no fractional bits either).
+// direction, chosen so that both sides' largest magnitudes meet near
+// T^(1/2), T = (2 log2(e)/eps) max|p| max|q|; the product is unchanged. With e
+// rounded to an integer one side's largest magnitude is at most (2T)^(1/2),
+// which stays below f16's largest finite value 65504 when T < 2^30 (near
+// 2^32 the hi parts become inf; fp32 scores would carry no fractional bits
+// there either).
 //
 // The column bias qhat_j and the row's running maximum M enter through one
 // fp32 MFMA at the end of the chain (k-slot 0: bias_j x 1, k-slot 1:
@@ -36,8 +38,9 @@
 // consecutive points fall in distinct LDS banks. Row records: hi then lo,
 // unswizzled (read once per workgroup). Biases and norms are fp32 arrays.
 // Workgroups of 8 waves own 256 rows and stream 128-column tiles through
-// double-buffered LDS with gfx950's direct global->LDS loads, as the fp32
-// kernel does; the lazy shared running maximum and the epilogue are the same.
+// double-buffered LDS with gfx950's direct global->LDS loads; the running
+// maximum is shared lazily by the two lane halves of a row and moved only when
+// a chunk sum leaves [2^-64, 2^16] (the epilogue in mfma_common.h).
 #include "mfma_common.h"
 
 #include <math.h>

@@ -154,6 +154,25 @@ def test_split_f16_long_solve_on_unit_gaussians():
     _check_solve(c, 0.25 * 8.0, 60, "d=64 N(0,I) 60 iterations")
 
 
+@pytest.mark.parametrize("log2_range,finite", [(29, True), (34, False)])
+def test_split_f16_range_precondition(log2_range, finite):
+    # The split-f16 records hold (2 log2(e)/eps) max|x| max|y| = T split
+    # evenly over the two sides up to a factor 2^(1/2); below T = 2^30 the hi
+    # parts stay finite in f16 and one half-step is as accurate as elsewhere,
+    # at T = 2^34 they overflow and the documented outcome is non-finite f.
+    c = random_clouds(300, 400, 32, seed=5, spread=1.0)
+    mx = float(np.abs(c["x"]).max()) * float(np.abs(c["y"]).max())
+    eps = 2.0 * np.log2(np.e) * mx / 2.0 ** log2_range
+    f1, _ = gpu_solve(c, eps, 1)
+    if finite:
+        f_ref = oracle.half_update(c["x"], c["y"], c["a"], np.zeros(400, np.float32), eps)
+        err = rel_inf(f1, f_ref)
+        print(f"T = 2^{log2_range}: eps {eps:.3g}, one half-step rel err f {err:.2e}", flush=True)
+        assert err <= TOL_SPLIT_HALF
+    else:
+        assert not np.all(np.isfinite(f1))
+
+
 def test_iters_zero_leaves_potentials():
     c = random_clouds(100, 80, 3, seed=1)
     f0 = np.linspace(-1, 1, 100).astype(np.float32)
