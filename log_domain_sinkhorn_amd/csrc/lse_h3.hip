@@ -44,6 +44,7 @@
 #include "mfma_common.h"
 
 #include <math.h>
+#include <type_traits>
 
 namespace otsk {
 
@@ -106,8 +107,10 @@ __global__ __launch_bounds__(kThreads) void lse_rows_h3_kernel(HalfStep h, int t
     float S = 0.f;
     float Mu_prev = M;
     floatx16 acc_prev = score_h3<KP>(lrec[0], lbias[0], 0, lane, li, hl, bh, bl, Mu_prev);
-    for (int t = tbeg; t < tend; ++t) {
-        const int b = (t - tbeg) & 1;
+    // One column tile from LDS buffer b (a compile-time constant, so every
+    // LDS operand address is a per-lane register plus an immediate offset).
+    auto tile = [&](int t, auto bc) {
+        constexpr int b = decltype(bc)::value;
         if (t + 1 < tend)
             issue_tile<TILE16, kWaves, kSub>(col4, colb, t + 1, lrec[b ^ 1], lbias[b ^ 1], wave,
                                              lane);
@@ -124,8 +127,8 @@ __global__ __launch_bounds__(kThreads) void lse_rows_h3_kernel(HalfStep h, int t
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        // First subtile of the next tile (on the last iteration: the idle
-        // buffer, never folded).
+        // First subtile of the next tile (on the last tile: the idle buffer,
+        // never folded).
         const float Mu_cur = M;
         const floatx16 acc_cur =
             score_h3<KP>(lrec[b ^ 1], lbias[b ^ 1], 0, lane, li, hl, bh, bl, Mu_cur);
@@ -134,6 +137,11 @@ __global__ __launch_bounds__(kThreads) void lse_rows_h3_kernel(HalfStep h, int t
         pin(M, S);
         acc_prev = acc_cur;
         Mu_prev = Mu_cur;
+    };
+    for (int t = tbeg; t < tend; t += 2) {
+        tile(t, std::integral_constant<int, 0>{});
+        if (t + 1 < tend)
+            tile(t + 1, std::integral_constant<int, 1>{});
     }
 
     const float So = __shfl_xor(S, 32);

@@ -32,6 +32,8 @@
 // partials are added in fp64, in split order. No atomics.
 #include "mfma_common.h"
 
+#include <type_traits>
+
 #include <math.h>
 
 namespace otsk {
@@ -147,8 +149,10 @@ __global__ __launch_bounds__(kThreads) void transport_mfma_kernel(
             O[nb][r] = 0.f;
     float rsum = 0.f;
 
-    for (int t = tbeg; t < tend; ++t) {
-        const int b = (t - tbeg) & 1;
+    // One column tile from LDS buffer b (a compile-time constant, so the
+    // operand addresses are per-lane registers plus immediate offsets).
+    auto tile = [&](int t, auto bc) {
+        constexpr int b = decltype(bc)::value;
         if (t + 1 < tend) {
             issue_tile<TILE4, kWaves, kSub>(col4, colb, t + 1, lrec[b ^ 1], lbias[b ^ 1], wave,
                                             lane);
@@ -200,6 +204,11 @@ __global__ __launch_bounds__(kThreads) void transport_mfma_kernel(
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+    for (int t = tbeg; t < tend; t += 2) {
+        tile(t, std::integral_constant<int, 0>{});
+        if (t + 1 < tend)
+            tile(t + 1, std::integral_constant<int, 1>{});
     }
 
     // The two lane halves summed different columns of the same row.
