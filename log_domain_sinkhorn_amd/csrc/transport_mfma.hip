@@ -76,6 +76,21 @@ __device__ __forceinline__ void split3_bf16(float v, __bf16 &h, __bf16 &m, __bf1
     l = (__bf16)r2;
 }
 
+// The same split for two values at once: each rounding is a lane of one
+// v_cvt_pk_bf16_f32, and the pair lands packed as the MFMA operand wants it.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split3_bf16x2(float2v v, bf16x2v &h, bf16x2v &m, bf16x2v &l) {
+    asm volatile("" : "+v"(v));
+    h = __builtin_convertvector(v, bf16x2v);
+    float2v r = v - __builtin_convertvector(h, float2v);
+    asm volatile("" : "+v"(r));
+    m = __builtin_convertvector(r, bf16x2v);
+    float2v r2 = r - __builtin_convertvector(m, float2v);
+    asm volatile("" : "+v"(r2));
+    l = __builtin_convertvector(r2, bf16x2v);
+}
+
 // Copy n16 16-byte chunks from src to LDS dst with direct global->LDS loads.
 template <int WAVES>
 __device__ __forceinline__ void issue_copy(const float4 *__restrict__ src, float4 *dst, int n16,
@@ -172,12 +187,16 @@ __global__ __launch_bounds__(kThreads) void transport_mfma_kernel(
             // B operands: chunk u = registers 8u..8u+7, three bf16 parts.
             bf16x8 ph[2], pm[2], plo[2];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                __bf16 h, mm, l;
-                split3_bf16(pr[r], h, mm, l);
-                ph[r / 8][r % 8] = h;
-                pm[r / 8][r % 8] = mm;
-                plo[r / 8][r % 8] = l;
+            for (int r = 0; r < 16; r += 2) {
+                bf16x2v h, mm, l;
+                float2v pv = {pr[r], pr[r + 1]};
+                split3_bf16x2(pv, h, mm, l);
+                ph[r / 8][r % 8] = h[0];
+                ph[r / 8][r % 8 + 1] = h[1];
+                pm[r / 8][r % 8] = mm[0];
+                pm[r / 8][r % 8 + 1] = mm[1];
+                plo[r / 8][r % 8] = l[0];
+                plo[r / 8][r % 8 + 1] = l[1];
             }
 #pragma unroll
             for (int nb = 0; nb < NVB; ++nb) {
