@@ -334,6 +334,7 @@ hipError_t launch_merge(const HalfStep &h, const Layout &L, int nsplit, hipStrea
 namespace {
 
 constexpr int kTargetBlocks = 2048;  // 8 waves per SIMD on 256 CUs x 4 SIMDs
+constexpr int kMinTilesPerSplit = 2;
 
 // Columns per LDS tile: 8 KB of fp64 records per buffer.
 constexpr int tile_cols_for(int rs) { return rs <= 4 ? 256 : (rs <= 8 ? 128 : (rs <= 16 ? 64 : 32)); }
@@ -364,6 +365,11 @@ ValuPlan plan_valu(const Layout &L, int64_t rows, int64_t cols_pad) {
     int64_t want = (kTargetBlocks + p.row_blocks - 1) / p.row_blocks;
     if (want > p.ntiles)
         want = p.ntiles;
+    // At least kMinTilesPerSplit tiles per workgroup, so its fixed costs (row
+    // records, the first tile's copy, the partial writes) are spread over
+    // more work (16384^2 at d = 3: 95 -> 90 us per half-step).
+    if (p.ntiles / want < kMinTilesPerSplit)
+        want = p.ntiles / kMinTilesPerSplit > 0 ? p.ntiles / kMinTilesPerSplit : 1;
     if (want > 65535)
         want = 65535;
     if (want < 1)
