@@ -278,42 +278,55 @@ __global__ __launch_bounds__(256) void lse_rows_valu_kernel(HalfStep h, int tile
     }
 }
 
-// Combine the per-split (M, S) pairs of each row: one wave per row, lane s
-// takes splits s, s + 64, ...; the maximum and the rescaled sum are reduced
-// across the wave in a fixed butterfly order (bitwise reproducible). A
-// thread-per-row loop over the splits is bound by the latency of its
-// dependent loads (25 us for 64 splits of 16384 rows); this takes one
-// round of loads.
-__device__ __forceinline__ double wave_max(double v) {
+// Combine the per-split (M, S) pairs of each row: G lanes per row (G = 32
+// when there are at most 32 splits, else 64), lane s takes splits s, s + G,
+// ...; the maximum and the rescaled sum are reduced across the G lanes in a
+// fixed butterfly order (bitwise reproducible, and the same for both G: the
+// extra butterfly step of G = 64 would only add zeros). A thread-per-row loop
+// over the splits is bound by the latency of its dependent loads (25 us for
+// 64 splits of 16384 rows); this takes one round of loads, and the first
+// split's pair stays in registers between the two reductions.
+template <int G>
+__device__ __forceinline__ double group_max(double v) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
+    for (int o = G / 2; o >= 1; o >>= 1)
         v = fmax(v, __shfl_xor(v, o));
     return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
+    for (int o = G / 2; o >= 1; o >>= 1)
         v += __shfl_xor(v, o);
     return v;
 }
 
+template <int G>
 __global__ __launch_bounds__(256) void lse_merge_kernel(HalfStep h, int nsplit, int kp, int rs) {
-    const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    constexpr int kRowsPerWave = 64 / G;
     const int lane = threadIdx.x & 63;
-    if (i >= h.rows)
-        return;  // whole waves only
-    double M = -INFINITY;
-    for (int s = lane; s < nsplit; s += 64)
-        M = fmax(M, h.partials[(int64_t)s * h.rows_pad + i].m);
-    M = wave_max(M);
-    float S = 0.f;
-    for (int s = lane; s < nsplit; s += 64) {
-        const Partial p = h.partials[(int64_t)s * h.rows_pad + i];
+    const int gl = lane % G;
+    const int64_t i =
+        ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowsPerWave + lane / G;
+    // Rows past the end take part in the shuffles with a valid row's data and
+    // write nothing.
+    const int64_t ir = i < h.rows ? i : h.rows - 1;
+    const bool has = gl < nsplit;
+    Partial first = {-INFINITY, 0.f, 0.f};
+    if (has)
+        first = h.partials[(int64_t)gl * h.rows_pad + ir];
+    double M = first.m;
+    for (int s = gl + G; s < nsplit; s += G)
+        M = fmax(M, h.partials[(int64_t)s * h.rows_pad + ir].m);
+    M = group_max<G>(M);
+    float S = has ? first.s * hw_exp2((float)(first.m - M)) : 0.f;
+    for (int s = gl + G; s < nsplit; s += G) {
+        const Partial p = h.partials[(int64_t)s * h.rows_pad + ir];
         S = fmaf(p.s, hw_exp2((float)(p.m - M)), S);
     }
-    S = wave_sum(S);
-    if (lane == 0) {
+    S = group_sum<G>(S);
+    if (gl == 0 && i < h.rows) {
         const double *p = static_cast<const double *>(h.row_rec) + i * rs;
         double q = 0.0;
         for (int k = 0; k < kp; ++k)
@@ -323,8 +336,15 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(HalfStep h, int nsplit, 
 }
 
 hipError_t launch_merge(const HalfStep &h, const Layout &L, int nsplit, hipStream_t s) {
-    const unsigned blocks = (unsigned)((h.rows + 3) / 4);
-    hipLaunchKernelGGL(lse_merge_kernel, dim3(blocks), dim3(256), 0, s, h, nsplit, L.kp, L.rs);
+    if (nsplit <= 32) {
+        const unsigned blocks = (unsigned)((h.rows + 7) / 8);
+        hipLaunchKernelGGL(lse_merge_kernel<32>, dim3(blocks), dim3(256), 0, s, h, nsplit, L.kp,
+                           L.rs);
+    } else {
+        const unsigned blocks = (unsigned)((h.rows + 3) / 4);
+        hipLaunchKernelGGL(lse_merge_kernel<64>, dim3(blocks), dim3(256), 0, s, h, nsplit, L.kp,
+                           L.rs);
+    }
     return hipGetLastError();
 }
 
