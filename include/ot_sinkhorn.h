@@ -40,6 +40,13 @@
  *    results, not an error code.
  *  - Outputs must not alias inputs unless a call says otherwise.
  *  - Calls are stateless; concurrent calls on different streams are safe.
+ *  - Graph capture: ot_sinkhorn_solve, ot_plan_stats, ot_transport_apply and
+ *    ot_birkhoff_project_batched have been captured into HIP graphs on
+ *    `stream` (their temporary memory becomes the graph's stream-ordered
+ *    allocations) and replayed with results identical to direct calls. The
+ *    calls that allocate inside another call (the cosine calls,
+ *    ot_barycentric_map, ot_cost_gradient_x) are not supported under
+ *    capture: a graph containing them faulted on replay.
  */
 #ifndef OT_SINKHORN_H
 #define OT_SINKHORN_H

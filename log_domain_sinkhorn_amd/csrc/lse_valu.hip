@@ -355,6 +355,7 @@ namespace {
 
 constexpr int kTargetBlocks = 2048;  // 8 waves per SIMD on 256 CUs x 4 SIMDs
 constexpr int kMinTilesPerSplit = 2;
+constexpr int kCUs = 256;
 
 // Columns per LDS tile: 8 KB of fp64 records per buffer.
 constexpr int tile_cols_for(int rs) { return rs <= 4 ? 256 : (rs <= 8 ? 128 : (rs <= 16 ? 64 : 32)); }
@@ -387,8 +388,10 @@ ValuPlan plan_valu(const Layout &L, int64_t rows, int64_t cols_pad) {
         want = p.ntiles;
     // At least kMinTilesPerSplit tiles per workgroup, so its fixed costs (row
     // records, the first tile's copy, the partial writes) are spread over
-    // more work (16384^2 at d = 3: 95 -> 90 us per half-step).
-    if (p.ntiles / want < kMinTilesPerSplit)
+    // more work (16384^2 at d = 3: 95 -> 90 us per half-step) -- unless that
+    // leaves fewer workgroups than CUs (1024^2: 16 -> 25 us per half-step).
+    if (p.ntiles / want < kMinTilesPerSplit &&
+        p.row_blocks * (p.ntiles / kMinTilesPerSplit) >= kCUs)
         want = p.ntiles / kMinTilesPerSplit > 0 ? p.ntiles / kMinTilesPerSplit : 1;
     if (want > 65535)
         want = 65535;
