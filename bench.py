@@ -271,11 +271,18 @@ def run_birkhoff(name, torch, lds, reps=5):
     iters = it.to(torch.int64)
     issued = int(iters.view(-1, 64).max(dim=1).values.sum().item()) * 64
     useful = int(iters.sum().item())
+    # Histogram of the iterations each matrix took (upper edges inclusive).
+    edges = [e for e in (1, 5, 10, 20, 50, 100, 150, 199) if e < w.max_iters] + [w.max_iters]
+    counts, lo = {}, 0
+    for e in edges:
+        counts[f"{lo + 1}-{e}"] = int(((iters > lo) & (iters <= e)).sum().item())
+        lo = e
     return {"name": name, "batch": w.batch, "max_iters": w.max_iters, "tol": w.tol,
             "ms": ms, "matrices_per_s": w.batch / (ms / 1e3),
             "useful_matrix_iters_per_s": useful / (ms / 1e3),
             "issued_matrix_iters_per_s": issued / (ms / 1e3),
             "mean_iters": useful / w.batch,
+            "iters_histogram": counts,
             "hbm_gb_per_s": w.batch * (64 + 64 + 4) / (ms / 1e3) / 1e9,
             # Iterations issued (a wave runs until its slowest lane stops)
             # against the issue-slot ceiling of the kernel's loop body.
