@@ -94,6 +94,7 @@ SHAPES = [
     (1, 1, 3), (1, 97, 3), (97, 1, 3), (7, 7, 3), (1023, 777, 3), (129, 4097, 1),
     (300, 200, 2), (2000, 1500, 5), (5000, 300, 3), (300, 5000, 3), (256, 256, 31),
     (256, 256, 32), (256, 256, 33), (512, 384, 64), (200, 300, 128), (257, 1000, 48),
+    (1, 97, 64), (97, 1, 64), (1, 1, 40), (129, 700, 96),
 ]
 
 
