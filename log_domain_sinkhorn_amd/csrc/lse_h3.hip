@@ -63,7 +63,9 @@ constexpr int kTargetBlocks = 1024;
 
 template <int KP>
 __global__ __launch_bounds__(kThreads) void lse_rows_h3_kernel(HalfStep h, int tiles_per_split,
-                                                               int ntiles) {
+                                                               int ntiles, int nrb, int nsplit) {
+    int rblk, split;
+    xcd_block(nrb, nsplit, rblk, split);
     constexpr int RC = KP / 4;
     constexpr int TILE16 = kTileCols * RC;
     static_assert(KP % 32 == 0, "records are whole groups of 8 chunks");
@@ -76,7 +78,6 @@ __global__ __launch_bounds__(kThreads) void lse_rows_h3_kernel(HalfStep h, int t
     const int wave = tid >> 6;
     const int hl = lane >> 5;
     const int li = lane & 31;
-    const int split = blockIdx.y;
     const int tbeg = split * tiles_per_split;
     const int tend = min(tbeg + tiles_per_split, ntiles);
     const float4 *col4 = static_cast<const float4 *>(h.col_rec);
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void lse_rows_h3_kernel(HalfStep h, int t
     }
     issue_tile<TILE16, kWaves, kSub>(col4, colb, tbeg, lrec[0], lbias[0], wave, lane);
     // Stationary B operands: this lane's k-halves of its row's hi and lo parts.
-    const int64_t i = (int64_t)blockIdx.x * kRowsPerBlock + wave * 32 + li;
+    const int64_t i = (int64_t)rblk * kRowsPerBlock + wave * 32 + li;
     const int64_t ic = i < h.rows ? i : h.rows - 1;
     half8 bh[KP / 16], bl[KP / 16];
     {
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void lse_rows_h3_kernel(HalfStep h, int t
     const float So = __shfl_xor(S, 32);
     const float Sm = hl == 0 ? S + So : So + S;
     if (hl == 0 && i < h.rows) {
-        if (gridDim.y == 1) {
+        if (nsplit == 1) {
             const float lse = M + hw_log2(Sm);
             const float hat = log2f(h.row_w[i]) - lse;
             static_cast<float *>(h.row_bias)[i] = hat;
@@ -433,9 +434,9 @@ H3Plan plan_h3(int64_t rows, int64_t cols_pad) {
 
 template <int KP>
 hipError_t launch_h3_kp(const HalfStep &h, const H3Plan &p, hipStream_t s) {
-    dim3 grid((unsigned)p.row_blocks, (unsigned)p.nsplit);
+    dim3 grid((unsigned)(p.row_blocks * p.nsplit));
     hipLaunchKernelGGL((lse_rows_h3_kernel<KP>), grid, dim3(kThreads), 0, s, h, p.tiles_per_split,
-                       p.ntiles);
+                       p.ntiles, (int)p.row_blocks, p.nsplit);
     return hipGetLastError();
 }
 

@@ -124,7 +124,9 @@ __device__ __forceinline__ void finish_row_f64(const HalfStep &h, int kp, int rs
 // --------------------------------------------------------------------------
 template <int KP, int R, int TJ>
 __global__ __launch_bounds__(256) void lse_rows_valu_kernel(HalfStep h, int tiles_per_split,
-                                                            int ntiles) {
+                                                            int ntiles, int nrb, int nsplit) {
+    int rblk, split;
+    xcd_block(nrb, nsplit, rblk, split);
     constexpr int RS = KP + 1;
     static_assert(RS % 4 == 0, "record stride must be a multiple of 4 elements");
     constexpr int RS2 = RS / 2;          // 16-byte words per record
@@ -137,8 +139,7 @@ __global__ __launch_bounds__(256) void lse_rows_valu_kernel(HalfStep h, int tile
     __shared__ double2 lds[2][TILE2];
 
     const int tid = threadIdx.x;
-    const int64_t row0 = (int64_t)blockIdx.x * (256 * R);
-    const int split = blockIdx.y;
+    const int64_t row0 = (int64_t)rblk * (256 * R);
     const int tbeg = split * tiles_per_split;
     const int tend = min(tbeg + tiles_per_split, ntiles);
     const double *row_rec = static_cast<const double *>(h.row_rec);
@@ -270,7 +271,7 @@ __global__ __launch_bounds__(256) void lse_rows_valu_kernel(HalfStep h, int tile
     for (int r = 0; r < R; ++r) {
         const int64_t i = row0 + tid + r * 256;
         if (i < h.rows) {
-            if (gridDim.y == 1)
+            if (nsplit == 1)
                 finish_row_f64(h, KP, RS, i, M[r], S[r], nrm[r]);
             else
                 h.partials[(int64_t)split * h.rows_pad + i] = Partial{M[r], S[r], 0.f};
@@ -405,9 +406,9 @@ ValuPlan plan_valu(const Layout &L, int64_t rows, int64_t cols_pad) {
 template <int KP, int R>
 hipError_t launch_kr(const HalfStep &h, const ValuPlan &p, hipStream_t s) {
     constexpr int TJ = tile_cols_for(KP + 1);
-    dim3 grid((unsigned)p.row_blocks, (unsigned)p.nsplit);
+    dim3 grid((unsigned)(p.row_blocks * p.nsplit));
     hipLaunchKernelGGL((lse_rows_valu_kernel<KP, R, TJ>), grid, dim3(256), 0, s, h,
-                       p.tiles_per_split, p.ntiles);
+                       p.tiles_per_split, p.ntiles, (int)p.row_blocks, p.nsplit);
     return hipGetLastError();
 }
 

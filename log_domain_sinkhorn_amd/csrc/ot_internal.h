@@ -162,4 +162,16 @@ hipError_t launch_birkhoff4_backward(const float *plan, const float *grad_plan, 
 // bias_mode values of launch_prep_side
 enum { kBiasZero = 0, kBiasHat = 1, kBiasRaw = 2 };
 
+// Workgroup -> (row block, column split) for a 1-D grid of nrb * nsplit
+// workgroups. The dispatcher deals workgroups to the 8 XCDs round robin; with
+// the split-major order below each XCD gets a contiguous run of (split, row
+// block) pairs, so it streams as few column splits through its L2 as
+// possible (at 65536^2, d = 64: one split per XCD pair, 17% less HBM traffic).
+__device__ __forceinline__ void xcd_block(int nrb, int nsplit, int &rb, int &split) {
+    const int L = (int)blockIdx.x, T = nrb * nsplit;
+    const int q = (T % 8 == 0) ? (L % 8) * (T / 8) + L / 8 : L;
+    split = q / nrb;
+    rb = q % nrb;
+}
+
 }  // namespace otsk
