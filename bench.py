@@ -360,6 +360,14 @@ def run_transport(name, torch, lds, reps=3):
         res["roofline_whole_call"] = {"bound": "mfma", "model_ms": model_ms,
                                       "frac": model_ms / res["apply_ms"],
                                       "model": f"{cycles} matrix-pipe cycles per 32x32 subtile"}
+    else:
+        # VALU path, per pair: d fp64 FMAs + 1 fp64 add (the exponent), one
+        # f64->f32 convert, exp2 at two issue slots, dv fp32 FMAs (P v).
+        slots = d + 1 + 1 + EXP_SLOTS + d
+        model_ms = n * m * slots / ISSUE_SLOTS_PER_S * 1e3
+        res["roofline_whole_call"] = {"bound": "alu", "model_ms": model_ms,
+                                      "frac": model_ms / res["apply_ms"],
+                                      "model": f"{slots:g} issue slots per pair"}
     return res
 
 
