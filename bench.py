@@ -323,7 +323,7 @@ def run_birkhoff_newton(name, torch, lds, reps=5):
             "backward_hbm_gb_per_s": w.batch * 192 / (bms / 1e3) / 1e9}
 
 
-def run_transport(name, torch, lds, reps=3):
+def run_transport(name, torch, lds, reps=10, warm=3):
     """Transport application P·y (values = the target points) and the
     x-gradient at the potentials of a short solve of workload ``name``."""
     from workloads import make_clouds
@@ -340,7 +340,8 @@ def run_transport(name, torch, lds, reps=3):
     res = {"name": name, "n": n, "m": m, "d": d, "dv": d}
     for label, fn in (("apply", lambda: lds.ot_transport_apply(x, y, f, g, eps, y, out)),
                       ("grad", lambda: lds.ot_cost_gradient_x(x, y, f, g, eps, out))):
-        fn()
+        for _ in range(warm):
+            fn()
         torch.cuda.synchronize()
         with Timer(torch) as t:
             for _ in range(reps):

@@ -180,11 +180,23 @@ struct TPlan {
 
 constexpr int tcols(int rs) { return rs <= 4 ? 256 : (rs <= 8 ? 128 : (rs <= 16 ? 64 : 32)); }
 
-TPlan plan_transport(const Layout &L, int64_t rows, int64_t cols_pad) {
+// Rows per lane: up to 4 for 3-D records with at most 4 value channels per
+// pass (more rows share each LDS read of a column; 65536^2 x 3: 1.26 -> 1.18 ms
+// against 2 rows), fewer while the grid would otherwise be short of
+// kTargetBlocks workgroups.
+TPlan plan_transport(const Layout &L, int64_t rows, int64_t cols_pad, int dvc) {
     TPlan p;
     p.TJ = tcols(L.rs);
     p.ntiles = (int)(cols_pad / p.TJ);
-    p.R = L.kp <= 3 ? 2 : 1;
+    const int max_r = L.kp <= 3 ? (dvc <= 4 ? 4 : 2) : 1;
+    p.R = 1;
+    for (int R = max_r; R >= 1; R /= 2) {
+        const int64_t rb = (rows + 256 * R - 1) / (256 * R);
+        if (rb * p.ntiles >= kTargetBlocks || R == 1) {
+            p.R = R;
+            break;
+        }
+    }
     p.row_blocks = (rows + 256 * p.R - 1) / (256 * p.R);
     int64_t want = (kTargetBlocks + p.row_blocks - 1) / p.row_blocks;
     if (want > p.ntiles)
@@ -213,6 +225,11 @@ template <int KP, int DV>
 hipError_t launch_tk(const double *xrec, const double *yrec, const float *v, int64_t m, int dv,
                      int k0, int64_t n, int64_t n_pad, double scale, const TPlan &p,
                      double *part, hipStream_t s) {
+    if (p.R == 4) {
+        if constexpr (KP <= 3 && DV <= 4)
+            return launch_tv<KP, 4, DV>(xrec, yrec, v, m, dv, k0, n, n_pad, scale, p, part, s);
+        return hipErrorInvalidValue;
+    }
     if (p.R == 2) {
         if constexpr (KP <= 3)
             return launch_tv<KP, 2, DV>(xrec, yrec, v, m, dv, k0, n, n_pad, scale, p, part, s);
@@ -245,10 +262,14 @@ hipError_t launch_t(const Layout &L, const double *xrec, const double *yrec, con
 
 }  // namespace
 
-int transport_value_chunk(int dv) { return dv <= 1 ? 1 : (dv <= 4 ? 4 : (dv <= 8 ? 8 : 16)); }
+// Value channels per pass: 3 exactly (the map and P.y of 3-D clouds), else
+// the next of 1, 4, 8, 16 (zero-padded channels cost their FMAs).
+int transport_value_chunk(int dv) {
+    return dv <= 1 ? 1 : (dv == 3 ? 3 : (dv <= 4 ? 4 : (dv <= 8 ? 8 : 16)));
+}
 
 size_t transport_scratch_doubles(const Layout &L, int64_t n, int64_t m_pad, int dv) {
-    const TPlan p = plan_transport(L, n, m_pad);
+    const TPlan p = plan_transport(L, n, m_pad, transport_value_chunk(dv));
     return (size_t)p.nsplit * (size_t)pad_points(n) * (size_t)transport_value_chunk(dv);
 }
 
@@ -256,14 +277,15 @@ hipError_t launch_transport_apply(const Layout &L, const void *xrec, const void 
                                   const float *v, int64_t n, int64_t n_pad, int64_t m,
                                   int64_t m_pad, int dv, double scale, double *part, float *out,
                                   hipStream_t s) {
-    const TPlan p = plan_transport(L, n, m_pad);
     const int dvc = transport_value_chunk(dv);
+    const TPlan p = plan_transport(L, n, m_pad, dvc);
     const double *xr = static_cast<const double *>(xrec);
     const double *yr = static_cast<const double *>(yrec);
     for (int k0 = 0; k0 < dv; k0 += dvc) {
         hipError_t e;
         switch (dvc) {
         case 1: e = launch_t<1>(L, xr, yr, v, m, dv, k0, n, n_pad, scale, p, part, s); break;
+        case 3: e = launch_t<3>(L, xr, yr, v, m, dv, k0, n, n_pad, scale, p, part, s); break;
         case 4: e = launch_t<4>(L, xr, yr, v, m, dv, k0, n, n_pad, scale, p, part, s); break;
         case 8: e = launch_t<8>(L, xr, yr, v, m, dv, k0, n, n_pad, scale, p, part, s); break;
         default: e = launch_t<16>(L, xr, yr, v, m, dv, k0, n, n_pad, scale, p, part, s); break;
@@ -275,6 +297,10 @@ hipError_t launch_transport_apply(const Layout &L, const void *xrec, const void 
         switch (dvc) {
         case 1:
             hipLaunchKernelGGL(transport_reduce_kernel<1>, dim3(blocks), dim3(256), 0, s, part,
+                               p.nsplit, n, n_pad, dv, k0, out);
+            break;
+        case 3:
+            hipLaunchKernelGGL(transport_reduce_kernel<3>, dim3(blocks), dim3(256), 0, s, part,
                                p.nsplit, n, n_pad, dv, k0, out);
             break;
         case 4:
