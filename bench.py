@@ -237,6 +237,25 @@ def roofline_for(r, workload):
             "work_per_launch": f"{n}*{m} pair-sides x ({flops_per_ps} flops + 1 exp2)"}
 
 
+def stats_roofline(n, m, d, stats_ms):
+    """Plan statistics (one row pass with cost, one column pass) against the
+    ceiling of the hardware that bounds them. d < 32: issue slots per pair,
+    row pass 2d (C by direct difference) + 3 (exponent) + 2 (exp2) + 2 (sums)
+    and column pass 2d + 3 + 2 + 1. d >= 32: each pass runs the half-step's
+    matrix work (6*kp f16 + 4 fp32 MFMA flops per pair, the fp32 ones
+    weighing 2500/157.3 f16 flops) against the f16 peak."""
+    if d >= 32:
+        kp = h3_kp(d)
+        equiv = 2.0 * n * m * (6 * kp + 4 * PEAK_MFMA_FP16_TFLOPS / PEAK_MFMA_FP32_TFLOPS)
+        model_ms = equiv / (PEAK_MFMA_FP16_TFLOPS * 1e12) * 1e3
+        return {"bound": "mfma", "model_ms": model_ms, "frac": model_ms / stats_ms,
+                "model": "2 passes x the half-step's matrix work"}
+    slots = (2 * d + 7) + (2 * d + 6)
+    model_ms = n * m * slots / ISSUE_SLOTS_PER_S * 1e3
+    return {"bound": "alu", "model_ms": model_ms, "frac": model_ms / stats_ms,
+            "model": f"{slots} issue slots per pair over both passes"}
+
+
 def cpu_baseline(name):
     import oracle
     from workloads import make_clouds
@@ -402,6 +421,7 @@ def main():
         "roofline": roofline_for(r, args.workload),
         "detail": {"calibration_copy_bytes": copy_bytes,
                    "solve_ms": r["solve_ms"], "stats_ms": r["stats_ms"],
+                   "stats_roofline": stats_roofline(r["n"], r["m"], r["d"], r["stats_ms"]),
                    "half_step_ms": r["half_step_ms"], "cost": r["cost"], "marg": r["marg"]},
     }
     if not args.no_cpu_baseline:
@@ -417,6 +437,7 @@ def main():
             s = run_cloud_workload(name, 1, 1, torch, lds)
             sec[name] = {"pair_evals_per_s": s["pair_evals_per_s"], "ms_per_step": s["ms_per_step"],
                          "solve_ms": s["solve_ms"], "stats_ms": s["stats_ms"],
+                         "stats_roofline": stats_roofline(s["n"], s["m"], s["d"], s["stats_ms"]),
                          "roofline": roofline_for(s, name)}
         for name in ("feature64_64k", "cube_gauss3d_64k"):
             key = f"transport:{name}"
