@@ -99,8 +99,9 @@ ot_status run_schedule_h3(const float *x, const float *y, const float *a, const 
     const size_t yv = align_up((size_t)m_pad * sizeof(float), 256);
     const size_t pb = align_up(part * sizeof(Partial), 256);
     const size_t mb = align_up(h3_maxabs_floats() * sizeof(float), 256);
+    const size_t cb = align_up(h3_center_scratch_bytes(d), 256);
     Scratch sc(s);
-    hipError_t e = sc.alloc(2 * xr + 2 * yr + 2 * xv + 2 * yv + pb + mb);
+    hipError_t e = sc.alloc(2 * xr + 2 * yr + 2 * xv + 2 * yv + pb + mb + cb);
     if (e != hipSuccess)
         return map_error(e);
     char *p = static_cast<char *>(sc.ptr);
@@ -114,18 +115,19 @@ ot_status run_schedule_h3(const float *x, const float *y, const float *a, const 
     p += 2 * yv;
     Partial *partials = reinterpret_cast<Partial *>(p);
     float *maxabs = reinterpret_cast<float *>(p + pb);
+    void *csc = p + pb + mb;
 
-    if ((e = launch_maxabs(x, n * d, y, m * d, maxabs, s)) != hipSuccess)
+    if ((e = launch_center_maxabs(x, n, y, m, d, csc, maxabs, s)) != hipSuccess)
         return map_error(e);
     for (int st = 0; st < stages; ++st) {
         const double eps = eps_list[st];
         const double scale = 2.0 * kLog2e / eps;
         const double hat_scale = kLog2e / eps;
         if ((e = launch_prep_h3(x, nullptr, n, n_pad, d, kp, scale, hat_scale, kBiasZero, maxabs,
-                                0, xcol, xrow, xnrm, xbias, s)) != hipSuccess)
+                                csc, 0, xcol, xrow, xnrm, xbias, s)) != hipSuccess)
             return map_error(e);
-        if ((e = launch_prep_h3(y, g, m, m_pad, d, kp, scale, hat_scale, kBiasHat, maxabs, 1, ycol,
-                                yrow, ynrm, ybias, s)) != hipSuccess)
+        if ((e = launch_prep_h3(y, g, m, m_pad, d, kp, scale, hat_scale, kBiasHat, maxabs, csc,
+                                1, ycol, yrow, ynrm, ybias, s)) != hipSuccess)
             return map_error(e);
         HalfStep hf{xrow, xbias, a, ycol, ybias, 1, 0, f, n, m_pad, scale, eps * kLn2,
                     partials, n_pad, xnrm};
@@ -220,8 +222,9 @@ ot_status plan_stats_h3(const float *x, const float *y, const float *a, const fl
     const size_t yv = align_up((size_t)m_pad * sizeof(float), 256);
     const size_t mb = align_up(h3_maxabs_floats() * sizeof(float), 256);
     const size_t db = plan_stats_h3_scratch_doubles(n, m, n_pad, m_pad) * sizeof(double);
+    const size_t cb = align_up(h3_center_scratch_bytes(d), 256);
     Scratch sc(s);
-    hipError_t e = sc.alloc(2 * xr + 2 * yr + 2 * xv + 2 * yv + mb + db);
+    hipError_t e = sc.alloc(2 * xr + 2 * yr + 2 * xv + 2 * yv + mb + db + cb);
     if (e != hipSuccess)
         return map_error(e);
     char *p = static_cast<char *>(sc.ptr);
@@ -235,15 +238,16 @@ ot_status plan_stats_h3(const float *x, const float *y, const float *a, const fl
     p += 2 * yv;
     float *maxabs = reinterpret_cast<float *>(p);
     double *dsc = reinterpret_cast<double *>(p + mb);
+    void *csc = p + mb + db;
     const double scale = 2.0 * kLog2e / (double)eps;
     const double hat_scale = kLog2e / (double)eps;
-    if ((e = launch_maxabs(x, n * d, y, m * d, maxabs, s)) != hipSuccess)
+    if ((e = launch_center_maxabs(x, n, y, m, d, csc, maxabs, s)) != hipSuccess)
         return map_error(e);
-    if ((e = launch_prep_h3(x, f, n, n_pad, d, kp, scale, hat_scale, kBiasHat, maxabs, 0, xcol,
-                            xrow, xnrm, xhat, s)) != hipSuccess)
+    if ((e = launch_prep_h3(x, f, n, n_pad, d, kp, scale, hat_scale, kBiasHat, maxabs, csc, 0,
+                            xcol, xrow, xnrm, xhat, s)) != hipSuccess)
         return map_error(e);
-    if ((e = launch_prep_h3(y, g, m, m_pad, d, kp, scale, hat_scale, kBiasHat, maxabs, 1, ycol,
-                            yrow, ynrm, yhat, s)) != hipSuccess)
+    if ((e = launch_prep_h3(y, g, m, m_pad, d, kp, scale, hat_scale, kBiasHat, maxabs, csc, 1,
+                            ycol, yrow, ynrm, yhat, s)) != hipSuccess)
         return map_error(e);
     e = launch_plan_stats_h3(kp, xrow, xcol, xhat, xnrm, yrow, ycol, yhat, ynrm, a, b, n, m, n_pad,
                              m_pad, scale, cost, marg, dsc, s);
@@ -378,9 +382,10 @@ static ot_status transport_apply_impl(const float *x, const float *y, const floa
         const size_t yv = align_up((size_t)m_pad * sizeof(float), 256);
         const size_t mb = align_up(h3_maxabs_floats() * sizeof(float), 256);
         const size_t pd = transport_mfma_scratch_doubles(n, m_pad, dv, rowsum != nullptr);
+        const size_t cb = align_up(h3_center_scratch_bytes(d), 256);
         Scratch sc(s);
-        if ((e = sc.alloc(2 * xr + 2 * yr + 2 * xv + 2 * yv + mb + pd * sizeof(double))) !=
-            hipSuccess)
+        if ((e = sc.alloc(2 * xr + 2 * yr + 2 * xv + 2 * yv + mb + cb +
+                          pd * sizeof(double))) != hipSuccess)
             return map_error(e);
         char *p = static_cast<char *>(sc.ptr);
         void *xcol = p, *xrow = p + xr;
@@ -392,12 +397,13 @@ static ot_status transport_apply_impl(const float *x, const float *y, const floa
         float *ynrm = reinterpret_cast<float *>(p), *yhat = reinterpret_cast<float *>(p + yv);
         p += 2 * yv;
         float *maxabs = reinterpret_cast<float *>(p);
-        double *part = reinterpret_cast<double *>(p + mb);
-        if ((e = launch_maxabs(x, n * d, y, m * d, maxabs, s)) != hipSuccess ||
-            (e = launch_prep_h3(x, f, n, n_pad, d, kp, scale, hat_scale, kBiasHat, maxabs, 0, xcol,
-                                xrow, xnrm, xhat, s)) != hipSuccess ||
-            (e = launch_prep_h3(y, g, m, m_pad, d, kp, scale, hat_scale, kBiasHat, maxabs, 1, ycol,
-                                yrow, ynrm, yhat, s)) != hipSuccess)
+        void *csc = p + mb;
+        double *part = reinterpret_cast<double *>(p + mb + cb);
+        if ((e = launch_center_maxabs(x, n, y, m, d, csc, maxabs, s)) != hipSuccess ||
+            (e = launch_prep_h3(x, f, n, n_pad, d, kp, scale, hat_scale, kBiasHat, maxabs, csc,
+                                0, xcol, xrow, xnrm, xhat, s)) != hipSuccess ||
+            (e = launch_prep_h3(y, g, m, m_pad, d, kp, scale, hat_scale, kBiasHat, maxabs, csc,
+                                1, ycol, yrow, ynrm, yhat, s)) != hipSuccess)
             return map_error(e);
         return map_error(launch_transport_apply_mfma(kp, xrow, xhat, ycol, yhat, v, n, n_pad, m,
                                                      m_pad, dv, part, out, rowsum, s));

@@ -182,9 +182,57 @@ __global__ __launch_bounds__(256) void lse_merge_h3_kernel(HalfStep h, int nspli
 // Records.
 // ---------------------------------------------------------------------------
 
-// Largest |coordinate| of x (blockIdx.y == 0) or y (1), one value per block.
+// Centre of the two clouds, c = (mean(x) + mean(y)) / 2 (unweighted). The
+// cost |x_i - y_j|^2 does not change when both clouds move by the same
+// vector; records of x - c and y - c keep |p| |q| near the size of the costs
+// themselves, so the expanded form |p|^2 + |q|^2 - 2 p.q does not cancel
+// away the precision of the dot product when the clouds sit far from the
+// origin. Per block: fp64 column sums over a strided set of rows of one side
+// (blockIdx.y), 256 / d threads per coordinate.
+__global__ __launch_bounds__(256) void center_partial_kernel(const float *__restrict__ x,
+                                                             int64_t n,
+                                                             const float *__restrict__ y,
+                                                             int64_t m, int d,
+                                                             double *__restrict__ part) {
+    __shared__ double red[256];
+    const float *p = blockIdx.y ? y : x;
+    const int64_t cnt = blockIdx.y ? m : n;
+    const int rows = 256 / d;
+    const int tid = threadIdx.x;
+    const int k = tid % d, r0 = tid / d;
+    double sum = 0.0;
+    if (r0 < rows)
+        for (int64_t r = (int64_t)blockIdx.x * rows + r0; r < cnt; r += (int64_t)gridDim.x * rows)
+            sum += (double)p[r * d + k];
+    red[tid] = sum;
+    __syncthreads();
+    if (tid < d) {
+        double t = 0.0;
+        for (int q = 0; q < rows; ++q)
+            t += red[q * d + tid];
+        part[((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * d + tid] = t;
+    }
+}
+
+__global__ __launch_bounds__(128) void center_final_kernel(const double *__restrict__ part, int nb,
+                                                           int d, int64_t n, int64_t m,
+                                                           float *__restrict__ center) {
+    const int k = threadIdx.x;
+    if (k >= d)
+        return;
+    double sx = 0.0, sy = 0.0;
+    for (int b = 0; b < nb; ++b) {
+        sx += part[(int64_t)b * d + k];
+        sy += part[((int64_t)nb + b) * d + k];
+    }
+    center[k] = (float)(0.5 * (sx / (double)n + sy / (double)m));
+}
+
+// Largest |coordinate| of x - c (blockIdx.y == 0) or y - c (1), one value per
+// block.
 __global__ __launch_bounds__(256) void maxabs_kernel(const float *__restrict__ x, int64_t nx,
                                                      const float *__restrict__ y, int64_t ny,
+                                                     const float *__restrict__ center, int d,
                                                      float *__restrict__ part) {
     __shared__ float red[4];
     const float *p = blockIdx.y ? y : x;
@@ -192,7 +240,7 @@ __global__ __launch_bounds__(256) void maxabs_kernel(const float *__restrict__ x
     float mx = 0.f;
     for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < cnt;
          e += (int64_t)gridDim.x * 256)
-        mx = fmaxf(mx, fabsf(p[e]));
+        mx = fmaxf(mx, fabsf((float)((double)p[e] - (double)center[e % d])));
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1)
         mx = fmaxf(mx, __shfl_xor(mx, o));
@@ -247,19 +295,20 @@ __device__ __forceinline__ float4 pack8(const _Float16 (&v)[8]) {
     return __builtin_bit_cast(float4, h);
 }
 
-// One side's records at one eps: column record (scaled, split, swizzled), row
-// record (split), |p|^2 and the bias (zero, hat of pot, or padding).
+// One side's records at one eps, of the centred points p = x - c: column
+// record (scaled, split, swizzled), row record (split), |p|^2 and the bias
+// (zero, hat of pot, or padding).
 __global__ __launch_bounds__(256) void prep_h3_kernel(
-    const float *__restrict__ pts, const float *__restrict__ pot, int64_t count, int64_t padded,
-    int d, int kp, double scale, double hat_scale, int bias_mode, const float *__restrict__ maxabs,
-    int own, float4 *__restrict__ colrec, float4 *__restrict__ rowrec, float *__restrict__ nrm_out,
-    float *__restrict__ bias) {
+    const float *__restrict__ pts, const float *__restrict__ pot, const float *__restrict__ center,
+    int64_t count, int64_t padded, int d, int kp, double scale, double hat_scale, int bias_mode,
+    const float *__restrict__ maxabs, int own, float4 *__restrict__ colrec,
+    float4 *__restrict__ rowrec, float *__restrict__ nrm_out, float *__restrict__ bias) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= padded)
         return;
     const double bo = maxabs[own], bt = maxabs[1 - own];
-    const float cf = (float)ldexp(scale, -balance_exp(scale, bo, bt));
-    const float rf = (float)ldexp(1.0, balance_exp(scale, bt, bo));
+    const double cf = ldexp(scale, -balance_exp(scale, bo, bt));
+    const double rf = ldexp(1.0, balance_exp(scale, bt, bo));
     const int rc = kp / 4;
     const int hc = kp / 8;
     const int sw = (int)(i & swizzle_mask(rc));
@@ -270,10 +319,10 @@ __global__ __launch_bounds__(256) void prep_h3_kernel(
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const int k = 8 * q + r;
-            const float v = (real && k < d) ? pts[i * d + k] : 0.f;
-            nrm = fma((double)v, (double)v, nrm);
-            ch[r] = split_hi(v * cf, cl[r]);
-            rh[r] = split_hi(v * rf, rl[r]);
+            const double v = (real && k < d) ? (double)pts[i * d + k] - (double)center[k] : 0.0;
+            nrm = fma(v, v, nrm);
+            ch[r] = split_hi((float)(v * cf), cl[r]);
+            rh[r] = split_hi((float)(v * rf), rl[r]);
         }
         colrec[i * rc + (q ^ sw)] = pack8(ch);
         colrec[i * rc + ((hc + q) ^ sw)] = pack8(cl);
@@ -441,6 +490,7 @@ hipError_t launch_h3_kp(const HalfStep &h, const H3Plan &p, hipStream_t s) {
 }
 
 constexpr int kMaxabsBlocks = 256;
+constexpr int kCenterBlocks = 256;
 
 }  // namespace
 
@@ -448,12 +498,28 @@ int h3_kp(int d) { return (d + 31) / 32 * 32; }
 
 size_t h3_maxabs_floats() { return 2 * kMaxabsBlocks + 2; }
 
-hipError_t launch_maxabs(const float *x, int64_t nx, const float *y, int64_t ny, float *scratch,
-                         hipStream_t s) {
-    hipLaunchKernelGGL(maxabs_kernel, dim3(kMaxabsBlocks, 2), dim3(256), 0, s, x, nx, y, ny,
-                       scratch + 2);
+size_t h3_center_scratch_bytes(int d) {
+    return (size_t)2 * kCenterBlocks * d * sizeof(double) + (size_t)d * sizeof(float);
+}
+
+hipError_t launch_center_maxabs(const float *x, int64_t n, const float *y, int64_t m, int d,
+                                void *center_scratch, float *scratch, hipStream_t s) {
+    if (d < 1 || d > 128)
+        return hipErrorInvalidValue;
+    double *part = static_cast<double *>(center_scratch);
+    float *center = reinterpret_cast<float *>(part + (size_t)2 * kCenterBlocks * d);
+    hipLaunchKernelGGL(center_partial_kernel, dim3(kCenterBlocks, 2), dim3(256), 0, s, x, n, y, m,
+                       d, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(center_final_kernel, dim3(1), dim3(128), 0, s, part, kCenterBlocks, d, n, m,
+                       center);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(maxabs_kernel, dim3(kMaxabsBlocks, 2), dim3(256), 0, s, x, n * d, y, m * d,
+                       center, d, scratch + 2);
+    if ((e = hipGetLastError()) != hipSuccess)
         return e;
     hipLaunchKernelGGL(maxabs_final_kernel, dim3(1), dim3(64), 0, s, scratch + 2, kMaxabsBlocks,
                        scratch);
@@ -462,11 +528,13 @@ hipError_t launch_maxabs(const float *x, int64_t nx, const float *y, int64_t ny,
 
 hipError_t launch_prep_h3(const float *pts, const float *pot, int64_t count, int64_t padded, int d,
                           int kp, double scale, double hat_scale, int bias_mode,
-                          const float *maxabs, int own, void *colrec, void *rowrec, float *nrm,
-                          float *bias, hipStream_t s) {
+                          const float *maxabs, const void *center_scratch, int own, void *colrec,
+                          void *rowrec, float *nrm, float *bias, hipStream_t s) {
     const unsigned blocks = (unsigned)((padded + 255) / 256);
-    hipLaunchKernelGGL(prep_h3_kernel, dim3(blocks), dim3(256), 0, s, pts, pot, count, padded, d,
-                       kp, scale, hat_scale, bias_mode, maxabs, own,
+    const float *center = reinterpret_cast<const float *>(
+        static_cast<const double *>(center_scratch) + (size_t)2 * kCenterBlocks * d);
+    hipLaunchKernelGGL(prep_h3_kernel, dim3(blocks), dim3(256), 0, s, pts, pot, center, count,
+                       padded, d, kp, scale, hat_scale, bias_mode, maxabs, own,
                        static_cast<float4 *>(colrec), static_cast<float4 *>(rowrec), nrm, bias);
     return hipGetLastError();
 }

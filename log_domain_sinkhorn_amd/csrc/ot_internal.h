@@ -117,17 +117,20 @@ hipError_t launch_combine(const float *w, int ws, const float *r, const float *x
                           int64_t n, int d, int mode, float *out, hipStream_t s);
 
 // Half-step with split-f16 matrix-core products (d >= 32): records from
-// launch_prep_h3 (column record, row record, |p|^2, fp32 bias per side) after
-// launch_maxabs has written max|x| and max|y| to maxabs[0..1] (scratch of
-// h3_maxabs_floats() floats).
+// launch_prep_h3 (column record, row record, |p|^2, fp32 bias per side) of
+// the centred points p = x - c, after launch_center_maxabs has written the
+// centre c = (mean(x) + mean(y)) / 2 into center_scratch
+// (h3_center_scratch_bytes(d) bytes) and max|x - c|, max|y - c| to
+// maxabs[0..1] (scratch of h3_maxabs_floats() floats).
 int h3_kp(int d);
 size_t h3_maxabs_floats();
-hipError_t launch_maxabs(const float *x, int64_t nx, const float *y, int64_t ny, float *scratch,
-                         hipStream_t s);
+size_t h3_center_scratch_bytes(int d);
+hipError_t launch_center_maxabs(const float *x, int64_t n, const float *y, int64_t m, int d,
+                                void *center_scratch, float *maxabs, hipStream_t s);
 hipError_t launch_prep_h3(const float *pts, const float *pot, int64_t count, int64_t padded, int d,
                           int kp, double scale, double hat_scale, int bias_mode,
-                          const float *maxabs, int own, void *colrec, void *rowrec, float *nrm,
-                          float *bias, hipStream_t s);
+                          const float *maxabs, const void *center_scratch, int own, void *colrec,
+                          void *rowrec, float *nrm, float *bias, hipStream_t s);
 size_t half_step_partials_h3(int64_t rows, int64_t cols_pad);
 // One plan-statistics pass on split-f16 records (hat biases of the
 // potentials): part[split][row] = (sum_j P_ij, cost ? sum_j P_ij C_ij : 0).

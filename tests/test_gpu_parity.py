@@ -126,6 +126,27 @@ def test_plan_stats_shapes(n, m, d):
     assert abs(st["marg_col"] - sk["marg_col"]) <= TOL_MARG
 
 
+@pytest.mark.parametrize("d,offset", [(64, 30.0), (40, -50.0), (3, 30.0)])
+def test_plan_stats_offset_clouds(d, offset):
+    # Both clouds far from the origin: the d >= 32 records are built from the
+    # centred points, so cost and marginals keep the precision they have near
+    # the origin (the d < 32 path forms its scores in fp64).
+    c = random_clouds(400, 500, d, seed=d + 11, spread=1.0 / np.sqrt(d))
+    c["x"] = c["x"] + np.float32(offset)
+    c["y"] = c["y"] + np.float32(offset)
+    eps = 0.3
+    fo, go = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, 6)
+    f, g = fo.astype(np.float32), go.astype(np.float32)
+    st = gpu_plan_stats(c, f, g, eps)
+    sk = oracle.plan_stats(c["x"], c["y"], c["a"], c["b"], f, g, eps)
+    ec = abs(st["cost"] - sk["cost"]) / abs(sk["cost"])
+    print(f"stats offset {offset:g} d={d}: cost rel {ec:.1e}; marg {st['marg_row']:.3e}/"
+          f"{st['marg_col']:.3e} vs {sk['marg_row']:.3e}/{sk['marg_col']:.3e}", flush=True)
+    assert ec <= TOL_COST
+    assert abs(st["marg_row"] - sk["marg_row"]) <= TOL_MARG
+    assert abs(st["marg_col"] - sk["marg_col"]) <= TOL_MARG
+
+
 # d >= 32 runs on split-f16 matrix-core products (three f16 products per fp32
 # product, fp32 accumulation). The split itself keeps ~22 bits of each
 # coordinate; the matrix core's aligned sums lose about 2^-21 of the largest
@@ -133,12 +154,24 @@ def test_plan_stats_shapes(n, m, d):
 # cases use N(0, I) clouds (coordinates up to ~4.5, so products up to ~20 and
 # many coordinates small enough that their lo parts are f16 subnormals), at
 # several eps; one half-step is held to the same bound as the other paths.
+# The records hold the points centred on the mean of the two cloud means, so
+# clouds far from the origin (offset != 0) meet the same bound: uncentred,
+# the expanded |x|^2 + |y|^2 - 2 x.y of clouds 30 units out cancels about
+# 2^10 of the products' precision (measured 2.8e-4 after three iterations).
 TOL_SPLIT_HALF = TOL_HALF
 
 
-@pytest.mark.parametrize("d,eps_factor", [(32, 0.5), (64, 0.5), (64, 0.1), (128, 0.1), (96, 1.0)])
-def test_split_f16_half_step_on_unit_gaussians(d, eps_factor):
+@pytest.mark.parametrize("d,eps_factor,offset", [(32, 0.5, 0.0), (64, 0.5, 0.0), (64, 0.1, 0.0),
+                                                 (128, 0.1, 0.0), (96, 1.0, 0.0),
+                                                 (64, 0.5, 30.0), (32, 0.1, -50.0)])
+def test_split_f16_half_step_on_unit_gaussians(d, eps_factor, offset):
+    # offset != 0: both clouds moved far from the origin. The records hold
+    # x - c and y - c (c the mean of the two cloud means; the cost does not
+    # change), so the products stay near the size of the costs and the same
+    # bound holds.
     c = random_clouds(1024, 1536, d, seed=d, spread=1.0)
+    c["x"] = c["x"] + np.float32(offset)
+    c["y"] = c["y"] + np.float32(offset)
     eps = eps_factor * d ** 0.5
     fo, go = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, 5)
     g32 = go.astype(np.float32)
@@ -146,7 +179,8 @@ def test_split_f16_half_step_on_unit_gaussians(d, eps_factor):
     f_ref = oracle.half_update(c["x"], c["y"], c["a"], g32, eps)
     g_ref = oracle.half_update(c["y"], c["x"], c["b"], f1, eps)
     ef, eg = rel_inf(f1, f_ref), rel_inf(g1, g_ref)
-    print(f"d={d} eps={eps:.3g}: one half-step rel err f {ef:.2e} g {eg:.2e}", flush=True)
+    print(f"d={d} eps={eps:.3g} offset {offset:g}: one half-step rel err f {ef:.2e} g {eg:.2e}",
+          flush=True)
     assert ef <= TOL_SPLIT_HALF and eg <= TOL_SPLIT_HALF
 
 

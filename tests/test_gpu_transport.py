@@ -124,6 +124,26 @@ def test_shapes(n, m, d):
     assert em <= TOL_APPLY and eg <= TOL_APPLY
 
 
+@pytest.mark.parametrize("d,offset", [(64, 30.0), (33, -50.0), (3, 30.0)])
+def test_offset_clouds(d, offset):
+    # Both clouds far from the origin: the plan comes from scores of the
+    # centred points (d >= 32) or fp64 scores (d < 32), so P.v keeps its
+    # precision.
+    c = random_clouds(300, 600, d, seed=d + 21, spread=1.0 / np.sqrt(d))
+    c["x"] = c["x"] + np.float32(offset)
+    c["y"] = c["y"] + np.float32(offset)
+    eps = 0.2
+    f, g = _oracle_potentials(c, eps, 8)
+    for dv in (3, 64):
+        v = random_values(600, dv, seed=dv + 5)
+        e = rel_inf(gpu_apply(c, f, g, eps, v), oracle.transport_apply(c["x"], c["y"], f, g, eps, v))
+        print(f"offset {offset:g} d={d} dv={dv}: apply rel err {e:.2e}", flush=True)
+        assert e <= TOL_APPLY
+    em = rel_inf(gpu_map(c, f, g, eps), oracle.barycentric_map(c["x"], c["y"], c["a"], f, g, eps))
+    print(f"offset {offset:g} d={d}: map rel err {em:.2e}", flush=True)
+    assert em <= TOL_APPLY
+
+
 @pytest.mark.parametrize("d,dv", [(3, 1024), (64, 1024), (64, 200), (3, 17)])
 def test_wide_values(d, dv):
     c = random_clouds(300, 400, d, seed=d + dv, spread=1.0 / np.sqrt(d))
