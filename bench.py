@@ -256,6 +256,24 @@ def stats_roofline(n, m, d, stats_ms):
             "model": f"{slots} issue slots per pair over both passes"}
 
 
+def gemm_calibration(torch, n=8192, reps=10):
+    """A plain f16 GEMM (n x n x n, torch.matmul on the vendor BLAS) timed on the
+    same GPU in the same run: the matrix-core throughput a dense library
+    product sustains here, under the same power and clock limits as the
+    half-step kernel. Context for the matrix roofline fraction; not a peak."""
+    a = torch.randn(n, n, device="cuda:0", dtype=torch.float16)
+    b = torch.randn(n, n, device="cuda:0", dtype=torch.float16)
+    for _ in range(3):
+        c = a @ b
+    with Timer(torch) as t:
+        for _ in range(reps):
+            c = a @ b
+    del c
+    tflops = 2.0 * n ** 3 * reps / (t.ms() / 1e3) / 1e12
+    return {"op": f"f16 GEMM {n}^3 (torch.matmul)", "tflops": tflops,
+            "frac_of_peak": tflops / PEAK_MFMA_FP16_TFLOPS}
+
+
 def cpu_baseline(name):
     import oracle
     from workloads import make_clouds
@@ -420,6 +438,7 @@ def main():
                    "step": "cold-start solve + plan statistics"},
         "roofline": roofline_for(r, args.workload),
         "detail": {"calibration_copy_bytes": copy_bytes,
+                   "f16_gemm_same_gpu": gemm_calibration(torch) if r["d"] >= 32 else None,
                    "solve_ms": r["solve_ms"], "stats_ms": r["stats_ms"],
                    "stats_roofline": stats_roofline(r["n"], r["m"], r["d"], r["stats_ms"]),
                    "half_step_ms": r["half_step_ms"], "cost": r["cost"], "marg": r["marg"]},
