@@ -47,6 +47,14 @@ EXP_SLOTS = 2.0
 # log-sum-exps of 4 terms (32 exp2 + 8 log2 at two slots each, ~60 other VALU
 # instructions, plus the bookkeeping of the loop) ~ 192 issue slots.
 BIRKHOFF_SLOTS_PER_ITER = 192.0
+# One step of the 4x4 Newton dual solver (fp64 exponents and row maxima, row
+# softmaxes, gradient and 3x3 Hessian, Cholesky solve, line search), from the
+# rocprofv3 instruction counts of the 2^20-matrix batch: 7363 VALU
+# instructions per matrix, 755 of them transcendental (two issue slots), over
+# 5.37 steps per matrix on average -> (7363 + 755) / 5.37 ~ 1512 issue slots
+# per matrix-step, the per-matrix setup and final plan included.
+NEWTON_SLOTS_PER_STEP = 1512.0
+HBM_PEAK_BYTES_PER_S = 8.0e12
 
 HALF_STEP_KERNELS = ("lse_rows_h3_kernel", "lse_rows_valu_kernel")
 
@@ -357,7 +365,19 @@ def run_birkhoff_newton(name, torch, lds, reps=5):
             "forward_matrices_per_s": w.batch / (fms / 1e3),
             "forward_backward_matrices_per_s": w.batch / ((fms + bms) / 1e3),
             "mean_steps": float(steps.float().mean().item()), "max_steps_taken": int(steps.max()),
-            "backward_hbm_gb_per_s": w.batch * 192 / (bms / 1e3) / 1e9}
+            "backward_hbm_gb_per_s": w.batch * 192 / (bms / 1e3) / 1e9,
+            # forward: issue-bound (one matrix per lane, fp64 and exp2 work in
+            # registers); backward: HBM-bound, 192 bytes per matrix
+            "roofline": {"bound": "alu",
+                         "achieved": float(steps.sum().item()) / (fms / 1e3),
+                         "peak": ISSUE_SLOTS_PER_S / NEWTON_SLOTS_PER_STEP,
+                         "unit": "matrix-steps/s",
+                         "frac": float(steps.sum().item()) / (fms / 1e3)
+                         / (ISSUE_SLOTS_PER_S / NEWTON_SLOTS_PER_STEP)},
+            "backward_roofline": {"bound": "hbm",
+                                  "achieved": w.batch * 192 / (bms / 1e3) / 1e9,
+                                  "peak": HBM_PEAK_BYTES_PER_S / 1e9, "unit": "GB/s",
+                                  "frac": w.batch * 192 / (bms / 1e3) / HBM_PEAK_BYTES_PER_S}}
 
 
 def run_transport(name, torch, lds, reps=10, warm=3):

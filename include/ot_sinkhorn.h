@@ -34,10 +34,12 @@
  *    invalid call returns OT_ERROR_INVALID_VALUE and enqueues nothing.
  *  - Preconditions that are NOT checked (checking would need a device read):
  *    finite inputs, a_i > 0, b_j > 0, and for d >= 32 the range of the
- *    split-f16 matrix-core products, (2 log2(e)/eps) * max_ik |x_ik| *
- *    max_jk |y_jk| < 2^30 (with x and y replaced by their unit-normalised
- *    rows and eps by 2 eps in the cosine calls). Violations give NaN or inf
- *    results, not an error code.
+ *    split-f16 matrix-core products, (2 log2(e)/eps) * max_ik |x_ik - c_k| *
+ *    max_jk |y_jk - c_k| < 2^30, where c = (mean_i x_i + mean_j y_j) / 2 is
+ *    the centre the d >= 32 calls subtract from both clouds before forming
+ *    products (the cost does not change; x and y are replaced by their
+ *    unit-normalised rows and eps by 2 eps in the cosine calls). Violations
+ *    give NaN or inf results, not an error code.
  *  - Outputs must not alias inputs unless a call says otherwise.
  *  - Calls are stateless; concurrent calls on different streams are safe.
  *  - Graph capture: ot_sinkhorn_solve, ot_plan_stats, ot_transport_apply and
