@@ -20,10 +20,13 @@
 // f16 MFMA stream, an exp2 stream mostly), which fp32 MFMAs do not, so the
 // exp2/add epilogue of the log-sum-exp largely overlaps the products.
 //
-// f16 range. To keep hi and lo inside f16's range, the column side stores
-// (2 log2(e)/eps) q 2^-e and the row side p 2^e with one power of two e per
-// direction, chosen so that both sides' largest magnitudes meet near
-// T^(1/2), T = (2 log2(e)/eps) max|p| max|q|; the product is unchanged. With e
+// f16 range. The records hold the centred points p = x - c, q = y - c (c the
+// mean of the two cloud means; the cost does not change, and |p| |q| stays
+// near the size of the costs). To keep hi and lo inside f16's range, the
+// column side stores (2 log2(e)/eps) q 2^-e and the row side p 2^e with one
+// power of two e per direction, chosen so that both sides' largest magnitudes
+// meet near T^(1/2), T = (2 log2(e)/eps) max|p| max|q|; the product is
+// unchanged. With e
 // rounded to an integer one side's largest magnitude is at most (2T)^(1/2),
 // which stays below f16's largest finite value 65504 when T < 2^30 (near
 // 2^32 the hi parts become inf; fp32 scores would carry no fractional bits
