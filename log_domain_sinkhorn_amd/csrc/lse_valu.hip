@@ -110,8 +110,8 @@ hipError_t launch_prep_side(const float *pts, const float *pot, int64_t count, i
 // Epilogue shared by the one-pass kernel and the merge: from the final
 // (M, S) of row i write its fp64 bias slot and its potential.
 // --------------------------------------------------------------------------
-__device__ __forceinline__ void finish_row_f64(const HalfStep &h, int kp, int rs, int64_t i,
-                                               double M, float S, double nrm) {
+__device__ __forceinline__ void finish_row_f64(const HalfStep &h, int64_t i, double M, float S,
+                                               double nrm) {
     const double lse = M + (double)hw_log2(S);
     const double hat = log2((double)h.row_w[i]) - lse;
     static_cast<double *>(h.row_bias)[i * h.bias_stride + h.bias_off] = hat;
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(256) void lse_rows_valu_kernel(HalfStep h, int tile
         const int64_t i = row0 + tid + r * 256;
         if (i < h.rows) {
             if (nsplit == 1)
-                finish_row_f64(h, KP, RS, i, M[r], S[r], nrm[r]);
+                finish_row_f64(h, i, M[r], S[r], nrm[r]);
             else
                 h.partials[(int64_t)split * h.rows_pad + i] = Partial{M[r], S[r], 0.f};
         }
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(HalfStep h, int nsplit, 
         double q = 0.0;
         for (int k = 0; k < kp; ++k)
             q = fma(p[k], p[k], q);
-        finish_row_f64(h, kp, rs, i, M, S, q);
+        finish_row_f64(h, i, M, S, q);
     }
 }
 
