@@ -184,6 +184,24 @@ def test_split_f16_half_step_on_unit_gaussians(d, eps_factor, offset):
     assert ef <= TOL_SPLIT_HALF and eg <= TOL_SPLIT_HALF
 
 
+@pytest.mark.parametrize("d,eps", [(3, 1e-3), (64, 1e-3), (3, 1e4), (64, 1e4)])
+def test_extreme_eps_half_step(d, eps):
+    # The degenerate ends of the method: eps far below the costs (the plan is
+    # close to an assignment, the log-sum-exp is its max term) and far above
+    # them (the plan is close to the product a b^T). One f and one g half-step
+    # from the oracle's iterate, on both paths (fp64 VALU scores for d = 3,
+    # split-f16 matrix cores for d = 64).
+    c = random_clouds(700, 500, d, seed=int(d + 1e3 * eps) % 9973, spread=1.0 / np.sqrt(d))
+    fo, go = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, 5)
+    g32 = go.astype(np.float32)
+    f1, g1 = gpu_solve(c, eps, 1, g0=g32)
+    f_ref = oracle.half_update(c["x"], c["y"], c["a"], g32, eps)
+    g_ref = oracle.half_update(c["y"], c["x"], c["b"], f1, eps)
+    ef, eg = rel_inf(f1, f_ref), rel_inf(g1, g_ref)
+    print(f"d={d} eps={eps:g}: one half-step rel err f {ef:.2e} g {eg:.2e}", flush=True)
+    assert ef <= TOL_HALF and eg <= TOL_HALF
+
+
 def test_split_f16_long_solve_on_unit_gaussians():
     c = random_clouds(700, 900, 64, seed=3, spread=1.0)
     _check_solve(c, 0.25 * 8.0, 60, "d=64 N(0,I) 60 iterations")
