@@ -89,8 +89,8 @@ ot_status run_schedule_h3(const float *x, const float *y, const float *a, const 
                           int iters, float *f, float *g, hipStream_t s) {
     const int kp = h3_kp(d);
     const int64_t n_pad = pad_points(n), m_pad = pad_points(m);
-    size_t part = half_step_partials_h3(n, m_pad);
-    const size_t part2 = half_step_partials_h3(m, n_pad);
+    size_t part = half_step_partials_h3(n, m_pad, kp);
+    const size_t part2 = half_step_partials_h3(m, n_pad, kp);
     if (part2 > part)
         part = part2;
     const size_t xr = align_up((size_t)n_pad * 4 * kp, 256);
@@ -221,7 +221,7 @@ ot_status plan_stats_h3(const float *x, const float *y, const float *a, const fl
     const size_t xv = align_up((size_t)n_pad * sizeof(float), 256);
     const size_t yv = align_up((size_t)m_pad * sizeof(float), 256);
     const size_t mb = align_up(h3_maxabs_floats() * sizeof(float), 256);
-    const size_t db = plan_stats_h3_scratch_doubles(n, m, n_pad, m_pad) * sizeof(double);
+    const size_t db = plan_stats_h3_scratch_doubles(n, m, n_pad, m_pad, kp) * sizeof(double);
     const size_t cb = align_up(h3_center_scratch_bytes(d), 256);
     Scratch sc(s);
     hipError_t e = sc.alloc(2 * xr + 2 * yr + 2 * xv + 2 * yv + mb + db + cb);
@@ -447,7 +447,7 @@ ot_status ot_transport_apply(const float *x, const float *y, const float *f, con
     }
     if (st == OT_SUCCESS)
         st = check_supported(n, m, d);
-    if (st == OT_SUCCESS && dv > OT_MAX_VALUE_DIM)
+    if (st == OT_SUCCESS && (dv > OT_MAX_VALUE_DIM || d > OT_MAX_TRANSPORT_DIM))
         st = OT_ERROR_NOT_SUPPORTED;
     if (st != OT_SUCCESS)
         return st;
@@ -476,6 +476,8 @@ static ot_status map_or_grad(const float *x, const float *y, const float *a, con
     }
     if (st == OT_SUCCESS)
         st = check_supported(n, m, d);
+    if (st == OT_SUCCESS && d > OT_MAX_TRANSPORT_DIM)
+        st = OT_ERROR_NOT_SUPPORTED;
     if (st != OT_SUCCESS)
         return st;
     hipStream_t s = (hipStream_t)stream;

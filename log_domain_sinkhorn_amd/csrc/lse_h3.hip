@@ -58,10 +58,9 @@ using namespace mfma;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerBlock = 32 * kWaves;
-constexpr int kTileCols = 128;
-constexpr int kSub = kTileCols / 32;
-static_assert(kSub <= kWaves, "one wave copies each subtile's biases");
-constexpr int kBiasSlots = 2 * kTileCols;
+// Columns per LDS tile: 128 up to KP = 128; 64 above, so that the two tile
+// buffers (2 * TC * KP * 4 bytes) still fit the LDS with one workgroup per CU.
+__host__ __device__ constexpr int tile_cols(int kp) { return kp <= 128 ? 128 : 64; }
 constexpr int kTargetBlocks = 1024;
 
 template <int KP>
@@ -70,11 +69,15 @@ __global__ __launch_bounds__(kThreads) void lse_rows_h3_kernel(HalfStep h, int t
     int rblk, split;
     xcd_block(nrb, nsplit, rblk, split);
     constexpr int RC = KP / 4;
-    constexpr int TILE16 = kTileCols * RC;
+    constexpr int TC = tile_cols(KP);
+    constexpr int SUB = TC / 32;
+    constexpr int BS = 2 * TC;
+    constexpr int TILE16 = TC * RC;
     static_assert(KP % 32 == 0, "records are whole groups of 8 chunks");
     static_assert(TILE16 % 64 == 0, "tiles are whole 64-lane chunks");
+    static_assert(SUB <= kWaves, "one wave copies each subtile's biases");
     __shared__ float4 lrec[2][TILE16];
-    __shared__ float lbias[2][kBiasSlots];
+    __shared__ float lbias[2][BS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -86,12 +89,12 @@ __global__ __launch_bounds__(kThreads) void lse_rows_h3_kernel(HalfStep h, int t
     const float4 *col4 = static_cast<const float4 *>(h.col_rec);
     const float *colb = static_cast<const float *>(h.col_bias);
 
-    for (int k = tid; k < 2 * kBiasSlots; k += kThreads) {
-        const int e = k % kBiasSlots;
+    for (int k = tid; k < 2 * BS; k += kThreads) {
+        const int e = k % BS;
         if ((e / 32) & 1)
-            lbias[k / kBiasSlots][e] = 1.f;
+            lbias[k / BS][e] = 1.f;
     }
-    issue_tile<TILE16, kWaves, kSub>(col4, colb, tbeg, lrec[0], lbias[0], wave, lane);
+    issue_tile<TILE16, kWaves, SUB>(col4, colb, tbeg, lrec[0], lbias[0], wave, lane);
     // Stationary B operands: this lane's k-halves of its row's hi and lo parts.
     const int64_t i = (int64_t)rblk * kRowsPerBlock + wave * 32 + li;
     const int64_t ic = i < h.rows ? i : h.rows - 1;
@@ -116,10 +119,10 @@ __global__ __launch_bounds__(kThreads) void lse_rows_h3_kernel(HalfStep h, int t
     auto tile = [&](int t, auto bc) {
         constexpr int b = decltype(bc)::value;
         if (t + 1 < tend)
-            issue_tile<TILE16, kWaves, kSub>(col4, colb, t + 1, lrec[b ^ 1], lbias[b ^ 1], wave,
+            issue_tile<TILE16, kWaves, SUB>(col4, colb, t + 1, lrec[b ^ 1], lbias[b ^ 1], wave,
                                              lane);
 #pragma unroll
-        for (int sub = 1; sub < kSub; ++sub) {
+        for (int sub = 1; sub < SUB; ++sub) {
             const float Mu_cur = M;
             const floatx16 acc_cur = score_h3<KP>(lrec[b], lbias[b], sub, lane, li, hl, bh, bl,
                                                   Mu_cur);
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(256) void center_partial_kernel(const float *__rest
     }
 }
 
-__global__ __launch_bounds__(128) void center_final_kernel(const double *__restrict__ part, int nb,
+__global__ __launch_bounds__(256) void center_final_kernel(const double *__restrict__ part, int nb,
                                                            int d, int64_t n, int64_t m,
                                                            float *__restrict__ center) {
     const int k = threadIdx.x;
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(256) void prep_h3_kernel(
 // log2 P_ij = (2 log2(e)/eps) p_i.q_j + qhat_j + phat_i from the split-f16
 // chain plus one fp32 MFMA (k-slot 0: qhat_j x 1, k-slot 1: 1 x phat_i), and
 // C_ij = |p_i|^2 + |q_j|^2 - 2 p_i.q_j from the chain's dot product before the
-// bias. Sums are fp32 within a tile of 128 columns and fp64 across tiles; the
+// bias. Sums are fp32 within a column tile and fp64 across tiles; the
 // two lane halves (disjoint columns of one row) are added at the end.
 // ---------------------------------------------------------------------------
 template <int KP, bool COST>
@@ -357,10 +360,14 @@ __global__ __launch_bounds__(kThreads) void plan_rows_h3_kernel(
     int64_t rows_pad, int tiles_per_split, int ntiles, float inv_scale,
     double2 *__restrict__ part) {
     constexpr int RC = KP / 4;
-    constexpr int TILE16 = kTileCols * RC;
+    constexpr int TC = tile_cols(KP);
+    constexpr int SUB = TC / 32;
+    constexpr int BS = 2 * TC;
+    constexpr int TILE16 = TC * RC;
+    static_assert(SUB <= kWaves, "one wave copies each subtile's biases");
     __shared__ float4 lrec[2][TILE16];
-    __shared__ float lbias[2][kBiasSlots];
-    __shared__ __attribute__((aligned(16))) float lnrm[2][kTileCols];
+    __shared__ float lbias[2][BS];
+    __shared__ __attribute__((aligned(16))) float lnrm[2][TC];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -371,18 +378,18 @@ __global__ __launch_bounds__(kThreads) void plan_rows_h3_kernel(
     const int tbeg = split * tiles_per_split;
     const int tend = min(tbeg + tiles_per_split, ntiles);
 
-    for (int k = tid; k < 2 * kBiasSlots; k += kThreads) {
-        const int e = k % kBiasSlots;
+    for (int k = tid; k < 2 * BS; k += kThreads) {
+        const int e = k % BS;
         if ((e / 32) & 1)
-            lbias[k / kBiasSlots][e] = 1.f;
+            lbias[k / BS][e] = 1.f;
     }
     // Column norms of a tile: waves 0 and 1, one dword per lane.
     auto issue_norms = [&](int t, float *dst) {
-        if (COST && wave < kTileCols / 64)
-            __builtin_amdgcn_global_load_lds(col_nrm + (int64_t)t * kTileCols + wave * 64 + lane,
+        if (COST && wave < TC / 64)
+            __builtin_amdgcn_global_load_lds(col_nrm + (int64_t)t * TC + wave * 64 + lane,
                                              (lds_void *)(dst + wave * 64), 4, 0, 0);
     };
-    issue_tile<TILE16, kWaves, kSub>(col4, colb, tbeg, lrec[0], lbias[0], wave, lane);
+    issue_tile<TILE16, kWaves, SUB>(col4, colb, tbeg, lrec[0], lbias[0], wave, lane);
     issue_norms(tbeg, lnrm[0]);
     const int64_t i = (int64_t)blockIdx.x * kRowsPerBlock + wave * 32 + li;
     const int64_t ic = i < rows ? i : rows - 1;
@@ -406,30 +413,18 @@ __global__ __launch_bounds__(kThreads) void plan_rows_h3_kernel(
     for (int t = tbeg; t < tend; ++t) {
         const int b = (t - tbeg) & 1;
         if (t + 1 < tend) {
-            issue_tile<TILE16, kWaves, kSub>(col4, colb, t + 1, lrec[b ^ 1], lbias[b ^ 1], wave,
+            issue_tile<TILE16, kWaves, SUB>(col4, colb, t + 1, lrec[b ^ 1], lbias[b ^ 1], wave,
                                              lane);
             issue_norms(t + 1, lnrm[b ^ 1]);
         }
         float rs = 0.f, cs = 0.f;
 #pragma unroll
-        for (int sub = 0; sub < kSub; ++sub) {
+        for (int sub = 0; sub < SUB; ++sub) {
             constexpr int SW = swizzle_mask(RC);
             const int j = sub * 32 + li;
             const float4 *ap = lrec[b] + j * RC;
             const int sw = j & SW;
-            floatx16 dot = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
-                            0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            half8 qh[KP / 16];
-#pragma unroll
-            for (int c = 0; c < KP / 16; ++c) {
-                qh[c] = as_half8(ap[(2 * c + hl) ^ sw]);
-                const half8 ql = as_half8(ap[(KP / 8 + 2 * c + hl) ^ sw]);
-                dot = __builtin_amdgcn_mfma_f32_32x32x16_f16(ql, bh[c], dot, 0, 0, 0);
-                dot = __builtin_amdgcn_mfma_f32_32x32x16_f16(qh[c], bl[c], dot, 0, 0, 0);
-            }
-#pragma unroll
-            for (int c = 0; c < KP / 16; ++c)
-                dot = __builtin_amdgcn_mfma_f32_32x32x16_f16(qh[c], bh[c], dot, 0, 0, 0);
+            const floatx16 dot = split_dot<KP>(ap, sw, hl, bh, bl);
             const float a0 = lbias[b][sub * 64 + lane];
             const float b0 = hl ? -Mu : 1.f;
             const floatx16 u = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, dot, 0, 0, 0);
@@ -468,9 +463,9 @@ struct H3Plan {
     int64_t row_blocks;
 };
 
-H3Plan plan_h3(int64_t rows, int64_t cols_pad) {
+H3Plan plan_h3(int64_t rows, int64_t cols_pad, int kp) {
     H3Plan p;
-    p.ntiles = (int)(cols_pad / kTileCols);
+    p.ntiles = (int)(cols_pad / tile_cols(kp));
     p.row_blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
     int64_t want = (kTargetBlocks + p.row_blocks - 1) / p.row_blocks;
     if (want > p.ntiles)
@@ -507,7 +502,7 @@ size_t h3_center_scratch_bytes(int d) {
 
 hipError_t launch_center_maxabs(const float *x, int64_t n, const float *y, int64_t m, int d,
                                 void *center_scratch, float *scratch, hipStream_t s) {
-    if (d < 1 || d > 128)
+    if (d < 1 || d > 192)
         return hipErrorInvalidValue;
     double *part = static_cast<double *>(center_scratch);
     float *center = reinterpret_cast<float *>(part + (size_t)2 * kCenterBlocks * d);
@@ -516,7 +511,7 @@ hipError_t launch_center_maxabs(const float *x, int64_t n, const float *y, int64
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(center_final_kernel, dim3(1), dim3(128), 0, s, part, kCenterBlocks, d, n, m,
+    hipLaunchKernelGGL(center_final_kernel, dim3(1), dim3(256), 0, s, part, kCenterBlocks, d, n, m,
                        center);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
@@ -542,13 +537,15 @@ hipError_t launch_prep_h3(const float *pts, const float *pot, int64_t count, int
     return hipGetLastError();
 }
 
-int plan_pass_h3_splits(int64_t rows, int64_t cols_pad) { return plan_h3(rows, cols_pad).nsplit; }
+int plan_pass_h3_splits(int64_t rows, int64_t cols_pad, int kp) {
+    return plan_h3(rows, cols_pad, kp).nsplit;
+}
 
 hipError_t launch_plan_pass_h3(int kp, bool cost, const void *row_rec, const float *row_hat,
                                const float *row_nrm, const void *col_rec, const float *col_hat,
                                const float *col_nrm, int64_t rows, int64_t rows_pad,
                                int64_t cols_pad, double scale, double2 *part, hipStream_t s) {
-    const H3Plan p = plan_h3(rows, cols_pad);
+    const H3Plan p = plan_h3(rows, cols_pad, kp);
     dim3 grid((unsigned)p.row_blocks, (unsigned)p.nsplit);
     const float4 *rr = static_cast<const float4 *>(row_rec);
     const float4 *cr = static_cast<const float4 *>(col_rec);
@@ -569,6 +566,8 @@ hipError_t launch_plan_pass_h3(int kp, bool cost, const void *row_rec, const flo
         OTSK_PR(64)
         OTSK_PR(96)
         OTSK_PR(128)
+        OTSK_PR(160)
+        OTSK_PR(192)
     default:
         return hipErrorInvalidValue;
     }
@@ -576,19 +575,21 @@ hipError_t launch_plan_pass_h3(int kp, bool cost, const void *row_rec, const flo
     return hipGetLastError();
 }
 
-size_t half_step_partials_h3(int64_t rows, int64_t cols_pad) {
-    const H3Plan p = plan_h3(rows, cols_pad);
+size_t half_step_partials_h3(int64_t rows, int64_t cols_pad, int kp) {
+    const H3Plan p = plan_h3(rows, cols_pad, kp);
     return p.nsplit > 1 ? (size_t)p.nsplit * (size_t)pad_points(rows) : 0;
 }
 
 hipError_t launch_half_step_h3(const HalfStep &h, int kp, hipStream_t s) {
-    const H3Plan p = plan_h3(h.rows, h.cols_pad);
+    const H3Plan p = plan_h3(h.rows, h.cols_pad, kp);
     hipError_t e;
     switch (kp) {
     case 32: e = launch_h3_kp<32>(h, p, s); break;
     case 64: e = launch_h3_kp<64>(h, p, s); break;
     case 96: e = launch_h3_kp<96>(h, p, s); break;
     case 128: e = launch_h3_kp<128>(h, p, s); break;
+    case 160: e = launch_h3_kp<160>(h, p, s); break;
+    case 192: e = launch_h3_kp<192>(h, p, s); break;
     default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess || p.nsplit <= 1)

@@ -53,36 +53,64 @@ __host__ __device__ constexpr int swizzle_mask(int rc) { return rc % 16 == 0 ? 1
 
 __device__ __forceinline__ half8 as_half8(float4 v) { return __builtin_bit_cast(half8, v); }
 
-// u[j][i] = s_ij - Mu_i for subtile `sub` of the tile in `rec` / `bias`.
+// The chain alone: D[j][i] = p_i.q_j (scaled) for the column record ap of
+// column j (swizzle sw) against the stationary row operands bh, bl.
 //
 // Order of the chain. The f16 MFMA adds its 16 products and the accumulator
 // in one aligned sum whose error is about 2^-21 of the largest term
 // (measured on gfx950; a lone product is exact), so the accumulator should be
 // small while the products go in: first the lo corrections (2^-11 of the
-// rest), then the hi x hi products onto them, and the bias and -M last,
-// through the fp32 MFMA, whose sum is rounded like fp32 arithmetic.
+// rest), then the hi x hi products onto them, and the bias and -M last (in
+// score_h3), through the fp32 MFMA, whose sum is rounded like fp32
+// arithmetic.
+template <int KP>
+__device__ __forceinline__ floatx16 split_dot(const float4 *ap, int sw, int hl,
+                                              const half8 (&bh)[KP / 16],
+                                              const half8 (&bl)[KP / 16]) {
+    floatx16 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
+                    0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if constexpr (KP <= 128) {
+        half8 qh[KP / 16];
+#pragma unroll
+        for (int c = 0; c < KP / 16; ++c) {
+            qh[c] = as_half8(ap[(2 * c + hl) ^ sw]);
+            const half8 ql = as_half8(ap[(KP / 8 + 2 * c + hl) ^ sw]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ql, bh[c], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qh[c], bl[c], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int c = 0; c < KP / 16; ++c)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qh[c], bh[c], acc, 0, 0, 0);
+    } else {
+        // Above KP = 128 the hi operands are read from LDS a second time for
+        // the hi x hi products instead of being held: KP/4 more registers do
+        // not fit beside the stationary row operands (KP/2 registers). Up to
+        // KP = 192 the kernels then compile without register spills; at 224
+        // and 256 they would spill, so the point-cloud calls stop at 192.
+#pragma unroll
+        for (int c = 0; c < KP / 16; ++c) {
+            const half8 ql = as_half8(ap[(KP / 8 + 2 * c + hl) ^ sw]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ql, bh[c], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(ap[(2 * c + hl) ^ sw]), bl[c],
+                                                         acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int c = 0; c < KP / 16; ++c)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_half8(ap[(2 * c + hl) ^ sw]), bh[c],
+                                                         acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// u[j][i] = s_ij - Mu_i for subtile `sub` of the tile in `rec` / `bias`.
 template <int KP>
 __device__ __forceinline__ floatx16 score_h3(const float4 *rec, const float *bias, int sub,
                                              int lane, int li, int hl, const half8 (&bh)[KP / 16],
                                              const half8 (&bl)[KP / 16], float Mu) {
     constexpr int RC = KP / 4;
     constexpr int SW = swizzle_mask(RC);
-    floatx16 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
-                    0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const int j = sub * 32 + li;
-    const float4 *ap = rec + j * RC;
-    const int sw = j & SW;
-    half8 qh[KP / 16];
-#pragma unroll
-    for (int c = 0; c < KP / 16; ++c) {
-        qh[c] = as_half8(ap[(2 * c + hl) ^ sw]);
-        const half8 ql = as_half8(ap[(KP / 8 + 2 * c + hl) ^ sw]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ql, bh[c], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qh[c], bl[c], acc, 0, 0, 0);
-    }
-#pragma unroll
-    for (int c = 0; c < KP / 16; ++c)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qh[c], bh[c], acc, 0, 0, 0);
+    const floatx16 acc = split_dot<KP>(rec + j * RC, j & SW, hl, bh, bl);
     const float a0 = bias[sub * 64 + lane];
     const float b0 = hl ? -Mu : 1.f;
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc, 0, 0, 0);

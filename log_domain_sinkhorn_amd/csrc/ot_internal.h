@@ -131,17 +131,18 @@ hipError_t launch_prep_h3(const float *pts, const float *pot, int64_t count, int
                           int kp, double scale, double hat_scale, int bias_mode,
                           const float *maxabs, const void *center_scratch, int own, void *colrec,
                           void *rowrec, float *nrm, float *bias, hipStream_t s);
-size_t half_step_partials_h3(int64_t rows, int64_t cols_pad);
+size_t half_step_partials_h3(int64_t rows, int64_t cols_pad, int kp);
 // One plan-statistics pass on split-f16 records (hat biases of the
 // potentials): part[split][row] = (sum_j P_ij, cost ? sum_j P_ij C_ij : 0).
-int plan_pass_h3_splits(int64_t rows, int64_t cols_pad);
+int plan_pass_h3_splits(int64_t rows, int64_t cols_pad, int kp);
 hipError_t launch_plan_pass_h3(int kp, bool cost, const void *row_rec, const float *row_hat,
                                const float *row_nrm, const void *col_rec, const float *col_hat,
                                const float *col_nrm, int64_t rows, int64_t rows_pad,
                                int64_t cols_pad, double scale, double2 *part, hipStream_t s);
 // Reductions of the two passes' partials into cost and marginal errors
 // (scratch of plan_stats_h3_scratch_doubles doubles).
-size_t plan_stats_h3_scratch_doubles(int64_t n, int64_t m, int64_t n_pad, int64_t m_pad);
+size_t plan_stats_h3_scratch_doubles(int64_t n, int64_t m, int64_t n_pad, int64_t m_pad,
+                                     int kp);
 hipError_t launch_plan_stats_h3(int kp, const void *xrow, const void *xcol, const float *xhat,
                                 const float *xnrm, const void *yrow, const void *ycol,
                                 const float *yhat, const float *ynrm, const float *a,

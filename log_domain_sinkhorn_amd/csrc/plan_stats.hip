@@ -399,10 +399,11 @@ hipError_t launch_plan_stats(const float *x_rec, const float *y_rec, const float
     return hipGetLastError();
 }
 
-size_t plan_stats_h3_scratch_doubles(int64_t n, int64_t m, int64_t n_pad, int64_t m_pad) {
+size_t plan_stats_h3_scratch_doubles(int64_t n, int64_t m, int64_t n_pad, int64_t m_pad,
+                                     int kp) {
     size_t d = 0;
-    d += 2 * (size_t)plan_pass_h3_splits(n, m_pad) * (size_t)n_pad;  // row partials
-    d += 2 * (size_t)plan_pass_h3_splits(m, n_pad) * (size_t)m_pad;  // column partials
+    d += 2 * (size_t)plan_pass_h3_splits(n, m_pad, kp) * (size_t)n_pad;  // row partials
+    d += 2 * (size_t)plan_pass_h3_splits(m, n_pad, kp) * (size_t)m_pad;  // column partials
     d += 2 * 2 * (size_t)kReduceBlocks;
     return d;
 }
@@ -417,15 +418,15 @@ hipError_t launch_plan_stats_h3(int kp, const void *xrow, const void *xcol, cons
                                 double *scratch, hipStream_t s) {
     hipError_t e;
     double2 *prow = reinterpret_cast<double2 *>(scratch);
-    double2 *pcol = prow + (size_t)plan_pass_h3_splits(n, m_pad) * n_pad;
-    double2 *brow = pcol + (size_t)plan_pass_h3_splits(m, n_pad) * m_pad;
+    double2 *pcol = prow + (size_t)plan_pass_h3_splits(n, m_pad, kp) * n_pad;
+    double2 *brow = pcol + (size_t)plan_pass_h3_splits(m, n_pad, kp) * m_pad;
     double2 *bcol = brow + kReduceBlocks;
     if ((e = launch_plan_pass_h3(kp, true, xrow, xhat, xnrm, ycol, yhat, ynrm, n, n_pad, m_pad,
                                  scale, prow, s)) != hipSuccess)
         return e;
     const int nrb = reduce_blocks(n);
     hipLaunchKernelGGL(reduce_rows_kernel, dim3(nrb), dim3(256), 0, s, prow,
-                       plan_pass_h3_splits(n, m_pad), n, n_pad, marg ? a : nullptr, brow);
+                       plan_pass_h3_splits(n, m_pad, kp), n, n_pad, marg ? a : nullptr, brow);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     int ncb = 0;
@@ -435,7 +436,7 @@ hipError_t launch_plan_stats_h3(int kp, const void *xrow, const void *xcol, cons
             return e;
         ncb = reduce_blocks(m);
         hipLaunchKernelGGL(reduce_rows_kernel, dim3(ncb), dim3(256), 0, s, pcol,
-                           plan_pass_h3_splits(m, n_pad), m, m_pad, b, bcol);
+                           plan_pass_h3_splits(m, n_pad, kp), m, m_pad, b, bcol);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
     }

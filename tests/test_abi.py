@@ -40,6 +40,7 @@ def test_every_declared_function_is_exported(lib):
 def test_header_max_dim_matches_binding():
     text = open(lds._HEADER).read()
     assert f"#define OT_MAX_DIM {lds.OT_MAX_DIM}" in text
+    assert f"#define OT_MAX_TRANSPORT_DIM {lds.OT_MAX_TRANSPORT_DIM}" in text
     assert f"#define OT_MAX_VALUE_DIM {lds.OT_MAX_VALUE_DIM}" in text
 
 
@@ -80,7 +81,7 @@ def test_eps_scaling_rejects_invalid(lib):
     assert f(X, Y, A, B, 10, 12, 3, 1.0, 0.0, 8, 5, F, G, None) == INVALID    # eps_end
     assert f(X, Y, A, B, 10, 12, 3, math.nan, 0.1, 8, 5, F, G, None) == INVALID
     assert f(X, Y, A, B, 10, 12, 3, 1.0, 0.1, 8, -1, F, G, None) == INVALID
-    assert f(X, Y, A, B, 10, 12, 129, 1.0, 0.1, 8, 5, F, G, None) == UNSUPPORTED
+    assert f(X, Y, A, B, 10, 12, lds.OT_MAX_DIM + 1, 1.0, 0.1, 8, 5, F, G, None) == UNSUPPORTED
 
 
 def test_plan_stats_rejects_invalid(lib):
@@ -112,6 +113,7 @@ def test_transport_apply_rejects_invalid(lib):
                dict(out=X), dict(out=V + 8), dict(out=F - 16)]:
         assert call(**kw) == INVALID, kw
     assert call(d=lds.OT_MAX_DIM + 1) == UNSUPPORTED
+    assert call(d=lds.OT_MAX_TRANSPORT_DIM + 1) == UNSUPPORTED
     assert call(dv=lds.OT_MAX_VALUE_DIM + 1) == UNSUPPORTED
     assert call(dv=lds.OT_MAX_VALUE_DIM + 1, eps=-1.0) == INVALID
 
@@ -178,7 +180,7 @@ def test_cosine_entries_reject_invalid(lib):
     assert sc(X, Y, A, B, 10, 12, 3, 0.0, 5, F, G, None) == INVALID
     assert sc(X, Y, A, B, 10, 12, 3, 0.1, -1, F, G, None) == INVALID
     assert sc(X, Y, A, B, 10, 12, 3, 0.1, 5, A, G, None) == INVALID    # f aliases a
-    assert sc(X, Y, A, B, 10, 12, 129, 0.1, 5, F, G, None) == UNSUPPORTED
+    assert sc(X, Y, A, B, 10, 12, lds.OT_MAX_DIM + 1, 0.1, 5, F, G, None) == UNSUPPORTED
     assert sc(X, Y, A, B, 10, 12, 3, 3e38, 5, F, G, None) == UNSUPPORTED  # 2 eps overflows
     assert sc(X, Y, A, B, 10, 12, 3, 0.1, 0, F, G, None) == 0           # host no-op
     assert pc(X, Y, A, B, F, G, 10, 12, 3, 0.1, None, None, None) == INVALID

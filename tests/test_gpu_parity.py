@@ -95,6 +95,8 @@ SHAPES = [
     (300, 200, 2), (2000, 1500, 5), (5000, 300, 3), (300, 5000, 3), (256, 256, 31),
     (256, 256, 32), (256, 256, 33), (512, 384, 64), (200, 300, 128), (257, 1000, 48),
     (1, 97, 64), (97, 1, 64), (1, 1, 40), (129, 700, 96),
+    # above 128 coordinates: 64-column tiles, hi operands read twice
+    (129, 700, 129), (300, 257, 160), (257, 300, 192), (1, 97, 192), (97, 1, 160),
 ]
 
 
@@ -106,7 +108,7 @@ def test_shapes(n, m, d):
 
 
 STATS_SHAPES = [(1, 300, 64), (300, 1, 64), (129, 257, 33), (600, 200, 96), (257, 300, 128),
-                (1, 1, 40), (300, 500, 31)]
+                (1, 1, 40), (300, 500, 31), (129, 257, 150), (300, 200, 192)]
 
 
 @pytest.mark.parametrize("n,m,d", STATS_SHAPES)
@@ -163,7 +165,9 @@ TOL_SPLIT_HALF = TOL_HALF
 
 @pytest.mark.parametrize("d,eps_factor,offset", [(32, 0.5, 0.0), (64, 0.5, 0.0), (64, 0.1, 0.0),
                                                  (128, 0.1, 0.0), (96, 1.0, 0.0),
-                                                 (64, 0.5, 30.0), (32, 0.1, -50.0)])
+                                                 (64, 0.5, 30.0), (32, 0.1, -50.0),
+                                                 (160, 0.5, 0.0), (192, 0.1, 0.0),
+                                                 (192, 0.5, 40.0)])
 def test_split_f16_half_step_on_unit_gaussians(d, eps_factor, offset):
     # offset != 0: both clouds moved far from the origin. The records hold
     # x - c and y - c (c the mean of the two cloud means; the cost does not
