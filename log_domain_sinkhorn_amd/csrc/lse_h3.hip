@@ -43,8 +43,8 @@
 // Workgroups of 8 waves own 256 rows and stream 128-column tiles (64 above
 // KP = 128, see tile_cols) through double-buffered LDS with gfx950's direct
 // global->LDS loads; the running maximum is shared lazily by the two lane
-// halves of a row and moved only when
-// a chunk sum leaves [2^-64, 2^16] (the epilogue in mfma_common.h).
+// halves of a row and moved only when a chunk sum leaves [2^-64, 2^16] (the
+// epilogue in mfma_common.h).
 #include "mfma_common.h"
 
 #include <math.h>
