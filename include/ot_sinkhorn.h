@@ -67,15 +67,10 @@ typedef enum {
     OT_ERROR_LAUNCH_FAILURE = 4  /* a HIP call or kernel launch reported an error */
 } ot_status;
 
-/* Largest feature dimension d the point-cloud calls accept: the solve, the
- * plan statistics and the cosine calls (the matrix-core kernels keep a row's
- * split coordinates in registers; above this size they would spill). */
+/* Largest feature dimension d the point-cloud calls accept (the matrix-core
+ * kernels keep a row's split coordinates in registers; above this size they
+ * would spill). */
 #define OT_MAX_DIM 192
-
-/* Largest feature dimension d of the transport calls (ot_transport_apply,
- * ot_barycentric_map, ot_cost_gradient_x): they also hold value operands in
- * registers, which leaves room for fewer coordinates. */
-#define OT_MAX_TRANSPORT_DIM 128
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *ot_status_string(ot_status s);
@@ -166,8 +161,8 @@ ot_status ot_marginal_error(const float *x, const float *y, const float *a,
  * Other arguments as ot_plan_stats. Terms of P are formed in fp64 and
  * exponentiated in fp32; sums over j are fp64 in a fixed order.
  * Errors: INVALID_VALUE (null pointer, sizes < 1, bad eps, overlap),
- * NOT_SUPPORTED (d > OT_MAX_TRANSPORT_DIM, dv > OT_MAX_VALUE_DIM),
- * OUT_OF_MEMORY, LAUNCH_FAILURE.
+ * NOT_SUPPORTED (d > OT_MAX_DIM, dv > OT_MAX_VALUE_DIM), OUT_OF_MEMORY,
+ * LAUNCH_FAILURE.
  */
 ot_status ot_transport_apply(const float *x, const float *y, const float *f,
                              const float *g, int64_t n, int64_t m, int32_t d,
@@ -177,8 +172,7 @@ ot_status ot_transport_apply(const float *x, const float *y, const float *f,
 /*
  * ot_barycentric_map -- out_i = sum_j P_ij y_j / a_i (n*d): the barycentric
  * projection of each source point under the plan (page "FlashSinkhorn ...",
- * "Methodik" section 3). a [n] are the source weights (> 0). Errors as
- * ot_transport_apply (d > OT_MAX_TRANSPORT_DIM is NOT_SUPPORTED).
+ * "Methodik" section 3). a [n] are the source weights (> 0).
  */
 ot_status ot_barycentric_map(const float *x, const float *y, const float *a,
                              const float *f, const float *g, int64_t n,
@@ -190,8 +184,7 @@ ot_status ot_barycentric_map(const float *x, const float *y, const float *a,
  * sum_ij P_ij C_ij with respect to x_i at the fixed plan of (f, g); at the
  * optimal potentials this is the gradient of the entropic OT cost with
  * respect to the source points (envelope theorem; page "FlashSinkhorn ...",
- * "Methodik" section 3, gradients as weighted averages). Errors as
- * ot_transport_apply (d > OT_MAX_TRANSPORT_DIM is NOT_SUPPORTED).
+ * "Methodik" section 3, gradients as weighted averages).
  */
 ot_status ot_cost_gradient_x(const float *x, const float *y, const float *f,
                              const float *g, int64_t n, int64_t m, int32_t d,

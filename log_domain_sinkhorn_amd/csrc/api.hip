@@ -381,7 +381,7 @@ static ot_status transport_apply_impl(const float *x, const float *y, const floa
         const size_t xv = align_up((size_t)n_pad * sizeof(float), 256);
         const size_t yv = align_up((size_t)m_pad * sizeof(float), 256);
         const size_t mb = align_up(h3_maxabs_floats() * sizeof(float), 256);
-        const size_t pd = transport_mfma_scratch_doubles(n, m_pad, dv, rowsum != nullptr);
+        const size_t pd = transport_mfma_scratch_doubles(n, m_pad, dv, rowsum != nullptr, kp);
         const size_t cb = align_up(h3_center_scratch_bytes(d), 256);
         Scratch sc(s);
         if ((e = sc.alloc(2 * xr + 2 * yr + 2 * xv + 2 * yv + mb + cb +
@@ -447,7 +447,7 @@ ot_status ot_transport_apply(const float *x, const float *y, const float *f, con
     }
     if (st == OT_SUCCESS)
         st = check_supported(n, m, d);
-    if (st == OT_SUCCESS && (dv > OT_MAX_VALUE_DIM || d > OT_MAX_TRANSPORT_DIM))
+    if (st == OT_SUCCESS && dv > OT_MAX_VALUE_DIM)
         st = OT_ERROR_NOT_SUPPORTED;
     if (st != OT_SUCCESS)
         return st;
@@ -476,8 +476,6 @@ static ot_status map_or_grad(const float *x, const float *y, const float *a, con
     }
     if (st == OT_SUCCESS)
         st = check_supported(n, m, d);
-    if (st == OT_SUCCESS && d > OT_MAX_TRANSPORT_DIM)
-        st = OT_ERROR_NOT_SUPPORTED;
     if (st != OT_SUCCESS)
         return st;
     hipStream_t s = (hipStream_t)stream;

@@ -105,7 +105,8 @@ hipError_t launch_transport_apply(const Layout &L, const void *xrec, const void 
 // biases of f and g): x's row records and y's column records; rowsum
 // (nullable) also receives r_i = sum_j P_ij, with rowsum = true in the
 // scratch size.
-size_t transport_mfma_scratch_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum);
+size_t transport_mfma_scratch_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum,
+                                      int kp);
 hipError_t launch_transport_apply_mfma(int kp, const void *xrow, const float *xhat,
                                        const void *ycol, const float *yhat, const float *v,
                                        int64_t n, int64_t n_pad, int64_t m, int64_t m_pad, int dv,

@@ -318,7 +318,10 @@ MPlan plan_tm(int64_t rows, int64_t cols_pad) {
     return p;
 }
 
-int value_blocks(int dv) { return dv <= 32 ? 1 : 2; }
+// Value channels per pass: 64 (two 32-channel blocks) when there are more
+// than 32, except above KP = 128, where the second block's accumulators and
+// operands do not fit beside the row operands.
+int value_blocks(int dv, int kp) { return dv <= 32 || kp > 128 ? 1 : 2; }
 
 template <int KP, int NVB>
 hipError_t launch_tm(const float4 *xrec, const float *xbias, const float4 *col4, const float *colb,
@@ -351,31 +354,40 @@ hipError_t launch_tm_kp(int kp, const float4 *xrec, const float *xbias, const fl
         OTSK_TM(96)
         OTSK_TM(128)
     default:
-        return hipErrorInvalidValue;
+        break;
     }
+    if constexpr (NVB == 1) {
+        switch (kp) {
+            OTSK_TM(160)
+            OTSK_TM(192)
+        default:
+            break;
+        }
+    }
+    return hipErrorInvalidValue;
 #undef OTSK_TM
 }
 
 // Doubles of scratch ahead of the staged values (partials and row sums),
 // rounded to a 256-byte boundary.
-size_t partial_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum) {
+size_t partial_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum, int kp) {
     const MPlan p = plan_tm(n, m_pad);
-    const size_t per_row = (size_t)(32 * value_blocks(dv)) + (rowsum ? 1 : 0);
+    const size_t per_row = (size_t)(32 * value_blocks(dv, kp)) + (rowsum ? 1 : 0);
     const size_t d = (size_t)p.nsplit * (size_t)pad_points(n) * per_row;
     return (d + 31) / 32 * 32;
 }
 
-int padded_channels(int dv) {
-    const int vc = 32 * value_blocks(dv);
+int padded_channels(int dv, int kp) {
+    const int vc = 32 * value_blocks(dv, kp);
     return (dv + vc - 1) / vc * vc;
 }
 
 }  // namespace
 
-size_t transport_mfma_scratch_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum) {
-    const size_t vt_bytes = (size_t)(m_pad / kTileCols) * 3 * (size_t)padded_channels(dv) *
+size_t transport_mfma_scratch_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum, int kp) {
+    const size_t vt_bytes = (size_t)(m_pad / kTileCols) * 3 * (size_t)padded_channels(dv, kp) *
                             kVRow * sizeof(__bf16);
-    return partial_doubles(n, m_pad, dv, rowsum) + (vt_bytes + 7) / 8;
+    return partial_doubles(n, m_pad, dv, rowsum, kp) + (vt_bytes + 7) / 8;
 }
 
 hipError_t launch_transport_apply_mfma(int kp, const void *xrow, const float *xhat,
@@ -383,14 +395,15 @@ hipError_t launch_transport_apply_mfma(int kp, const void *xrow, const float *xh
                                        int64_t n, int64_t n_pad, int64_t m, int64_t m_pad, int dv,
                                        double *part, float *out, float *rowsum, hipStream_t s) {
     const MPlan p = plan_tm(n, m_pad);
-    const int nvb = value_blocks(dv);
+    const int nvb = value_blocks(dv, kp);
     const int vc = 32 * nvb;
-    const int dv_pad = padded_channels(dv);
+    const int dv_pad = padded_channels(dv, kp);
     const float4 *xr = static_cast<const float4 *>(xrow);
     const float4 *col4 = static_cast<const float4 *>(ycol);
     // Row-sum partials follow the value partials; the staged values follow both.
     double *rpart = rowsum ? part + (size_t)p.nsplit * (size_t)n_pad * (size_t)vc : nullptr;
-    __bf16 *vt = reinterpret_cast<__bf16 *>(part + partial_doubles(n, m_pad, dv, rowsum != nullptr));
+    __bf16 *vt =
+        reinterpret_cast<__bf16 *>(part + partial_doubles(n, m_pad, dv, rowsum != nullptr, kp));
     {
         const int64_t total = (int64_t)p.ntiles * dv_pad * kVRow;
         hipLaunchKernelGGL(values_bf16x3_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),

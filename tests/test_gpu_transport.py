@@ -109,6 +109,9 @@ def test_reduced_workload_apply_map_grad(name, n, m, iters):
     (1, 1, 3), (1, 700, 3), (700, 1, 3), (333, 517, 5), (257, 255, 17), (300, 600, 31),
     (300, 600, 32), (257, 513, 33), (400, 350, 48), (1, 900, 64), (900, 1, 64),
     (513, 1025, 64), (300, 700, 100), (260, 300, 128),
+    # above 128 coordinates: 64-column tiles, hi operands read twice, one
+    # 32-channel value block per pass
+    (300, 400, 160), (257, 300, 192), (1, 500, 192),
 ])
 def test_shapes(n, m, d):
     c = random_clouds(n, m, d, seed=n + m + d, spread=1.0 / np.sqrt(d))
@@ -144,7 +147,7 @@ def test_offset_clouds(d, offset):
     assert em <= TOL_APPLY
 
 
-@pytest.mark.parametrize("d,dv", [(3, 1024), (64, 1024), (64, 200), (3, 17)])
+@pytest.mark.parametrize("d,dv", [(3, 1024), (64, 1024), (64, 200), (3, 17), (192, 200)])
 def test_wide_values(d, dv):
     c = random_clouds(300, 400, d, seed=d + dv, spread=1.0 / np.sqrt(d))
     f, g = _oracle_potentials(c, 0.3, 5)
