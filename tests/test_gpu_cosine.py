@@ -55,6 +55,25 @@ def test_cosine_solve_and_stats(name, n, m, eps, iters):
     assert ec <= TOL_COST and em <= TOL_MARG
 
 
+@pytest.mark.parametrize("d", [160, 192])
+def test_cosine_high_dimension(d):
+    # Embedding-sized features: the normalised points go through the
+    # 64-column-tile kernels above 128 coordinates.
+    c = random_clouds(600, 800, d, seed=d, spread=1.0)
+    eps, iters = 0.02, 20
+    f, g = gpu_solve_cos(c, eps, iters)
+    fo, go = oracle.sinkhorn_cosine(c["x"], c["y"], c["a"], c["b"], eps, iters)
+    ef, eg = rel_inf(f, fo, eps), rel_inf(g, go, eps)
+    cost, marg = gpu_stats_cos(c, f, g, eps)
+    so = oracle.plan_stats_cosine(c["x"], c["y"], c["a"], c["b"], fo, go, eps)
+    ec = abs(cost - so["cost"]) / abs(so["cost"])
+    em = abs(marg.sum() - so["marg"])
+    print(f"d={d} cos eps {eps}: f {ef:.2e} g {eg:.2e}; cost rel {ec:.1e}; marg diff {em:.1e}",
+          flush=True)
+    assert ef <= TOL_POT and eg <= TOL_POT
+    assert ec <= TOL_COST and em <= TOL_MARG
+
+
 def test_cosine_scale_invariance_and_warm_start():
     c = random_clouds(500, 700, 16, seed=3)
     rng = np.random.default_rng(4)
