@@ -370,9 +370,19 @@ struct ValuPlan {
     int64_t row_blocks;
 };
 
+// Narrow tiles for small problems with one-record-chunk records (d <= 3).
+constexpr int kSmallTileCols = 64;
+
 ValuPlan plan_valu(const Layout &L, int64_t rows, int64_t cols_pad) {
     ValuPlan p;
     p.TJ = tile_cols_for(L.rs);
+    // When full-width tiles would leave fewer workgroups than CUs even at one
+    // row per lane, narrower tiles give more column splits (1024^2 at d = 3:
+    // 16 -> 10 us per half-step); larger problems keep the wide tiles, whose
+    // per-workgroup costs are lower (16384^2: 85 us, against 110 us with
+    // 64-column tiles). Such plans always end at one row per lane.
+    if (L.rs <= 4 && (rows + 255) / 256 * (cols_pad / p.TJ) < kCUs)
+        p.TJ = kSmallTileCols;
     p.ntiles = (int)(cols_pad / p.TJ);
     const int max_r = L.kp <= 3 ? 4 : (L.kp <= 15 ? 2 : 1);
     p.R = 1;
@@ -403,9 +413,10 @@ ValuPlan plan_valu(const Layout &L, int64_t rows, int64_t cols_pad) {
     return p;
 }
 
-template <int KP, int R>
+template <int KP, int R, int TJ = tile_cols_for(KP + 1)>
 hipError_t launch_kr(const HalfStep &h, const ValuPlan &p, hipStream_t s) {
-    constexpr int TJ = tile_cols_for(KP + 1);
+    if (p.TJ != TJ)
+        return hipErrorInvalidValue;
     dim3 grid((unsigned)(p.row_blocks * p.nsplit));
     hipLaunchKernelGGL((lse_rows_valu_kernel<KP, R, TJ>), grid, dim3(256), 0, s, h,
                        p.tiles_per_split, p.ntiles, (int)p.row_blocks, p.nsplit);
@@ -424,6 +435,9 @@ hipError_t launch_k(const HalfStep &h, const ValuPlan &p, hipStream_t s) {
             return launch_kr<KP, 2>(h, p, s);
         return hipErrorInvalidValue;
     default:
+        if constexpr (KP <= 3)
+            if (p.TJ == kSmallTileCols)
+                return launch_kr<KP, 1, kSmallTileCols>(h, p, s);
         return launch_kr<KP, 1>(h, p, s);
     }
 }
