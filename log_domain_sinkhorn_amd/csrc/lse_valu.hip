@@ -371,16 +371,17 @@ struct ValuPlan {
 };
 
 // Narrow tiles for small problems with one-record-chunk records (d <= 3).
-constexpr int kSmallTileCols = 64;
+constexpr int kSmallTileCols = 32;
 
 ValuPlan plan_valu(const Layout &L, int64_t rows, int64_t cols_pad) {
     ValuPlan p;
     p.TJ = tile_cols_for(L.rs);
     // When full-width tiles would leave fewer workgroups than CUs even at one
     // row per lane, narrower tiles give more column splits (1024^2 at d = 3:
-    // 16 -> 10 us per half-step); larger problems keep the wide tiles, whose
-    // per-workgroup costs are lower (16384^2: 85 us, against 110 us with
-    // 64-column tiles). Such plans always end at one row per lane.
+    // 16 us per half-step with 256 columns, ~9.5 with 64, ~8 with 32); larger
+    // problems keep the wide tiles, whose per-workgroup costs are lower
+    // (16384^2: 85 us, against 110 us with 64-column tiles). Such plans
+    // always end at one row per lane.
     if (L.rs <= 4 && (rows + 255) / 256 * (cols_pad / p.TJ) < kCUs)
         p.TJ = kSmallTileCols;
     p.ntiles = (int)(cols_pad / p.TJ);
