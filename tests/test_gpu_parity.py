@@ -252,6 +252,21 @@ def test_eps_scaling_schedule_d64():
     _check_stats(c, f, g, fo, go, eps_list[-1], "d=64 schedule")
 
 
+def test_eps_scaling_schedule_d160():
+    # Above 128 coordinates (64-column tiles, hi operands read twice), with
+    # the records rebuilt per stage; the d = 64 workload's distributions at
+    # d = 160 (N(0, I/d), the target shifted by 0.3 along a unit vector).
+    from workloads import geometric_eps_schedule
+    c = make_clouds("feature64_64k", n=900, m=1300, d=160)
+    eps_list = geometric_eps_schedule(2.0, 0.05, 5)
+    f, g = gpu_solve_schedule(c, eps_list[0], eps_list[-1], len(eps_list), 15)
+    fo, go = oracle.sinkhorn_schedule(c["x"], c["y"], c["a"], c["b"], eps_list, 15)
+    ef, eg = rel_inf(f, fo, eps_list[-1]), rel_inf(g, go, eps_list[-1])
+    print(f"d=160 schedule: rel err f {ef:.2e} g {eg:.2e}", flush=True)
+    assert ef <= TOL_POT and eg <= TOL_POT
+    _check_stats(c, f, g, fo, go, eps_list[-1], "d=160 schedule")
+
+
 def test_warm_start_d64():
     c = random_clouds(600, 900, 64, seed=8, spread=0.2)
     eps = 0.1

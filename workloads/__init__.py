@@ -166,18 +166,20 @@ def _sphere(rng: np.random.Generator, size: int, d: int) -> np.ndarray:
     return z / np.linalg.norm(z, axis=1, keepdims=True)
 
 
-def make_clouds(name: str, seed: int = 0, n: Optional[int] = None, m: Optional[int] = None) -> dict:
+def make_clouds(name: str, seed: int = 0, n: Optional[int] = None, m: Optional[int] = None,
+                d: Optional[int] = None) -> dict:
     """Draw the inputs of a point-cloud workload.
 
     ``n`` and ``m`` override the workload's sizes (same distributions, same
-    recipe) for smaller test cases. Returns a dict with fp32 ``x`` (n x d),
-    ``y`` (m x d), ``a`` (n), ``b`` (m) and the schedule ``eps`` (tuple) and
-    ``iters`` (per stage).
+    recipe) for smaller test cases; ``d`` overrides the feature dimension
+    (meant for ``feature64_64k``, whose distributions are defined for any d).
+    Returns a dict with fp32 ``x`` (n x d), ``y`` (m x d), ``a`` (n), ``b``
+    (m) and the schedule ``eps`` (tuple) and ``iters`` (per stage).
     """
     w = CLOUD_WORKLOADS[name]
     n = w.n if n is None else int(n)
     m = w.m if m is None else int(m)
-    d = w.d
+    d = w.d if d is None else int(d)
     rng = np.random.default_rng(seed)
     if name == "gauss3d_1k":
         x = rng.normal(0.0, 1.0, size=(n, d))
