@@ -5,13 +5,16 @@ One step = one whole solve of the workload (cold start, every iteration of
 alternating f/g half-steps) followed by its plan statistics (transport cost
 and marginal errors), on seeded synthetic inputs already resident in HBM.
 The headline workload is the 65536 x 65536 point-cloud problem in d = 64
-(fp32, Dirichlet weights, eps = 0.5, 100 iterations), whose half-steps run on
-the fp32 matrix cores. ``value`` = n*m*iterations*steps / timed seconds.
+(fp32, Dirichlet weights, eps = 0.5, 100 iterations), whose half-steps form
+each fp32 dot product as three split f16 matrix-core products. ``value`` =
+n*m*iterations*steps / timed seconds.
 
 Printed: one JSON line with the metric, the roofline of the dominant kernel
 (the half-step), the fp64 CPU oracle timed on a bounded sample of the same
 workload on this host's cores, and secondary measurements of the other
-workloads (d = 3 VALU path, eps-scaling schedule, batched 4x4 projection).
+workloads (d = 3 VALU path, eps-scaling schedule, the feature workload at
+d = 192, transport application, batched 4x4 projection by Sinkhorn-Knopp and
+by Newton with its backward).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--no-cpu-baseline] [--no-secondary]
@@ -472,7 +475,8 @@ def main():
     if not args.no_secondary:
         sec = {}
         wanted = None if args.secondary_only is None else set(args.secondary_only.split(","))
-        for name in ("cube_gauss3d_64k", "cube_gauss3d_16k", "mixture_sphere3d_eps_scaling"):
+        for name in ("cube_gauss3d_64k", "cube_gauss3d_16k", "mixture_sphere3d_eps_scaling",
+                     "feature192_64k"):
             if name == args.workload or (wanted is not None and name not in wanted):
                 continue
             print(f"# secondary {name}", file=sys.stderr, flush=True)
