@@ -295,7 +295,8 @@ def test_warm_start_from_shifted_g():
     np.testing.assert_allclose(g2, g1 - shift, atol=2e-5)
 
 
-@pytest.mark.parametrize("n,m,d", [(1024, 1024, 3), (65536, 4096, 3), (3000, 2000, 64)])
+@pytest.mark.parametrize("n,m,d", [(1024, 1024, 3), (65536, 4096, 3), (3000, 2000, 64),
+                                   (2000, 3000, 160)])
 def test_bitwise_deterministic(n, m, d):
     c = random_clouds(n, m, d, seed=4)
     f1, g1 = gpu_solve(c, 0.3, 3)
