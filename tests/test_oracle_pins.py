@@ -328,6 +328,95 @@ def test_schedule_converges_to_final_eps_fixed_point():
 # plan statistics                                                              #
 # --------------------------------------------------------------------------- #
 
+def test_plan_stats_single_target_unbalanced_closed_form():
+    # m = 1 with b_1 != sum a, one iteration from g = 0: the f step makes
+    # P_i1 = a_i, the g step rescales the column to b_1, so
+    # P_i1 = a_i b_1 / sum a. Row sums miss a_i by a_i (b_1/sum a - 1), all of
+    # one sign: the row L1 error is |b_1 - sum a| exactly, while an L-inf or
+    # squared reduction of the same deviations gives a different number for
+    # non-uniform a. The column is exact after the g step.
+    rng = np.random.default_rng(40)
+    x = rng.normal(size=(9, 3))
+    y = rng.normal(size=(1, 3))
+    a = rng.dirichlet(np.ones(9))
+    b = np.array([0.6])
+    eps = 0.3
+    f, g = oracle.sinkhorn(x, y, a, b, eps, 1)
+    st = oracle.plan_stats(x, y, a, b, f, g, eps)
+    np.testing.assert_allclose(st["rowsum"], a * b[0] / a.sum(), rtol=1e-12)
+    assert st["marg_row"] == pytest.approx(abs(b[0] - a.sum()), rel=1e-12)
+    dev = np.abs(a * b[0] / a.sum() - a)
+    assert abs(st["marg_row"] - dev.max()) > 0.1 * dev.sum()   # not L-inf
+    assert abs(st["marg_row"] - (dev**2).sum()) > 0.1 * dev.sum()  # not squared
+    assert st["marg_col"] == pytest.approx(0.0, abs=1e-14)
+    assert st["marg"] == pytest.approx(st["marg_row"] + st["marg_col"], rel=1e-15)
+    C = dense_cost(x, y)[:, 0]
+    assert st["cost"] == pytest.approx(float((a * b[0] / a.sum()) @ C), rel=1e-12)
+
+
+def test_plan_stats_single_target_after_f_step_only():
+    # m = 1 after an f half-step alone (any g): P_i1 = a_i, so the row error is
+    # zero and the column sum is sum a: column L1 error |sum a - b_1|.
+    rng = np.random.default_rng(41)
+    x = rng.normal(size=(11, 2))
+    y = rng.normal(size=(1, 2))
+    a = rng.dirichlet(np.ones(11))
+    b = np.array([1.7])
+    eps = 0.25
+    g = np.array([0.37])
+    f = oracle.half_update(x, y, a, g, eps)
+    st = oracle.plan_stats(x, y, a, b, f, g, eps)
+    assert st["marg_row"] == pytest.approx(0.0, abs=1e-14)
+    assert st["marg_col"] == pytest.approx(abs(a.sum() - b[0]), rel=1e-12)
+    np.testing.assert_allclose(st["colsum"], [a.sum()], rtol=1e-13)
+
+
+def test_plan_stats_column_errors_of_mixed_sign_closed_form():
+    # n = 1 at the origin, targets at +-1 on a line: every cost is exactly 1.
+    # After an f half-step from g = 0 the plan is P_1j = a_1 / m, so the
+    # column sums miss the Dirichlet b_j with both signs and the column L1
+    # error is sum_j |a_1/m - b_j|; the row error is zero.
+    rng = np.random.default_rng(42)
+    m = 12
+    x = np.zeros((1, 1))
+    y = np.where(np.arange(m) % 2 == 0, 1.0, -1.0).reshape(m, 1)
+    a = np.array([1.0])
+    b = rng.dirichlet(np.ones(m))
+    eps = 0.4
+    f = oracle.half_update(x, y, a, np.zeros(m), eps)
+    st = oracle.plan_stats(x, y, a, b, f, np.zeros(m), eps)
+    dev = np.abs(a[0] / m - b)
+    assert (a[0] / m - b).min() < 0 < (a[0] / m - b).max()  # both signs present
+    assert st["marg_col"] == pytest.approx(dev.sum(), rel=1e-12)
+    assert st["marg_row"] == pytest.approx(0.0, abs=1e-14)
+    np.testing.assert_allclose(st["colsum"], np.full(m, a[0] / m), rtol=1e-13)
+    assert st["cost"] == pytest.approx(1.0, rel=1e-13)
+
+
+def test_plan_stats_row_errors_of_mixed_sign_closed_form():
+    # m = 1 at the origin, sources at +-1 on a line (every cost 1), row
+    # potentials f_i = eps log w_i: the g half-step gives
+    # P_i1 = b_1 w_i / sum w, so the row L1 error is sum_i |b_1 w_i/sum w - a_i|
+    # (deviations of both signs) and the column error is zero.
+    rng = np.random.default_rng(43)
+    n = 10
+    x = np.where(np.arange(n) % 3 == 0, 1.0, -1.0).reshape(n, 1)
+    y = np.zeros((1, 1))
+    a = rng.dirichlet(np.ones(n))
+    w = rng.dirichlet(np.ones(n))
+    b = np.array([1.0])
+    eps = 0.15
+    f = eps * np.log(w)
+    g = oracle.half_update(y, x, b, f, eps)
+    st = oracle.plan_stats(x, y, a, b, f, g, eps)
+    P = b[0] * w / w.sum()
+    assert (P - a).min() < 0 < (P - a).max()
+    np.testing.assert_allclose(st["rowsum"], P, rtol=1e-12)
+    assert st["marg_row"] == pytest.approx(np.abs(P - a).sum(), rel=1e-12)
+    assert st["marg_col"] == pytest.approx(0.0, abs=1e-14)
+    assert st["cost"] == pytest.approx(1.0, rel=1e-13)
+
+
 def test_plan_stats_column_marginal_exact_after_g_step():
     c = random_clouds(30, 25, 3, seed=16)
     f, g = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], 0.4, 4)
