@@ -42,13 +42,17 @@
  *    give NaN or inf results, not an error code.
  *  - Outputs must not alias inputs unless a call says otherwise.
  *  - Calls are stateless; concurrent calls on different streams are safe.
+ *  - Each call takes at most one temporary allocation, sized up front.
+ *    When it cannot be had the call returns OT_ERROR_OUT_OF_MEMORY before
+ *    anything is enqueued.
  *  - Graph capture: ot_sinkhorn_solve, ot_plan_stats, ot_transport_apply and
  *    ot_birkhoff_project_batched have been captured into HIP graphs on
  *    `stream` (their temporary memory becomes the graph's stream-ordered
- *    allocations) and replayed with results identical to direct calls. The
- *    calls that allocate inside another call (the cosine calls,
- *    ot_barycentric_map, ot_cost_gradient_x) are not supported under
- *    capture: a graph containing them faulted on replay.
+ *    allocation) and replayed with results identical to direct calls. A
+ *    graph that also held the cosine calls, ot_barycentric_map and
+ *    ot_cost_gradient_x faulted on replay, cause unknown; those four calls
+ *    return OT_ERROR_NOT_SUPPORTED, enqueueing nothing, when `stream` is
+ *    capturing.
  */
 #ifndef OT_SINKHORN_H
 #define OT_SINKHORN_H
@@ -90,8 +94,8 @@ const char *ot_status_string(ot_status s);
  * Warm start (e.g. a decreasing eps schedule) is a second call with the f, g
  * of the first.  f and g must not overlap each other or any input.
  * Errors: INVALID_VALUE (null pointer, n or m < 1, d < 1, eps <= 0 or not
- * finite, iters < 0), NOT_SUPPORTED (d > OT_MAX_DIM), OUT_OF_MEMORY,
- * LAUNCH_FAILURE.
+ * finite, iters < 0), NOT_SUPPORTED (d > OT_MAX_DIM, n or m > 2^34),
+ * OUT_OF_MEMORY, LAUNCH_FAILURE.
  */
 ot_status ot_sinkhorn_solve(const float *x, const float *y, const float *a,
                             const float *b, int64_t n, int64_t m, int32_t d,

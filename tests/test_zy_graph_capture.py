@@ -104,11 +104,52 @@ def test_birkhoff_capture():
     _replays_match(run, [out, it], reset)
 
 
-@pytest.mark.skip(reason="replaying this graph faulted the GPU (illegal address in "
-                         "prep_h3_kernel) after the same sequence ran correctly eagerly; the "
-                         "cause is not found (it is the only captured sequence with "
-                         "temporary allocations nested inside another call's allocation), "
-                         "so it stays off the GPU")
+def test_calls_refused_under_capture():
+    # The calls of the sequence that faulted under capture and whose cause is
+    # not known return OT_ERROR_NOT_SUPPORTED on a capturing stream and
+    # enqueue nothing; outside a capture they run.
+    c = random_clouds(300, 200, 40, seed=6, spread=0.3)
+    x, y, a, b = dev(c["x"]), dev(c["y"]), dev(c["a"]), dev(c["b"])
+    f = torch.zeros(300, device=DEV)
+    g = torch.zeros(200, device=DEV)
+    cost = torch.zeros(1, dtype=torch.float64, device=DEV)
+    marg = torch.zeros(2, dtype=torch.float64, device=DEV)
+    out = torch.zeros(300, 40, device=DEV)
+    calls = {
+        "ot_sinkhorn_solve_cosine": lambda: lds.ot_sinkhorn_solve_cosine(x, y, a, b, 0.1, 3, f, g),
+        "ot_plan_stats_cosine": lambda: lds.ot_plan_stats_cosine(x, y, a, b, f, g, 0.1, cost,
+                                                                 marg),
+        "ot_barycentric_map": lambda: lds.ot_barycentric_map(x, y, a, f, g, 0.2, out),
+        "ot_cost_gradient_x": lambda: lds.ot_cost_gradient_x(x, y, f, g, 0.2, out),
+    }
+    marker = torch.zeros(1, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    status = {}
+    with torch.cuda.graph(graph, stream=side):
+        marker.add_(1.0)  # keeps the captured graph non-empty
+        for name, call in calls.items():
+            try:
+                call()
+                status[name] = 0
+            except lds.OTError as e:
+                status[name] = e.status
+    torch.cuda.synchronize()
+    print("status under capture:", status, flush=True)
+    assert all(v == 2 for v in status.values()), status
+    for name, call in calls.items():
+        call()
+    torch.cuda.synchronize()
+    assert torch.isfinite(f).all() and torch.isfinite(out).all()
+
+
+@pytest.mark.skip(reason="replaying this graph faulted the GPU (illegal address reported in "
+                         "prep_h3_kernel) after the same sequence ran correctly eagerly; reading "
+                         "the kernels' index ranges and the scratch layout found no out-of-range "
+                         "access, so the cause is unknown and the case stays off the GPU; the "
+                         "cosine calls, the barycentric map and the x-gradient refuse capture "
+                         "(test_calls_refused_under_capture)")
 def test_other_entry_points_capture():
     # eps schedule, cosine cost, barycentric map, x-gradient, 4x4 Newton and
     # its backward, all in one captured sequence.
