@@ -6,7 +6,10 @@ Calls only the fp64 oracle (``oracle/``) and the seeded input generators
 For each point-cloud workload named on the command line it draws the inputs,
 runs the oracle's alternating log-domain Sinkhorn iterations over the whole
 workload (every stage of an eps schedule, warm-started) from a cold start,
-and stores in ``tests/golden/full_<workload>.npz``:
+and stores in ``tests/golden/full_<workload>.npz``
+(``tests/golden/<workload>_<n>x<m>.npz`` when the workload is named as
+``<workload>@<n>x<m>``: the same distributions, schedule and iteration count
+at a smaller size):
 
 * ``f``, ``g``      the oracle's final potentials (fp64);
 * ``cost``, ``marg_row``, ``marg_col``  the oracle's plan statistics of those
@@ -28,7 +31,8 @@ workloads), so it checkpoints (f, g, position in the schedule) every
 schedule in chunks is exactly the same computation as one long run: the
 oracle updates f and g in place, half-step after half-step.
 
-Usage:  python tests/golden/make_full_size.py cube_gauss3d_16k feature64_64k
+Usage:  python tests/golden/make_full_size.py cube_gauss3d_16k feature64_64k \
+            mixture_sphere3d_eps_scaling@65536x49152
 """
 from __future__ import annotations
 
@@ -63,8 +67,19 @@ def input_key(c: dict) -> str:
     return h.hexdigest()
 
 
-def fixture_path(name: str) -> str:
-    return os.path.join(HERE, f"full_{name}.npz")
+def fixture_path(name: str, n=None, m=None) -> str:
+    if n is None:
+        return os.path.join(HERE, f"full_{name}.npz")
+    return os.path.join(HERE, f"{name}_{n}x{m}.npz")
+
+
+def parse_spec(spec: str):
+    """``name`` or ``name@NxM`` -> (name, n or None, m or None)."""
+    if "@" not in spec:
+        return spec, None, None
+    name, size = spec.split("@", 1)
+    n, m = size.lower().split("x")
+    return name, int(n), int(m)
 
 
 def _save_atomic(path: str, **arrays) -> None:
@@ -73,14 +88,17 @@ def _save_atomic(path: str, **arrays) -> None:
     os.replace(tmp, path)
 
 
-def run(name: str, ckpt_dir: str, chunk: int) -> None:
-    c = make_clouds(name)
+def run(spec: str, ckpt_dir: str, chunk: int) -> None:
+    name, n_over, m_over = parse_spec(spec)
+    c = make_clouds(name, n=n_over, m=m_over)
+    out_path = fixture_path(name, n_over, m_over)
+    tag = os.path.splitext(os.path.basename(out_path))[0]
     key = input_key(c)
     eps_list = [float(e) for e in c["eps"]]
     iters = int(c["iters"])
     total = iters * len(eps_list)
     os.makedirs(ckpt_dir, exist_ok=True)
-    ck = os.path.join(ckpt_dir, f"ckpt_{name}.npz")
+    ck = os.path.join(ckpt_dir, f"ckpt_{tag}.npz")
     done, f, g = 0, np.zeros(c["n"]), np.zeros(c["m"])
     if os.path.exists(ck):
         z = np.load(ck)
@@ -101,11 +119,12 @@ def run(name: str, ckpt_dir: str, chunk: int) -> None:
     f32 = f.astype(np.float32).astype(np.float64)
     g32 = g.astype(np.float32).astype(np.float64)
     s32 = oracle.plan_stats(c["x"], c["y"], c["a"], c["b"], f32, g32, eps)
-    _save_atomic(fixture_path(name), key=key, name=name, f=f, g=g, eps=np.array(eps_list),
+    _save_atomic(out_path, key=key, name=name, n=c["n"], m=c["m"], f=f, g=g,
+                 eps=np.array(eps_list),
                  iters=iters, cost=s64["cost"], marg_row=s64["marg_row"],
                  marg_col=s64["marg_col"], cost32=s32["cost"], marg_row32=s32["marg_row"],
                  marg_col32=s32["marg_col"], oracle_threads=oracle.num_threads())
-    print(f"[{name}] wrote {fixture_path(name)}: cost {s64['cost']:.12g}, "
+    print(f"[{name}] wrote {out_path}: cost {s64['cost']:.12g}, "
           f"marg {s64['marg_row']:.3e} + {s64['marg_col']:.3e}", flush=True)
 
 
@@ -116,8 +135,8 @@ def main() -> int:
     ap.add_argument("--chunk", type=int, default=5, help="iterations between checkpoints")
     args = ap.parse_args()
     oracle.build(force=False)
-    for name in args.workloads:
-        run(name, args.ckpt_dir, args.chunk)
+    for spec in args.workloads:
+        run(spec, args.ckpt_dir, args.chunk)
     return 0
 
 
