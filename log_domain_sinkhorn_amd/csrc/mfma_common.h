@@ -143,7 +143,8 @@ __device__ __forceinline__ void fold(const floatx16 &u, float Mu, float c, float
         // S is 0 or >= 2^-64 (the common path only adds when S + c >= 2^-64)
         // and Mn >= M + log2 S, so the factor stays below 2^64; S = 0 is kept
         // apart because M may move down by ~1e30 past a padding-only chunk.
-        S = S > 0.f ? S * hw_exp2(M - Mn) : 0.f;
+        // A NaN sum (from NaN inputs) stays NaN.
+        S = S == 0.f ? 0.f : S * hw_exp2(M - Mn);
         const float off = Mn - Mu;
         float c0 = 0.f, c1 = 0.f;
 #pragma unroll
