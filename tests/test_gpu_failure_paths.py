@@ -60,12 +60,12 @@ def test_out_of_memory_before_any_launch(d, n):
     assert e1.value.status == lds.OT_ERROR_OUT_OF_MEMORY
     assert e2.value.status == lds.OT_ERROR_OUT_OF_MEMORY
     assert torch.count_nonzero(f) == 0 and torch.count_nonzero(g) == 0  # nothing ran
-    # the next call succeeds and is correct (first rows checked by the oracle)
+    # the next call succeeds and is correct (sampled rows checked by the oracle)
     lds.ot_sinkhorn_solve(x, y, a, b, 0.5, 1, f, g)
     torch.cuda.synchronize()
     rows = np.arange(0, n, n // 64)
     fo = oracle.half_update(c["x"], c["y"], c["a"], np.zeros(n), 0.5, rows=rows)
-    assert rel_inf(f.cpu().numpy()[rows], fo, 0.5) <= 1e-5
+    assert rel_inf(f.cpu().numpy()[rows], fo, 0.5) <= TOL_POT
 
 
 @pytest.mark.parametrize("d", [3, 64])
