@@ -102,6 +102,40 @@ ot_status ot_sinkhorn_solve(const float *x, const float *y, const float *a,
                             float eps, int32_t iters, float *f, float *g,
                             void *stream);
 
+/* Bytes of the static device array ot_sinkhorn_solve_no_alloc works in, per GPU. */
+#define OT_NO_ALLOC_SCRATCH_BYTES (128ull << 20)
+
+/*
+ * ot_sinkhorn_solve_no_alloc -- for callers that cannot allocate device
+ * memory: code under HIP graph capture that must not record allocation
+ * nodes, tight serving loops, harnesses that forbid hipMalloc. It computes
+ * exactly what ot_sinkhorn_solve computes (same kernels, same results) but
+ * takes its scratch from a static device array of OT_NO_ALLOC_SCRATCH_BYTES
+ * (128 MiB) that the library holds on every GPU it runs on until the process
+ * ends, and calls no allocating routine.
+ *
+ * Scratch needed (n', m' = n, m rounded up to 256; kp = d rounded up to 32):
+ * the records of both clouds, 32 (n' + m') bytes for d < 32 and
+ * (8 kp + 8)(n' + m') bytes for d >= 32, plus 16 bytes per row and column
+ * split of the larger half-step (plus about 4 KiB per coordinate for
+ * d >= 32). n = m = 65536 needs 36 MiB at d = 3 and 69.25 MiB at d = 64,
+ * 131072 x 98304 at d = 3 needs 40 MiB; 65536 x 65536 at d = 128 (133.5 MiB)
+ * does not fit. A problem whose scratch exceeds the array returns
+ * OT_ERROR_NOT_SUPPORTED and enqueues nothing.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last
+ * call's contents (the solve writes every part it reads, so nothing needs
+ * clearing): calls that overlap in time on one GPU (from other threads or on
+ * other streams) race and must be serialised by the caller. The first call
+ * on a GPU looks up the array's address on that GPU (stream's device).
+ * Arguments, results and other errors as ot_sinkhorn_solve.
+ */
+ot_status ot_sinkhorn_solve_no_alloc(const float *x, const float *y,
+                                     const float *a, const float *b,
+                                     int64_t n, int64_t m, int32_t d, float eps,
+                                     int32_t iters, float *f, float *g,
+                                     void *stream);
+
 /*
  * ot_sinkhorn_solve_eps_scaling -- `stages` calls of ot_sinkhorn_solve with
  * eps_s = eps0 * (eps_end/eps0)^(s/(stages-1)), s = 0..stages-1 (eps0 alone

@@ -29,6 +29,7 @@ __all__ = [
     "ot_status_string",
     "ot_sinkhorn_solve",
     "ot_sinkhorn_solve_eps_scaling",
+    "ot_sinkhorn_solve_no_alloc",
     "ot_plan_stats",
     "ot_plan_cost",
     "ot_marginal_error",
@@ -56,6 +57,7 @@ OT_ERROR_OUT_OF_MEMORY = 3
 OT_ERROR_LAUNCH_FAILURE = 4
 OT_MAX_DIM = 192
 OT_MAX_VALUE_DIM = 1024
+OT_NO_ALLOC_SCRATCH_BYTES = 128 << 20
 
 _lock = threading.Lock()
 _handle = None
@@ -68,6 +70,8 @@ _f32 = ctypes.c_float
 _SIGNATURES = {
     "ot_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "ot_sinkhorn_solve": ([_p, _p, _p, _p, _i64, _i64, _i32, _f32, _i32, _p, _p, _p], ctypes.c_int),
+    "ot_sinkhorn_solve_no_alloc": ([_p, _p, _p, _p, _i64, _i64, _i32, _f32, _i32, _p, _p, _p],
+                                   ctypes.c_int),
     "ot_sinkhorn_solve_eps_scaling": (
         [_p, _p, _p, _p, _i64, _i64, _i32, _f32, _f32, _i32, _i32, _p, _p, _p], ctypes.c_int),
     "ot_plan_stats": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _f32, _p, _p, _p], ctypes.c_int),
@@ -205,6 +209,19 @@ def ot_sinkhorn_solve(x, y, a, b, eps: float, iters: int, f, g, stream=None) -> 
     _dev_tensor(g, "g", "f32", (m,))
     _call("ot_sinkhorn_solve", _ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d, float(eps),
           int(iters), _ptr(f), _ptr(g), _stream_of(x, stream))
+
+
+def ot_sinkhorn_solve_no_alloc(x, y, a, b, eps: float, iters: int, f, g, stream=None) -> None:
+    """:func:`ot_sinkhorn_solve` with its scratch in the library's static device
+    array (no allocation); NOT_SUPPORTED when the problem's scratch exceeds
+    ``OT_NO_ALLOC_SCRATCH_BYTES``. Calls on one GPU must not overlap."""
+    n, m, d = _clouds(x, y)
+    _dev_tensor(a, "a", "f32", (n,))
+    _dev_tensor(b, "b", "f32", (m,))
+    _dev_tensor(f, "f", "f32", (n,))
+    _dev_tensor(g, "g", "f32", (m,))
+    _call("ot_sinkhorn_solve_no_alloc", _ptr(x), _ptr(y), _ptr(a), _ptr(b), n, m, d,
+          float(eps), int(iters), _ptr(f), _ptr(g), _stream_of(x, stream))
 
 
 def ot_sinkhorn_solve_eps_scaling(x, y, a, b, eps0: float, eps_end: float, stages: int,

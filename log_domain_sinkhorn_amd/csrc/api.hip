@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace otsk {
 
 Layout choose_layout(int d) {
@@ -261,6 +263,49 @@ ot_status solve_alloc(const float *x, const float *y, const float *a, const floa
     return run_schedule(x, y, a, b, n, m, d, eps_list, stages, iters, f, g, B, s);
 }
 
+// Scratch of ot_sinkhorn_solve_no_alloc: a static device array, one copy on
+// every GPU the library runs on, kept until the process ends. Host code uses
+// only the per-device address that hipGetSymbolAddress returns for it (the
+// array's name on the host side is a stand-in, not a device address).
+constexpr size_t kNoAllocBytes = (size_t)OT_NO_ALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the array on the device of stream s; looked up once per device
+// with that device current.
+hipError_t no_alloc_scratch(hipStream_t s, void **out) {
+    int dev = 0, cur = 0;
+    hipError_t e = hipStreamGetDevice(s, &dev);
+    if (e == hipSuccess)
+        e = hipGetDevice(&cur);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+            return e;
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t r = hipSetDevice(cur);
+            if (e == hipSuccess)
+                e = r;
+        }
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return e;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 ot_status check_solve_outputs(const float *x, const float *y, const float *a, const float *b,
                               int64_t n, int64_t m, int32_t d, const float *f, const float *g) {
     if (!a || !b || !f || !g)
@@ -435,6 +480,31 @@ ot_status ot_sinkhorn_solve(const float *x, const float *y, const float *a, cons
         return st;
     const double e = eps;
     return solve_alloc(x, y, a, b, n, m, d, &e, 1, iters, f, g, (hipStream_t)stream);
+}
+
+ot_status ot_sinkhorn_solve_no_alloc(const float *x, const float *y, const float *a,
+                                     const float *b, int64_t n, int64_t m, int32_t d, float eps,
+                                     int32_t iters, float *f, float *g, void *stream) {
+    ot_status st = check_clouds(x, y, n, m, d, eps);
+    if (st == OT_SUCCESS && iters < 0)
+        st = OT_ERROR_INVALID_VALUE;
+    if (st == OT_SUCCESS)
+        st = check_solve_outputs(x, y, a, b, n, m, d, f, g);
+    if (st == OT_SUCCESS)
+        st = check_supported(n, m, d);
+    if (st == OT_SUCCESS && solve_scratch_bytes(n, m, d) > kNoAllocBytes)
+        st = OT_ERROR_NOT_SUPPORTED;
+    if (st != OT_SUCCESS || iters == 0)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    void *base = nullptr;
+    const hipError_t e = no_alloc_scratch(s, &base);
+    if (e != hipSuccess)
+        return map_error(e);
+    Carve c(base);
+    const SolveBufs B = carve_solve(c, n, m, d);
+    const double ed = eps;
+    return run_schedule(x, y, a, b, n, m, d, &ed, 1, iters, f, g, B, s);
 }
 
 ot_status ot_sinkhorn_solve_eps_scaling(const float *x, const float *y, const float *a,

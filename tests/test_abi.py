@@ -27,7 +27,7 @@ def test_header_declares_expected_functions():
         "ot_plan_stats", "ot_plan_cost", "ot_marginal_error", "ot_birkhoff_project_batched",
         "ot_transport_apply", "ot_barycentric_map", "ot_cost_gradient_x",
         "ot_birkhoff_project_newton_batched", "ot_birkhoff_projection_backward_batched",
-        "ot_sinkhorn_solve_cosine", "ot_plan_stats_cosine",
+        "ot_sinkhorn_solve_cosine", "ot_plan_stats_cosine", "ot_sinkhorn_solve_no_alloc",
     ])
 
 
@@ -41,6 +41,26 @@ def test_header_max_dim_matches_binding():
     text = open(lds._HEADER).read()
     assert f"#define OT_MAX_DIM {lds.OT_MAX_DIM}" in text
     assert f"#define OT_MAX_VALUE_DIM {lds.OT_MAX_VALUE_DIM}" in text
+    assert "#define OT_NO_ALLOC_SCRATCH_BYTES (128ull << 20)" in text
+    assert lds.OT_NO_ALLOC_SCRATCH_BYTES == 128 << 20
+
+
+def test_no_alloc_refuses_scratch_beyond_the_array_on_the_host(lib):
+    # 65536 x 65536 at d = 128 needs 133.5 MiB of scratch, more than the
+    # 128 MiB array: refused by the host-side size check before any HIP
+    # call, so placeholder addresses (far apart, never dereferenced) suffice.
+    n, d = 65536, 128
+    base = 1 << 44
+    step = 1 << 36
+    ptrs = [ctypes.c_void_p(base + k * step) for k in range(6)]
+    st = lib.ot_sinkhorn_solve_no_alloc(ptrs[0], ptrs[1], ptrs[2], ptrs[3], n, n, d,
+                                        ctypes.c_float(0.5), 1, ptrs[4], ptrs[5], None)
+    assert st == UNSUPPORTED
+    # 65536 x 65536 at d = 64 fits (69.25 MiB): with iters = 0 the call
+    # returns success without touching the device
+    st = lib.ot_sinkhorn_solve_no_alloc(ptrs[0], ptrs[1], ptrs[2], ptrs[3], n, n, 64,
+                                        ctypes.c_float(0.5), 0, ptrs[4], ptrs[5], None)
+    assert st == 0
 
 
 def test_status_strings(lib):
