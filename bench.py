@@ -37,26 +37,30 @@ METRIC = "Sinkhorn pair-evals/sec (n·m·iters/s) at n=m=65536 + % of FP32/exp r
 # MI355X published peaks used for the roofline fractions (dense).
 PEAK_MFMA_FP32_TFLOPS = 157.3
 PEAK_MFMA_FP16_TFLOPS = 2500.0
-# ALU ceiling of the d < 32 half-step, derived from the chip's issue slots
-# (256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz) and the per-pair-side instruction
-# mix of that kernel: kp fp64 FMAs + 1 fp64 add (the score, formed in fp64),
-# 1 f64->f32 convert, 1/2 v_max3_f32, 1 v_exp_f32 and 1 fp32 add. Every
-# instruction takes one issue slot except v_exp_f32, which issues at half
-# rate on gfx950 (measured: 31 vs 59 lane-ops/clk/CU for v_fma_f32; exp and
-# FMA streams do not overlap).
-ISSUE_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
-EXP_SLOTS = 2.0
-# One 4x4 Sinkhorn-Knopp iteration of the Birkhoff kernel: 8 max-subtracted
-# log-sum-exps of 4 terms (32 exp2 + 8 log2 at two slots each, ~60 other VALU
-# instructions, plus the bookkeeping of the loop) ~ 192 issue slots.
-BIRKHOFF_SLOTS_PER_ITER = 192.0
+# Vector-ALU capacity at the published fp32 vector peak (157.3 TFLOP/s, an
+# FMA being 2 flops): 7.865e13 fp32 FMA lane-operations per second. One
+# "slot" below is one such FMA lane-operation; what an exp2, a log2 or an add
+# costs in slots is measured in the same run by the rate microbenchmarks
+# (ratebench/rates.hip) as the FMA rate over its own rate.
+VALU_SLOTS_PER_S = 157.3e12 / 2.0
+# Work of the method per unit, from the operation counts of the update
+# (not from the kernels' instruction mix):
+#  d < 32 half-step, per pair-side: d FMAs for the score with the bias folded
+#    in, 1 max, 1 subtract, 1 add (2d + 3 flops, d + 3 slots) and one exp2;
+#  d >= 32 half-step, per pair-side: the 2d flops of the dot product (the
+#    bias enters the accumulator; the epilogue is the d < 32 one minus the
+#    score);
+#  4x4 Sinkhorn-Knopp iteration: 8 max-subtracted log-sum-exps of 4 terms,
+#    24 exp2 + 8 log2 + about 100 other operations.
+BIRKHOFF_EXP2, BIRKHOFF_LOG2, BIRKHOFF_OTHER = 24, 8, 100
 # One step of the 4x4 Newton dual solver (fp64 exponents and row maxima, row
 # softmaxes, gradient and 3x3 Hessian, Cholesky solve, line search), from the
 # rocprofv3 instruction counts of the 2^20-matrix batch: 7363 VALU
 # instructions per matrix, 755 of them transcendental (two issue slots), over
-# 5.37 steps per matrix on average -> (7363 + 755) / 5.37 ~ 1512 issue slots
-# per matrix-step, the per-matrix setup and final plan included.
-NEWTON_SLOTS_PER_STEP = 1512.0
+# 5.37 steps per matrix on average; each non-transcendental counted as one
+# slot and each transcendental at its measured cost. (The pages give no
+# operation count for the Newton solve; this is the implementation's.)
+NEWTON_VALU_PER_MATRIX, NEWTON_TRANS_PER_MATRIX, NEWTON_STEPS = 7363.0, 755.0, 5.37
 HBM_PEAK_BYTES_PER_S = 8.0e12
 
 HALF_STEP_KERNELS = ("lse_rows_h3_kernel", "lse_rows_valu_kernel")
@@ -75,11 +79,50 @@ def parse():
     return p.parse_args()
 
 
-def alu_peak_pair_sides(d: int) -> float:
-    """Pair-sides/s ceiling of the VALU half-step for feature dimension d."""
-    kp = (d + 1 + 3) // 4 * 4 - 1
-    slots = kp + 1 + 1 + 0.5 + EXP_SLOTS + 1
-    return ISSUE_SLOTS_PER_S / slots
+RATE_KINDS = {  # kind -> (name, chain steps per lane); see ratebench/rates.hip
+    0: ("v_fma_f32", 20000), 1: ("v_exp_f32", 20000), 2: ("v_log_f32 + v_add_f32", 10000),
+    3: ("v_exp_f32 beside v_fma_f32", 10000), 4: ("v_fma_f64", 10000),
+    5: ("v_mfma_f32_32x32x16_f16", 12000), 6: ("v_mfma_f32_32x32x2f32", 4000),
+    7: ("v_add_f32", 20000)}
+
+
+def measure_rates():
+    """Instruction rates of this GPU (ratebench/librates.so) with the shader
+    clock each ran at, and the slot costs (relative to an fp32 FMA) of exp2,
+    log2 and add that the ALU ceilings use."""
+    import ctypes
+
+    path = os.path.join(ROOT, "log_domain_sinkhorn_amd", "ratebench", "librates.so")
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.otr_measure.argtypes = [ctypes.c_int, ctypes.c_int, dp, dp]
+    rates, clocks = {}, {}
+    for kind, (name, iters) in RATE_KINDS.items():
+        v, hz = ctypes.c_double(0.0), ctypes.c_double(0.0)
+        st = lib.otr_measure(kind, iters, ctypes.byref(v), ctypes.byref(hz))
+        if st != 0:
+            raise RuntimeError(f"rate microbenchmark {name} failed with HIP error {st}")
+        rates[name], clocks[name] = v.value, hz.value
+    fma = rates["v_fma_f32"]
+    add_slots = fma / rates["v_add_f32"]
+    per_clk = {k: rates[k] / (clocks[k] * 256) for k in rates if clocks[k] > 0}
+    return {
+        "lane_ops_per_s": {k: v for k, v in rates.items() if "mfma" not in k},
+        "mfma_tflops": {k: v / 1e12 for k, v in rates.items() if "mfma" in k},
+        "shader_clock_ghz": {k: v / 1e9 for k, v in clocks.items()},
+        "per_clock_per_cu": per_clk,
+        "exp2_slots": fma / rates["v_exp_f32"],
+        "log2_slots": fma / rates["v_log_f32 + v_add_f32"] - add_slots,
+        "add_slots": add_slots,
+        "exp2_beside_fma_slots": 2.0 * fma / rates["v_exp_f32 beside v_fma_f32"],
+        "source": "log_domain_sinkhorn_amd/ratebench/rates.hip",
+    }
+
+
+def alu_slots_per_pair_side(d: int, rates) -> float:
+    """Slots of the method's work per pair-side of a d < 32 half-step: d FMAs,
+    max, subtract, add, one exp2."""
+    return d + 3 * rates["add_slots"] + rates["exp2_slots"]
 
 
 def source_digest(files):
@@ -191,14 +234,36 @@ def run_cloud_workload(name, steps, warmup, torch, lds, with_stats=True):
     solve_ms = [t.ms() for t in solve_ms]
     stats_ms = [t.ms() for t in stats_ms]
     total_iters = iters * len(eps_list)
-    half_steps = 2 * total_iters
-    half_ms = sum(solve_ms) / steps / half_steps
+    # The half-step launch duration, live, on the stream the library launches
+    # on: solves of k_long and k_short iterations differ by exactly
+    # 2 (k_long - k_short) half-steps (each: the half-step kernel and, with
+    # column splits, its merge); the per-solve record preparation cancels.
+    k_long, k_short = min(iters, 21), 1
+    eps_last = eps_list[-1]
+
+    def solve_k(k):
+        g.zero_()
+        lds.ot_sinkhorn_solve(x, y, a, b, eps_last, k, f, g)
+
+    half_ms = None
+    if k_long > k_short:
+        t_long, t_short = [], []
+        for _ in range(3):
+            with Timer(torch) as tl:
+                solve_k(k_long)
+            with Timer(torch) as tsh:
+                solve_k(k_short)
+            t_long.append(tl)
+            t_short.append(tsh)
+        d_ms = [tl.ms() - tsh.ms() for tl, tsh in zip(t_long, t_short)]
+        half_ms = sorted(d_ms)[1] / (2 * (k_long - k_short))
     return {
         "name": name, "n": n, "m": m, "d": d, "eps": list(eps_list), "iters": iters,
         "total_iters": total_iters, "steps": steps, "total_ms": total_ms, "wall_s": wall,
         "ms_per_step": total_ms / steps, "solve_ms": sum(solve_ms) / steps,
         "stats_ms": (sum(stats_ms) / steps) if stats_ms else None,
         "half_step_ms": half_ms,
+        "half_step_ms_whole_solve": sum(solve_ms) / steps / (2 * total_iters),
         "pair_evals_per_s": n * m * total_iters * steps / (total_ms / 1e3),
         "cost": cost.item(), "marg": marg.cpu().tolist(),
     }
@@ -209,62 +274,73 @@ def h3_kp(d: int) -> int:
     return (d + 31) // 32 * 32
 
 
-def roofline_for(r, workload):
+def roofline_for(r, workload, rates):
+    """Roofline of the half-step kernel: the method's work per launch (per
+    pair-side counts above) over the live launch duration, against the peak
+    of what executes it."""
     n, m, d = r["n"], r["m"], r["d"]
     launch_s = r["half_step_ms"] / 1e3
     if d >= 32:
-        # The d >= 32 half-step forms each fp32 dot product as three f16
-        # matrix-core products (hi.hi + lo.hi + hi.lo) over kp = 32*ceil(d/32)
-        # coordinates, 6 * kp f16 MFMA flops per pair-side, and adds the
-        # column bias and the row offset with one fp32 MFMA k-step pair,
-        # 4 fp32 MFMA flops per pair-side. Both run on the same matrix pipe,
-        # one after the other, so the ceiling is their time at the published
-        # peaks: achieved is counted in f16-equivalent flops, an fp32 MFMA
-        # flop weighing 2500/157.3 f16 flops. The f16 flops alone against the
-        # f16 peak, and the fp32-equivalent rate of the method (2d flops per
-        # pair-side) against the fp32 MFMA peak, are printed beside it.
+        # The dot products run on the f16 matrix cores (each fp32 product as
+        # three split f16 products), so the peak is the f16 dense peak; the
+        # method's work is 2d flops per pair-side.
         kp = h3_kp(d)
-        f16 = 6.0 * kp * n * m
-        f32 = 4.0 * n * m
-        equiv = f16 + f32 * PEAK_MFMA_FP16_TFLOPS / PEAK_MFMA_FP32_TFLOPS
-        ach = equiv / launch_s / 1e12
-        alg = 2.0 * d * n * m / launch_s / 1e12
+        work = 2.0 * d * n * m
+        ach = work / launch_s / 1e12
+        # Implementation model, beside it: the kernel issues 6*kp f16 MFMA
+        # flops (three split products over kp = 32*ceil(d/32) coordinates)
+        # and 4 fp32 MFMA flops (column bias and row offset) per pair-side on
+        # the one matrix pipe, one after the other; at the published peaks
+        # that is kp*6/2500 + 4/157.3 ps per pair-side (448 cycles per 32x32
+        # subtile-wave at d = 64). Its ceiling on the method's rate is
+        # 2d / (6 kp + 4 * 2500/157.3).
+        impl_flops = 6.0 * kp + 4.0 * PEAK_MFMA_FP16_TFLOPS / PEAK_MFMA_FP32_TFLOPS
+        impl_ach = impl_flops * n * m / launch_s / 1e12
         return {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_FP16_TFLOPS,
                 "unit": "TFLOP/s", "frac": ach / PEAK_MFMA_FP16_TFLOPS,
                 "traffic": traffic_for("lse_rows_h3_kernel", workload),
                 "kernel": f"lse_rows_h3_kernel<{kp}>", "launch_ms": r["half_step_ms"],
-                "work_per_launch": (f"{n}*{m} pair-sides x ({6 * kp} f16 + 4 fp32 MFMA flops), "
-                                    f"counted as {6 * kp + 4 * PEAK_MFMA_FP16_TFLOPS / PEAK_MFMA_FP32_TFLOPS:.1f} "
-                                    "f16-equivalent flops"),
-                "f16_only_tflops": f16 / launch_s / 1e12,
-                "f16_only_frac": f16 / launch_s / 1e12 / PEAK_MFMA_FP16_TFLOPS,
-                "fp32_equivalent_tflops": alg, "fp32_mfma_peak": PEAK_MFMA_FP32_TFLOPS}
+                "work_per_launch": f"{n}*{m} pair-sides x {2 * d} flops (the dot product, 2d)",
+                "peak_dtype": "f16 (dense matrix cores; the fp32 dot products are formed as "
+                              "three split f16 products with fp32 accumulation)",
+                "implementation_model": {
+                    "matrix_flops_per_pair_side": f"{6 * kp} f16 + 4 fp32 MFMA",
+                    "f16_equivalent_per_pair_side": impl_flops,
+                    "achieved_f16_equivalent_tflops": impl_ach,
+                    "frac_of_f16_peak": impl_ach / PEAK_MFMA_FP16_TFLOPS,
+                    "ceiling_on_frac": 2.0 * d / impl_flops},
+                "vs_fp32_mfma_peak": {"fp32_equivalent_tflops": ach,
+                                      "peak": PEAK_MFMA_FP32_TFLOPS,
+                                      "ratio": ach / PEAK_MFMA_FP32_TFLOPS}}
+    slots = alu_slots_per_pair_side(d, rates)
     flops_per_ps = 2 * d + 3
     ach = flops_per_ps * n * m / launch_s / 1e12
-    peak = alu_peak_pair_sides(d) * flops_per_ps / 1e12
+    peak = VALU_SLOTS_PER_S / slots * flops_per_ps / 1e12
     return {"bound": "alu", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
             "frac": ach / peak, "traffic": traffic_for("lse_rows_valu_kernel", workload),
             "kernel": "lse_rows_valu_kernel", "launch_ms": r["half_step_ms"],
-            "work_per_launch": f"{n}*{m} pair-sides x ({flops_per_ps} flops + 1 exp2)"}
+            "work_per_launch": f"{n}*{m} pair-sides x ({flops_per_ps} flops + 1 exp2)",
+            "peak_model": f"{VALU_SLOTS_PER_S:.4g} fp32 FMA lane-ops/s (157.3 TFLOP/s) / "
+                          f"{slots:.2f} slots per pair-side ({d} FMA + max + sub + add at "
+                          f"{rates['add_slots']:.2f} + exp2 at {rates['exp2_slots']:.2f} slots, "
+                          "measured)"}
 
 
-def stats_roofline(n, m, d, stats_ms):
+def stats_roofline(n, m, d, stats_ms, rates):
     """Plan statistics (one row pass with cost, one column pass) against the
-    ceiling of the hardware that bounds them. d < 32: issue slots per pair,
-    row pass 2d (C by direct difference) + 3 (exponent) + 2 (exp2) + 2 (sums)
-    and column pass 2d + 3 + 2 + 1. d >= 32: each pass runs the half-step's
-    matrix work (6*kp f16 + 4 fp32 MFMA flops per pair, the fp32 ones
-    weighing 2500/157.3 f16 flops) against the f16 peak."""
+    method's work. Per pair and pass: the score (d FMAs), the exp2, the sum
+    of P (1 add) and in the row pass the cost term (C from the score: 2
+    flops, P*C: 1 FMA). d < 32: issue slots at the published clock; d >= 32:
+    the score's 2d flops per pass on the f16 matrix-core peak."""
     if d >= 32:
-        kp = h3_kp(d)
-        equiv = 2.0 * n * m * (6 * kp + 4 * PEAK_MFMA_FP16_TFLOPS / PEAK_MFMA_FP32_TFLOPS)
-        model_ms = equiv / (PEAK_MFMA_FP16_TFLOPS * 1e12) * 1e3
-        return {"bound": "mfma", "model_ms": model_ms, "frac": model_ms / stats_ms,
-                "model": "2 passes x the half-step's matrix work"}
-    slots = (2 * d + 7) + (2 * d + 6)
-    model_ms = n * m * slots / ISSUE_SLOTS_PER_S * 1e3
+        work_ms = 2.0 * 2.0 * d * n * m / (PEAK_MFMA_FP16_TFLOPS * 1e12) * 1e3
+        return {"bound": "mfma", "model_ms": work_ms, "frac": work_ms / stats_ms,
+                "model": "2 passes x 2d flops per pair on the f16 peak"}
+    e, ad = rates["exp2_slots"], rates["add_slots"]
+    slots = (d + ad + e + 3 * ad) + (d + ad + e)
+    model_ms = n * m * slots / VALU_SLOTS_PER_S * 1e3
     return {"bound": "alu", "model_ms": model_ms, "frac": model_ms / stats_ms,
-            "model": f"{slots} issue slots per pair over both passes"}
+            "model": f"{slots:.2f} issue slots per pair over both passes"}
 
 
 def gemm_calibration(torch, n=8192, reps=10):
@@ -306,9 +382,11 @@ def cpu_baseline(name):
                       f"iterations at eps={c['eps'][0]} ({dt:.1f} s)"}
 
 
-def run_birkhoff(name, torch, lds, reps=5):
+def run_birkhoff(name, torch, lds, rates, reps=5):
     from workloads import BIRKHOFF_WORKLOADS, make_logits
 
+    slots = (BIRKHOFF_EXP2 * rates["exp2_slots"] + BIRKHOFF_LOG2 * rates["log2_slots"]
+             + BIRKHOFF_OTHER * rates["add_slots"])
     w = BIRKHOFF_WORKLOADS[name]
     L = torch.from_numpy(make_logits(w.batch, w.sigmas, seed=0)).to("cuda:0")
     out = torch.empty_like(L)
@@ -336,14 +414,17 @@ def run_birkhoff(name, torch, lds, reps=5):
             "iters_histogram": counts,
             "hbm_gb_per_s": w.batch * (64 + 64 + 4) / (ms / 1e3) / 1e9,
             # Iterations issued (a wave runs until its slowest lane stops)
-            # against the issue-slot ceiling of the kernel's loop body.
+            # against the issue-slot ceiling of the method's work per
+            # iteration (24 exp2 + 8 log2 + ~100 operations, transcendentals
+            # at their measured slot cost).
             "roofline": {"bound": "alu", "achieved": issued / (ms / 1e3),
-                         "peak": ISSUE_SLOTS_PER_S / BIRKHOFF_SLOTS_PER_ITER,
+                         "peak": VALU_SLOTS_PER_S / slots,
                          "unit": "matrix-iterations/s",
-                         "frac": issued / (ms / 1e3) / (ISSUE_SLOTS_PER_S / BIRKHOFF_SLOTS_PER_ITER)}}
+                         "frac": issued / (ms / 1e3) / (VALU_SLOTS_PER_S / slots),
+                         "slots_per_iteration": slots}}
 
 
-def run_birkhoff_newton(name, torch, lds, reps=5):
+def run_birkhoff_newton(name, torch, lds, rates, reps=5):
     """Newton forward (tol 1e-6, cap 50 steps) and the implicit backward on the
     batch of ``name``; the backward is HBM-bound (plan and dl/dP in, dl/dL
     out: 192 bytes per matrix)."""
@@ -366,27 +447,31 @@ def run_birkhoff_newton(name, torch, lds, reps=5):
             lds.ot_birkhoff_projection_backward_batched(out, grad, w.eps, gl)
     fms, bms = tf.ms() / reps, tb.ms() / reps
     steps = it.to(torch.int64)
+    step_slots = ((NEWTON_VALU_PER_MATRIX - NEWTON_TRANS_PER_MATRIX) * rates["add_slots"]
+                  + NEWTON_TRANS_PER_MATRIX * rates["exp2_slots"]) / NEWTON_STEPS
     return {"name": f"{name}:newton", "batch": w.batch, "tol": 1e-6, "max_steps": 50,
             "forward_ms": fms, "backward_ms": bms,
             "forward_matrices_per_s": w.batch / (fms / 1e3),
             "forward_backward_matrices_per_s": w.batch / ((fms + bms) / 1e3),
             "mean_steps": float(steps.float().mean().item()), "max_steps_taken": int(steps.max()),
             "backward_hbm_gb_per_s": w.batch * 192 / (bms / 1e3) / 1e9,
-            # forward: issue-bound (one matrix per lane, fp64 and exp2 work in
-            # registers); backward: HBM-bound, 192 bytes per matrix
+            # forward: ALU-bound (one matrix per lane, fp64 and exp2 work in
+            # registers), against the implementation's instruction count;
+            # backward: HBM-bound, 192 bytes per matrix
             "roofline": {"bound": "alu",
                          "achieved": float(steps.sum().item()) / (fms / 1e3),
-                         "peak": ISSUE_SLOTS_PER_S / NEWTON_SLOTS_PER_STEP,
+                         "peak": VALU_SLOTS_PER_S / step_slots,
                          "unit": "matrix-steps/s",
                          "frac": float(steps.sum().item()) / (fms / 1e3)
-                         / (ISSUE_SLOTS_PER_S / NEWTON_SLOTS_PER_STEP)},
+                         / (VALU_SLOTS_PER_S / step_slots),
+                         "slots_per_step": step_slots},
             "backward_roofline": {"bound": "hbm",
                                   "achieved": w.batch * 192 / (bms / 1e3) / 1e9,
                                   "peak": HBM_PEAK_BYTES_PER_S / 1e9, "unit": "GB/s",
                                   "frac": w.batch * 192 / (bms / 1e3) / HBM_PEAK_BYTES_PER_S}}
 
 
-def run_transport(name, torch, lds, reps=10, warm=3):
+def run_transport(name, torch, lds, rates, reps=10, warm=3):
     """Transport application P·y (values = the target points) and the
     x-gradient at the potentials of a short solve of workload ``name``."""
     from workloads import make_clouds
@@ -425,10 +510,10 @@ def run_transport(name, torch, lds, reps=10, warm=3):
                                       "frac": model_ms / res["apply_ms"],
                                       "model": f"{cycles} matrix-pipe cycles per 32x32 subtile"}
     else:
-        # VALU path, per pair: d fp64 FMAs + 1 fp64 add (the exponent), one
-        # f64->f32 convert, exp2 at two issue slots, dv fp32 FMAs (P v).
-        slots = d + 1 + 1 + EXP_SLOTS + d
-        model_ms = n * m * slots / ISSUE_SLOTS_PER_S * 1e3
+        # VALU path, the method's work per pair: the exponent (d FMAs and
+        # the bias add), one exp2, dv FMAs (P v).
+        slots = d + rates["add_slots"] + rates["exp2_slots"] + d
+        model_ms = n * m * slots / VALU_SLOTS_PER_S * 1e3
         res["roofline_whole_call"] = {"bound": "alu", "model_ms": model_ms,
                                       "frac": model_ms / res["apply_ms"],
                                       "model": f"{slots:g} issue slots per pair"}
@@ -454,20 +539,27 @@ def main():
     print(f"# headline {args.workload}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr,
           flush=True)
     r = run_cloud_workload(args.workload, args.steps, args.warmup, torch, lds)
+    print("# instruction rates", file=sys.stderr, flush=True)
+    rates = measure_rates()
+    dtype = ("f32 (dot products as three split f16 matrix-core products, fp32 accumulation)"
+             if r["d"] >= 32 else "f32 (scores formed in f64)")
     out = {
         "metric": METRIC, "value": r["pair_evals_per_s"], "unit": "pair-evals/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": dtype, "data": "synthetic",
         "config": {"workload": args.workload, "n": r["n"], "m": r["m"], "d": r["d"],
                    "eps": r["eps"], "iters": r["iters"],
                    "step": "cold-start solve + plan statistics"},
-        "roofline": roofline_for(r, args.workload),
+        "roofline": roofline_for(r, args.workload, rates),
         "detail": {"calibration_copy_bytes": copy_bytes,
                    "f16_gemm_same_gpu": gemm_calibration(torch) if r["d"] >= 32 else None,
                    "solve_ms": r["solve_ms"], "stats_ms": r["stats_ms"],
-                   "stats_roofline": stats_roofline(r["n"], r["m"], r["d"], r["stats_ms"]),
-                   "half_step_ms": r["half_step_ms"], "cost": r["cost"], "marg": r["marg"]},
+                   "stats_roofline": stats_roofline(r["n"], r["m"], r["d"], r["stats_ms"],
+                                                    rates),
+                   "half_step_ms": r["half_step_ms"],
+                   "half_step_ms_whole_solve": r["half_step_ms_whole_solve"],
+                   "cost": r["cost"], "marg": r["marg"], "rates": rates},
     }
     if not args.no_cpu_baseline:
         print("# cpu baseline", file=sys.stderr, flush=True)
@@ -483,22 +575,24 @@ def main():
             s = run_cloud_workload(name, 1, 1, torch, lds)
             sec[name] = {"pair_evals_per_s": s["pair_evals_per_s"], "ms_per_step": s["ms_per_step"],
                          "solve_ms": s["solve_ms"], "stats_ms": s["stats_ms"],
-                         "stats_roofline": stats_roofline(s["n"], s["m"], s["d"], s["stats_ms"]),
-                         "roofline": roofline_for(s, name)}
+                         "stats_roofline": stats_roofline(s["n"], s["m"], s["d"], s["stats_ms"],
+                                                          rates),
+                         "roofline": roofline_for(s, name, rates)}
         for name in ("feature64_64k", "cube_gauss3d_64k"):
             key = f"transport:{name}"
             if wanted is not None and key not in wanted:
                 continue
             print(f"# secondary {key}", file=sys.stderr, flush=True)
-            sec[key] = run_transport(name, torch, lds)
+            sec[key] = run_transport(name, torch, lds, rates)
         for name in ("birkhoff4x4_1m_fixed20", "birkhoff4x4_1m"):
             if wanted is not None and name not in wanted:
                 continue
             print(f"# secondary {name}", file=sys.stderr, flush=True)
-            sec[name] = run_birkhoff(name, torch, lds)
+            sec[name] = run_birkhoff(name, torch, lds, rates)
         if wanted is None or "birkhoff4x4_1m:newton" in wanted:
             print("# secondary birkhoff4x4_1m:newton", file=sys.stderr, flush=True)
-            sec["birkhoff4x4_1m:newton"] = run_birkhoff_newton("birkhoff4x4_1m", torch, lds)
+            sec["birkhoff4x4_1m:newton"] = run_birkhoff_newton("birkhoff4x4_1m", torch, lds,
+                                                               rates)
         out["secondary"] = sec
     print(json.dumps(out))
 

@@ -1,8 +1,10 @@
-"""Build the gfx950 HIP library ``libotsinkhorn.so`` in-tree with hipcc.
+"""Build the gfx950 HIP libraries in-tree with hipcc.
 
 Every source under ``csrc/`` is compiled for ``--offload-arch=gfx950`` only,
 with packed fp32 instructions disabled (``-packed-fp32-ops``), and linked into
-one shared library next to this file. Run ``python -m
+``libotsinkhorn.so`` next to this file (the solver library). The instruction
+rate microbenchmarks the benchmark uses for its ceilings,
+``ratebench/rates.hip``, become ``ratebench/librates.so``. Run ``python -m
 log_domain_sinkhorn_amd.build`` or call :func:`build`.
 """
 from __future__ import annotations
@@ -20,6 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libotsinkhorn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
+RATES_SRC = os.path.join(HERE, "ratebench", "rates.hip")
+RATES_LIB = os.path.join(HERE, "ratebench", "librates.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -45,20 +49,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link ``libotsinkhorn.so``; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
+def _link(objs, path):
+    tmp = path + f".tmp{os.getpid()}"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link ``libotsinkhorn.so`` (and the rate
+    microbenchmarks' ``librates.so``); returns the solver library's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sources() + [RATES_SRC]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:-1], LIB_PATH)
+    _link(objs[-1:], RATES_LIB)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {RATES_LIB}")
     return LIB_PATH
 
 
