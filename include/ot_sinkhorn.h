@@ -71,10 +71,14 @@ typedef enum {
     OT_ERROR_LAUNCH_FAILURE = 4  /* a HIP call or kernel launch reported an error */
 } ot_status;
 
-/* Largest feature dimension d the point-cloud calls accept (the matrix-core
- * kernels keep a row's split coordinates in registers; above this size they
- * would spill). */
-#define OT_MAX_DIM 192
+/* Largest feature dimension d the point-cloud calls accept: up to 192 the
+ * matrix-core kernels work on 32x32 tiles, from 193 to 512 on 16x16 tiles
+ * (half the row-operand registers per lane). */
+#define OT_MAX_DIM 512
+
+/* Largest d of the transport calls (ot_transport_apply, ot_barycentric_map,
+ * ot_cost_gradient_x); above it they return OT_ERROR_NOT_SUPPORTED. */
+#define OT_MAX_TRANSPORT_DIM 192
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *ot_status_string(ot_status s);

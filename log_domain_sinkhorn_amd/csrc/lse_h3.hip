@@ -204,8 +204,18 @@ __global__ __launch_bounds__(256) void center_partial_kernel(const float *__rest
     __shared__ double red[256];
     const float *p = blockIdx.y ? y : x;
     const int64_t cnt = blockIdx.y ? m : n;
-    const int rows = 256 / d;
     const int tid = threadIdx.x;
+    if (d > 256) {
+        // One row per block step; thread tid sums coordinates tid, tid + 256.
+        for (int k = tid; k < d; k += 256) {
+            double sum = 0.0;
+            for (int64_t r = blockIdx.x; r < cnt; r += gridDim.x)
+                sum += (double)p[r * d + k];
+            part[((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * d + k] = sum;
+        }
+        return;
+    }
+    const int rows = 256 / d;
     const int k = tid % d, r0 = tid / d;
     double sum = 0.0;
     if (r0 < rows)
@@ -224,15 +234,14 @@ __global__ __launch_bounds__(256) void center_partial_kernel(const float *__rest
 __global__ __launch_bounds__(256) void center_final_kernel(const double *__restrict__ part, int nb,
                                                            int d, int64_t n, int64_t m,
                                                            float *__restrict__ center) {
-    const int k = threadIdx.x;
-    if (k >= d)
-        return;
-    double sx = 0.0, sy = 0.0;
-    for (int b = 0; b < nb; ++b) {
-        sx += part[(int64_t)b * d + k];
-        sy += part[((int64_t)nb + b) * d + k];
+    for (int k = threadIdx.x; k < d; k += blockDim.x) {
+        double sx = 0.0, sy = 0.0;
+        for (int b = 0; b < nb; ++b) {
+            sx += part[(int64_t)b * d + k];
+            sy += part[((int64_t)nb + b) * d + k];
+        }
+        center[k] = (float)(0.5 * (sx / (double)n + sy / (double)m));
     }
-    center[k] = (float)(0.5 * (sx / (double)n + sy / (double)m));
 }
 
 // Largest |coordinate| of x - c (blockIdx.y == 0) or y - c (1), one value per
@@ -493,7 +502,9 @@ constexpr int kCenterBlocks = 256;
 
 }  // namespace
 
-int h3_kp(int d) { return (d + 31) / 32 * 32; }
+// Coordinates per record: 32k up to 192 (the 32x32 kernels); above, the
+// wide kernels' sizes 224, 256, 320, 384, 448, 512.
+int h3_kp(int d) { return d <= 256 ? (d + 31) / 32 * 32 : (d + 63) / 64 * 64; }
 
 size_t h3_maxabs_floats() { return 2 * kMaxabsBlocks + 2; }
 
@@ -503,7 +514,7 @@ size_t h3_center_scratch_bytes(int d) {
 
 hipError_t launch_center_maxabs(const float *x, int64_t n, const float *y, int64_t m, int d,
                                 void *center_scratch, float *scratch, hipStream_t s) {
-    if (d < 1 || d > 192)
+    if (d < 1 || d > 512)
         return hipErrorInvalidValue;
     double *part = static_cast<double *>(center_scratch);
     float *center = reinterpret_cast<float *>(part + (size_t)2 * kCenterBlocks * d);
@@ -539,6 +550,8 @@ hipError_t launch_prep_h3(const float *pts, const float *pot, int64_t count, int
 }
 
 int plan_pass_h3_splits(int64_t rows, int64_t cols_pad, int kp) {
+    if (kp > 192)
+        return plan_pass_wide_splits(rows, cols_pad, kp);
     return plan_h3(rows, cols_pad, kp).nsplit;
 }
 
@@ -546,6 +559,9 @@ hipError_t launch_plan_pass_h3(int kp, bool cost, const void *row_rec, const flo
                                const float *row_nrm, const void *col_rec, const float *col_hat,
                                const float *col_nrm, int64_t rows, int64_t rows_pad,
                                int64_t cols_pad, double scale, double2 *part, hipStream_t s) {
+    if (kp > 192)
+        return launch_plan_pass_wide(kp, cost, row_rec, row_hat, row_nrm, col_rec, col_hat,
+                                     col_nrm, rows, rows_pad, cols_pad, scale, part, s);
     const H3Plan p = plan_h3(rows, cols_pad, kp);
     dim3 grid((unsigned)p.row_blocks, (unsigned)p.nsplit);
     const float4 *rr = static_cast<const float4 *>(row_rec);
@@ -577,11 +593,21 @@ hipError_t launch_plan_pass_h3(int kp, bool cost, const void *row_rec, const flo
 }
 
 size_t half_step_partials_h3(int64_t rows, int64_t cols_pad, int kp) {
+    if (kp > 192)
+        return half_step_partials_wide(rows, cols_pad, kp);
     const H3Plan p = plan_h3(rows, cols_pad, kp);
     return p.nsplit > 1 ? (size_t)p.nsplit * (size_t)pad_points(rows) : 0;
 }
 
+hipError_t launch_merge_h3(const HalfStep &h, int nsplit, hipStream_t s) {
+    hipLaunchKernelGGL(lse_merge_h3_kernel, dim3((unsigned)((h.rows + 255) / 256)), dim3(256), 0,
+                       s, h, nsplit);
+    return hipGetLastError();
+}
+
 hipError_t launch_half_step_h3(const HalfStep &h, int kp, hipStream_t s) {
+    if (kp > 192)
+        return launch_half_step_wide(h, kp, s);
     const H3Plan p = plan_h3(h.rows, h.cols_pad, kp);
     hipError_t e;
     switch (kp) {
@@ -595,9 +621,7 @@ hipError_t launch_half_step_h3(const HalfStep &h, int kp, hipStream_t s) {
     }
     if (e != hipSuccess || p.nsplit <= 1)
         return e;
-    hipLaunchKernelGGL(lse_merge_h3_kernel, dim3((unsigned)((h.rows + 255) / 256)), dim3(256), 0,
-                       s, h, p.nsplit);
-    return hipGetLastError();
+    return launch_merge_h3(h, p.nsplit, s);
 }
 
 }  // namespace otsk

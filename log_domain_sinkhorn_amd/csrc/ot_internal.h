@@ -151,6 +151,19 @@ hipError_t launch_plan_stats_h3(int kp, const void *xrow, const void *xcol, cons
                                 int64_t m_pad, double scale, double *cost, double *marg,
                                 double *scratch, hipStream_t s);
 hipError_t launch_half_step_h3(const HalfStep &h, int kp, hipStream_t s);
+// Merge of the column splits' (max, sum) partials of a split-f16 half-step.
+hipError_t launch_merge_h3(const HalfStep &h, int nsplit, hipStream_t s);
+// The same half-step and statistics pass for kp in {224, 256, 320, 384, 448,
+// 512} on 16x16 matrix-core tiles (lse_wide.hip); the h3 entry points above
+// dispatch to them for kp > 192.
+bool wide_kp(int kp);
+size_t half_step_partials_wide(int64_t rows, int64_t cols_pad, int kp);
+hipError_t launch_half_step_wide(const HalfStep &h, int kp, hipStream_t s);
+int plan_pass_wide_splits(int64_t rows, int64_t cols_pad, int kp);
+hipError_t launch_plan_pass_wide(int kp, bool cost, const void *row_rec, const float *row_hat,
+                                 const float *row_nrm, const void *col_rec, const float *col_hat,
+                                 const float *col_nrm, int64_t rows, int64_t rows_pad,
+                                 int64_t cols_pad, double scale, double2 *part, hipStream_t s);
 
 // Cosine cost: normalised copies of the points, scaled potentials.
 hipError_t launch_normalize(const float *pts, int64_t count, int d, float *out, hipStream_t s);
