@@ -76,10 +76,6 @@ typedef enum {
  * (half the row-operand registers per lane). */
 #define OT_MAX_DIM 512
 
-/* Largest d of the transport calls (ot_transport_apply, ot_barycentric_map,
- * ot_cost_gradient_x); above it they return OT_ERROR_NOT_SUPPORTED. */
-#define OT_MAX_TRANSPORT_DIM 192
-
 /* Human-readable name of a status code (static string, never NULL). */
 const char *ot_status_string(ot_status s);
 

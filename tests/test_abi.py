@@ -41,7 +41,6 @@ def test_header_max_dim_matches_binding():
     text = open(lds._HEADER).read()
     assert f"#define OT_MAX_DIM {lds.OT_MAX_DIM}" in text
     assert f"#define OT_MAX_VALUE_DIM {lds.OT_MAX_VALUE_DIM}" in text
-    assert f"#define OT_MAX_TRANSPORT_DIM {lds.OT_MAX_TRANSPORT_DIM}" in text
     assert "#define OT_NO_ALLOC_SCRATCH_BYTES (128ull << 20)" in text
     assert lds.OT_NO_ALLOC_SCRATCH_BYTES == 128 << 20
 
@@ -133,7 +132,6 @@ def test_transport_apply_rejects_invalid(lib):
                dict(out=X), dict(out=V + 8), dict(out=F - 16)]:
         assert call(**kw) == INVALID, kw
     assert call(d=lds.OT_MAX_DIM + 1) == UNSUPPORTED
-    assert call(d=lds.OT_MAX_TRANSPORT_DIM + 1) == UNSUPPORTED
     assert call(dv=lds.OT_MAX_VALUE_DIM + 1) == UNSUPPORTED
     assert call(dv=lds.OT_MAX_VALUE_DIM + 1, eps=-1.0) == INVALID
 
@@ -145,12 +143,10 @@ def test_map_and_gradient_reject_invalid(lib):
     assert bm(X, Y, A, F, G, 10, 12, 3, 0.1, A, None) == INVALID           # out aliases a
     assert bm(X, Y, A, F, G, 0, 12, 3, 0.1, OUT, None) == INVALID
     assert bm(X, Y, A, F, G, 10, 12, lds.OT_MAX_DIM + 1, 0.1, OUT, None) == UNSUPPORTED
-    assert bm(X, Y, A, F, G, 10, 12, lds.OT_MAX_TRANSPORT_DIM + 1, 0.1, OUT, None) == UNSUPPORTED
     assert gx(X, Y, None, G, 10, 12, 3, 0.1, OUT, None) == INVALID
     assert gx(X, Y, F, G, 10, 12, 3, 0.1, Y + 4, None) == INVALID          # out overlaps y
     assert gx(X, Y, F, G, 10, 12, 3, -0.1, OUT, None) == INVALID
     assert gx(X, Y, F, G, 10, 12, lds.OT_MAX_DIM + 1, 0.1, OUT, None) == UNSUPPORTED
-    assert gx(X, Y, F, G, 10, 12, lds.OT_MAX_TRANSPORT_DIM + 1, 0.1, OUT, None) == UNSUPPORTED
 
 
 def test_birkhoff_rejects_invalid(lib):

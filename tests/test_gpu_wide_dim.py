@@ -12,7 +12,9 @@ Transport on GPU", "Experimentelle Ergebnisse"); the update is the one of
   and at the feature workload's distributions at d = 256, the eps schedule,
   plan statistics on identical inputs, bitwise determinism;
 * at 65536 x 65536 x 256, one half-step from the GPU's own iterate on sampled
-  rows (the size the benchmark measures at d = 256).
+  rows (the size the benchmark measures at d = 256);
+* the transport application, barycentric map and x-gradient ("Methodik"
+  section 3) on the same tiles, P.V on 16x16x32 bf16 matrix cores.
 """
 import numpy as np
 import pytest
@@ -149,12 +151,49 @@ def test_wide_full_size_sampled_half_steps():
     assert err <= TOL_HALF
 
 
-def test_wide_transport_not_supported():
-    c = random_clouds(100, 120, 256, seed=1)
+TOL_APPLY = 5e-5  # the transport tests' bound (see test_gpu_transport.py)
+
+
+def _apply(c, f, g, eps, v):
     x, y = dev(c["x"]), dev(c["y"])
-    f = torch.zeros(100, device=DEV)
-    g = torch.zeros(120, device=DEV)
-    out = torch.zeros(100, 256, device=DEV)
-    with pytest.raises(lds.OTError) as e:
-        lds.ot_transport_apply(x, y, f, g, 0.5, y, out)
-    assert e.value.status == lds.OT_ERROR_NOT_SUPPORTED
+    out = torch.empty((x.shape[0], v.shape[1]), dtype=torch.float32, device=DEV)
+    lds.ot_transport_apply(x, y, dev(f), dev(g), eps, dev(v), out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("n,m,d,dv", [(700, 900, 224, 224), (1000, 700, 256, 5),
+                                      (300, 1300, 384, 40), (500, 600, 512, 512),
+                                      (1, 300, 256, 33), (257, 1, 320, 64)])
+def test_wide_transport_apply(n, m, d, dv):
+    # out_i = sum_j P_ij v_j on 16x16 tiles; oracle potentials, random values.
+    from workloads import random_values
+    c = random_clouds(n, m, d, seed=n + m + d, spread=1.0 / np.sqrt(d))
+    eps = 0.3
+    print(f"transport {n}x{m}x{d}, dv={dv}", flush=True)
+    fo, go = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, 8)
+    f, g = fo.astype(np.float32), go.astype(np.float32)
+    v = random_values(m, dv, seed=d)
+    out = _apply(c, f, g, eps, v)
+    ref = oracle.transport_apply(c["x"], c["y"], f, g, eps, v)
+    err = rel_inf(out, ref)
+    print(f"  rel err {err:.2e}", flush=True)
+    assert err <= TOL_APPLY
+
+
+def test_wide_map_and_gradient_d256():
+    c = make_clouds("feature64_64k", n=900, m=1100, d=256)
+    eps = c["eps"][0]
+    print("barycentric map and x-gradient at d=256", flush=True)
+    fo, go = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, 20)
+    f, g = fo.astype(np.float32), go.astype(np.float32)
+    x, y, a = dev(c["x"]), dev(c["y"]), dev(c["a"])
+    bary = torch.empty_like(x)
+    grad = torch.empty_like(x)
+    lds.ot_barycentric_map(x, y, a, dev(f), dev(g), eps, bary)
+    lds.ot_cost_gradient_x(x, y, dev(f), dev(g), eps, grad)
+    torch.cuda.synchronize()
+    eb = rel_inf(bary.cpu().numpy(), oracle.barycentric_map(c["x"], c["y"], c["a"], f, g, eps))
+    eg = rel_inf(grad.cpu().numpy(), oracle.grad_x(c["x"], c["y"], f, g, eps))
+    print(f"  map rel err {eb:.2e}, gradient rel err {eg:.2e}", flush=True)
+    assert eb <= TOL_APPLY and eg <= TOL_APPLY
