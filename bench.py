@@ -568,7 +568,7 @@ def main():
         sec = {}
         wanted = None if args.secondary_only is None else set(args.secondary_only.split(","))
         for name in ("cube_gauss3d_64k", "cube_gauss3d_16k", "mixture_sphere3d_eps_scaling",
-                     "feature192_64k"):
+                     "feature192_64k", "feature256_64k"):
             if name == args.workload or (wanted is not None and name not in wanted):
                 continue
             print(f"# secondary {name}", file=sys.stderr, flush=True)

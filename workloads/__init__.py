@@ -112,12 +112,20 @@ CLOUD_WORKLOADS: Dict[str, CloudWorkload] = {
             "y uniform on the unit sphere, uniform weights, eps 1.0 -> 0.01 over 8 geometric "
             "stages, 50 iterations per stage, warm start",
         ),
-        # The feature workload's distributions at d=192, the largest feature
-        # dimension the point-cloud calls take.
+        # The feature workload's distributions at d=192, the largest on the
+        # 32x32-tile kernels.
         CloudWorkload(
             "feature192_64k", 65536, 65536, 192, (0.5,), 100,
             "normal(0, I/192)", "normal(0, I/192) + 0.3*u", "dirichlet",
             "n=m=65536, d=192, x,y~N(0,I/192), y shifted by 0.3 along a random unit vector, "
+            "Dirichlet(1) weights, eps=0.5, 100 iterations",
+        ),
+        # The feature workload's distributions at d=256, on the 16x16-tile
+        # kernels of wide feature dimensions.
+        CloudWorkload(
+            "feature256_64k", 65536, 65536, 256, (0.5,), 100,
+            "normal(0, I/256)", "normal(0, I/256) + 0.3*u", "dirichlet",
+            "n=m=65536, d=256, x,y~N(0,I/256), y shifted by 0.3 along a random unit vector, "
             "Dirichlet(1) weights, eps=0.5, 100 iterations",
         ),
         # Same distributions as cube_gauss3d_16k at n=m=65536: the d=3 point at the
@@ -195,7 +203,7 @@ def make_clouds(name: str, seed: int = 0, n: Optional[int] = None, m: Optional[i
     elif name in ("cube_gauss3d_16k", "cube_gauss3d_64k"):
         x = rng.uniform(0.0, 1.0, size=(n, d))
         y = rng.normal(0.5, 0.1, size=(m, d))
-    elif name in ("feature64_64k", "feature192_64k"):
+    elif name in ("feature64_64k", "feature192_64k", "feature256_64k"):
         x = rng.normal(0.0, 1.0 / math.sqrt(d), size=(n, d))
         y = rng.normal(0.0, 1.0 / math.sqrt(d), size=(m, d))
         z = rng.normal(size=d)
