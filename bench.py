@@ -63,8 +63,6 @@ BIRKHOFF_EXP2, BIRKHOFF_LOG2, BIRKHOFF_OTHER = 24, 8, 100
 NEWTON_VALU_PER_MATRIX, NEWTON_TRANS_PER_MATRIX, NEWTON_STEPS = 7363.0, 755.0, 5.37
 HBM_PEAK_BYTES_PER_S = 8.0e12
 
-HALF_STEP_KERNELS = ("lse_rows_h3_kernel", "lse_rows_valu_kernel")
-
 
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -270,8 +268,9 @@ def run_cloud_workload(name, steps, warmup, torch, lds, with_stats=True):
 
 
 def h3_kp(d: int) -> int:
-    """Coordinates per record of the split-f16 half-step (d padded to 32k)."""
-    return (d + 31) // 32 * 32
+    """Coordinates per record of the split-f16 half-step: d padded to a
+    multiple of 32 up to 256, of 64 above."""
+    return (d + 31) // 32 * 32 if d <= 256 else (d + 63) // 64 * 64
 
 
 def roofline_for(r, workload, rates):
@@ -285,26 +284,31 @@ def roofline_for(r, workload, rates):
         # three split f16 products), so the peak is the f16 dense peak; the
         # method's work is 2d flops per pair-side.
         kp = h3_kp(d)
+        wide = kp > 192
         work = 2.0 * d * n * m
         ach = work / launch_s / 1e12
         # Implementation model, beside it: the kernel issues 6*kp f16 MFMA
-        # flops (three split products over kp = 32*ceil(d/32) coordinates)
-        # and 4 fp32 MFMA flops (column bias and row offset) per pair-side on
-        # the one matrix pipe, one after the other; at the published peaks
-        # that is kp*6/2500 + 4/157.3 ps per pair-side (448 cycles per 32x32
-        # subtile-wave at d = 64). Its ceiling on the method's rate is
-        # 2d / (6 kp + 4 * 2500/157.3).
-        impl_flops = 6.0 * kp + 4.0 * PEAK_MFMA_FP16_TFLOPS / PEAK_MFMA_FP32_TFLOPS
+        # flops (three split products over the kp padded coordinates) and
+        # fp32 MFMA flops for the column bias and row offset per pair-side on
+        # the one matrix pipe, one after the other: 4 on 32x32 tiles (d <=
+        # 192; 448 cycles per 32x32 subtile-wave at d = 64), 8 on the 16x16
+        # tiles of wider d (the 16x16x4 instruction's four k-slots, two
+        # used). At the published peaks its ceiling on the method's rate is
+        # 2d / (6 kp + fp32 flops * 2500/157.3).
+        bias_flops = 8.0 if wide else 4.0
+        impl_flops = 6.0 * kp + bias_flops * PEAK_MFMA_FP16_TFLOPS / PEAK_MFMA_FP32_TFLOPS
         impl_ach = impl_flops * n * m / launch_s / 1e12
         return {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_FP16_TFLOPS,
                 "unit": "TFLOP/s", "frac": ach / PEAK_MFMA_FP16_TFLOPS,
-                "traffic": traffic_for("lse_rows_h3_kernel", workload),
-                "kernel": f"lse_rows_h3_kernel<{kp}>", "launch_ms": r["half_step_ms"],
+                "traffic": traffic_for("lse_rows_wide_kernel" if wide else "lse_rows_h3_kernel",
+                                       workload),
+                "kernel": f"lse_rows_{'wide' if wide else 'h3'}_kernel<{kp}>",
+                "launch_ms": r["half_step_ms"],
                 "work_per_launch": f"{n}*{m} pair-sides x {2 * d} flops (the dot product, 2d)",
                 "peak_dtype": "f16 (dense matrix cores; the fp32 dot products are formed as "
                               "three split f16 products with fp32 accumulation)",
                 "implementation_model": {
-                    "matrix_flops_per_pair_side": f"{6 * kp} f16 + 4 fp32 MFMA",
+                    "matrix_flops_per_pair_side": f"{6 * kp} f16 + {bias_flops:.0f} fp32 MFMA",
                     "f16_equivalent_per_pair_side": impl_flops,
                     "achieved_f16_equivalent_tflops": impl_ach,
                     "frac_of_f16_peak": impl_ach / PEAK_MFMA_FP16_TFLOPS,
