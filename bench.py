@@ -77,11 +77,16 @@ def parse():
     return p.parse_args()
 
 
+# f16 MFMA stream with data-carrying operands (random mantissas that change
+# every step) over ~0.2 s: under it the board lowers its clock (power), so
+# this is the f16 matrix rate a long product can sustain, below the
+# published peak, which assumes 2.4 GHz.
+SUSTAINED_F16 = "v_mfma_f32_32x32x16_f16 sustained, random operands"
 RATE_KINDS = {  # kind -> (name, chain steps per lane); see ratebench/rates.hip
     0: ("v_fma_f32", 20000), 1: ("v_exp_f32", 20000), 2: ("v_log_f32 + v_add_f32", 10000),
     3: ("v_exp_f32 beside v_fma_f32", 10000), 4: ("v_fma_f64", 10000),
     5: ("v_mfma_f32_32x32x16_f16", 12000), 6: ("v_mfma_f32_32x32x2f32", 4000),
-    7: ("v_add_f32", 20000)}
+    7: ("v_add_f32", 20000), 8: (SUSTAINED_F16, 300000)}
 
 
 def measure_rates():
@@ -313,6 +318,10 @@ def roofline_for(r, workload, rates):
                     "achieved_f16_equivalent_tflops": impl_ach,
                     "frac_of_f16_peak": impl_ach / PEAK_MFMA_FP16_TFLOPS,
                     "ceiling_on_frac": 2.0 * d / impl_flops},
+                "vs_sustained_f16_mfma": {
+                    "sustained_tflops": rates["mfma_tflops"][SUSTAINED_F16],
+                    "shader_clock_ghz": rates["shader_clock_ghz"][SUSTAINED_F16],
+                    "implementation_frac": impl_ach / rates["mfma_tflops"][SUSTAINED_F16]},
                 "vs_fp32_mfma_peak": {"fp32_equivalent_tflops": ach,
                                       "peak": PEAK_MFMA_FP32_TFLOPS,
                                       "ratio": ach / PEAK_MFMA_FP32_TFLOPS}}

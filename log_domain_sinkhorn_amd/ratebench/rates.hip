@@ -16,6 +16,11 @@
 //   5  v_mfma_f32_32x32x16_f16   f16 matrix-core flops (4 accumulators)
 //   6  v_mfma_f32_32x32x2f32     fp32 matrix-core flops (4 accumulators)
 //   7  v_add_f32                 v = v + c
+//   8  v_mfma_f32_32x32x16_f16   as 5, but with operands of random f16
+//                                mantissas in +-[1, 2) whose bits change every
+//                                step, run long enough (~0.4 s) for the board's
+//                                power management to settle: the matrix-core
+//                                rate a data-carrying f16 product sustains
 // Lane 0 of every workgroup also reads the shader-clock counter and the
 // constant-rate wall counter when it starts and ends, so the average shader
 // clock under each stream is known and the rates can be put per clock.
@@ -30,6 +35,7 @@ constexpr int kThreads = 256;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // Clock readings of lane 0 of a workgroup: (shader cycles, wall ticks).
 __device__ __forceinline__ void clock_mark(long long *clk, int slot) {
@@ -96,11 +102,28 @@ __global__ __launch_bounds__(kThreads) void mfma_rate_kernel(int iters, float *o
         ah[r] = (_Float16)(0.001f * (float)((tid + r) & 7));
         bh[r] = (_Float16)(0.002f * (float)((tid + 2 * r) & 7));
     }
+    // KIND 8: xorshift32 bits with the exponent fixed (halves in +-[1, 2)).
+    u32x4 ua, ub;
+    unsigned x = (unsigned)tid * 2654435761u + 12345u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        x ^= x << 13; x ^= x >> 17; x ^= x << 5;
+        ua[r] = (x & 0x83FF83FFu) | 0x3C003C00u;
+        x ^= x << 13; x ^= x >> 17; x ^= x << 5;
+        ub[r] = (x & 0x83FF83FFu) | 0x3C003C00u;
+    }
     const float af = 0.001f * (float)(tid & 7), bf = 0.002f * (float)(tid & 3);
     for (int i = 0; i < iters; ++i) {
+        if (KIND == 8) {
+            const unsigned flip = (0x02AB02ABu * (unsigned)((i & 7) + 1)) & 0x03FF03FFu;
+            ua ^= flip;
+            ub ^= flip >> 1;
+            ah = __builtin_bit_cast(half8, ua);
+            bh = __builtin_bit_cast(half8, ub);
+        }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            if (KIND == 5)
+            if (KIND == 5 || KIND == 8)
                 acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, acc[c], 0, 0, 0);
             else
                 acc[c] = __builtin_amdgcn_mfma_f32_32x32x2f32(af, bf, acc[c], 0, 0, 0);
@@ -124,7 +147,7 @@ extern "C" {
 // operations per second to *rate and the average shader clock of the
 // workgroups (Hz) to *clock_hz. Returns 0 or the HIP error code.
 int otr_measure(int kind, int iters, double *rate, double *clock_hz) {
-    if (kind < 0 || kind > 7 || iters < 1 || !rate || !clock_hz)
+    if (kind < 0 || kind > 8 || iters < 1 || !rate || !clock_hz)
         return (int)hipErrorInvalidValue;
     int dev = 0, wall_khz = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -156,6 +179,7 @@ int otr_measure(int kind, int iters, double *rate, double *clock_hz) {
         case 4: hipLaunchKernelGGL(valu_rate_kernel<4>, g, b, 0, nullptr, iters, out, clk); break;
         case 5: hipLaunchKernelGGL(mfma_rate_kernel<5>, g, b, 0, nullptr, iters, out, clk); break;
         case 6: hipLaunchKernelGGL(mfma_rate_kernel<6>, g, b, 0, nullptr, iters, out, clk); break;
+        case 8: hipLaunchKernelGGL(mfma_rate_kernel<8>, g, b, 0, nullptr, iters, out, clk); break;
         default: hipLaunchKernelGGL(valu_rate_kernel<7>, g, b, 0, nullptr, iters, out, clk); break;
         }
         e = hipGetLastError();
@@ -188,7 +212,7 @@ int otr_measure(int kind, int iters, double *rate, double *clock_hz) {
     if (kind <= 4 || kind == 7)
         ops = lanes * iters * kChains * (kind == 3 ? 2.0 : 1.0);
     else  // per wave and instruction: 32*32*16*2 (f16) or 32*32*2*2 (fp32) flops
-        ops = (lanes / 64.0) * iters * 4.0 * (kind == 5 ? 32768.0 : 4096.0);
+        ops = (lanes / 64.0) * iters * 4.0 * (kind == 6 ? 4096.0 : 32768.0);
     *rate = ops / (ms / 1e3);
     return 0;
 }
