@@ -50,7 +50,7 @@ def _replays_match(run, outputs, reset):
     print(f"{REPLAYS} replays identical to the eager call", flush=True)
 
 
-@pytest.mark.parametrize("d", [3, 64])
+@pytest.mark.parametrize("d", [3, 64, 256])
 def test_solve_and_plan_stats_capture(d):
     c = random_clouds(1500, 1100, d, seed=d)
     x, y, a, b = dev(c["x"]), dev(c["y"]), dev(c["a"]), dev(c["b"])
@@ -71,7 +71,7 @@ def test_solve_and_plan_stats_capture(d):
     _replays_match(run, [f, g, cost, marg], reset)
 
 
-@pytest.mark.parametrize("d", [3, 64])
+@pytest.mark.parametrize("d", [3, 64, 256])
 def test_transport_capture(d):
     c = random_clouds(700, 900, d, seed=10 + d, spread=1.0 / np.sqrt(d))
     x, y = dev(c["x"]), dev(c["y"])
