@@ -73,8 +73,14 @@ typedef enum {
 
 /* Largest feature dimension d the point-cloud calls accept: up to 192 the
  * matrix-core kernels work on 32x32 tiles, from 193 to 512 on 16x16 tiles
- * (half the row-operand registers per lane). */
-#define OT_MAX_DIM 512
+ * (half the row-operand registers per lane), from 513 to 1024 on 16x16 tiles
+ * with each row's coordinates split in quarters over four waves. */
+#define OT_MAX_DIM 1024
+
+/* Largest d of the transport calls (ot_transport_apply, ot_barycentric_map,
+ * ot_cost_gradient_x); from OT_MAX_TRANSPORT_DIM + 1 to OT_MAX_DIM they return
+ * NOT_SUPPORTED. */
+#define OT_MAX_TRANSPORT_DIM 512
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *ot_status_string(ot_status s);
@@ -199,8 +205,8 @@ ot_status ot_marginal_error(const float *x, const float *y, const float *a,
  * Other arguments as ot_plan_stats. Terms of P are formed in fp64 and
  * exponentiated in fp32; sums over j are fp64 in a fixed order.
  * Errors: INVALID_VALUE (null pointer, sizes < 1, bad eps, overlap),
- * NOT_SUPPORTED (d > OT_MAX_DIM, dv > OT_MAX_VALUE_DIM), OUT_OF_MEMORY,
- * LAUNCH_FAILURE.
+ * NOT_SUPPORTED (d > OT_MAX_TRANSPORT_DIM, dv > OT_MAX_VALUE_DIM),
+ * OUT_OF_MEMORY, LAUNCH_FAILURE.
  */
 ot_status ot_transport_apply(const float *x, const float *y, const float *f,
                              const float *g, int64_t n, int64_t m, int32_t d,
@@ -210,7 +216,8 @@ ot_status ot_transport_apply(const float *x, const float *y, const float *f,
 /*
  * ot_barycentric_map -- out_i = sum_j P_ij y_j / a_i (n*d): the barycentric
  * projection of each source point under the plan (page "FlashSinkhorn ...",
- * "Methodik" section 3). a [n] are the source weights (> 0).
+ * "Methodik" section 3). a [n] are the source weights (> 0). d is limited to
+ * OT_MAX_TRANSPORT_DIM, as for ot_transport_apply.
  */
 ot_status ot_barycentric_map(const float *x, const float *y, const float *a,
                              const float *f, const float *g, int64_t n,
@@ -222,7 +229,8 @@ ot_status ot_barycentric_map(const float *x, const float *y, const float *a,
  * sum_ij P_ij C_ij with respect to x_i at the fixed plan of (f, g); at the
  * optimal potentials this is the gradient of the entropic OT cost with
  * respect to the source points (envelope theorem; page "FlashSinkhorn ...",
- * "Methodik" section 3, gradients as weighted averages).
+ * "Methodik" section 3, gradients as weighted averages). d is limited to
+ * OT_MAX_TRANSPORT_DIM.
  */
 ot_status ot_cost_gradient_x(const float *x, const float *y, const float *f,
                              const float *g, int64_t n, int64_t m, int32_t d,

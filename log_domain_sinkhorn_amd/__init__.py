@@ -42,6 +42,7 @@ __all__ = [
     "ot_birkhoff_project_newton_batched",
     "ot_birkhoff_projection_backward_batched",
     "OT_MAX_DIM",
+    "OT_MAX_TRANSPORT_DIM",
     "OT_MAX_VALUE_DIM",
 ]
 
@@ -55,7 +56,8 @@ OT_ERROR_INVALID_VALUE = 1
 OT_ERROR_NOT_SUPPORTED = 2
 OT_ERROR_OUT_OF_MEMORY = 3
 OT_ERROR_LAUNCH_FAILURE = 4
-OT_MAX_DIM = 512
+OT_MAX_DIM = 1024
+OT_MAX_TRANSPORT_DIM = 512
 OT_MAX_VALUE_DIM = 1024
 OT_NO_ALLOC_SCRATCH_BYTES = 128 << 20
 

@@ -586,7 +586,7 @@ ot_status ot_transport_apply(const float *x, const float *y, const float *f, con
     }
     if (st == OT_SUCCESS)
         st = check_supported(n, m, d);
-    if (st == OT_SUCCESS && dv > OT_MAX_VALUE_DIM)
+    if (st == OT_SUCCESS && (d > OT_MAX_TRANSPORT_DIM || dv > OT_MAX_VALUE_DIM))
         st = OT_ERROR_NOT_SUPPORTED;
     if (st != OT_SUCCESS)
         return st;
@@ -629,6 +629,8 @@ ot_status map_or_grad(const float *x, const float *y, const float *a, const floa
     }
     if (st == OT_SUCCESS)
         st = check_supported(n, m, d);
+    if (st == OT_SUCCESS && d > OT_MAX_TRANSPORT_DIM)
+        st = OT_ERROR_NOT_SUPPORTED;
     if (st != OT_SUCCESS)
         return st;
     hipStream_t s = (hipStream_t)stream;

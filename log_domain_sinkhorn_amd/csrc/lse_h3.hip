@@ -503,8 +503,14 @@ constexpr int kCenterBlocks = 256;
 }  // namespace
 
 // Coordinates per record: 32k up to 192 (the 32x32 kernels); above, the
-// wide kernels' sizes 224, 256, 320, 384, 448, 512.
-int h3_kp(int d) { return d <= 256 ? (d + 31) / 32 * 32 : (d + 63) / 64 * 64; }
+// 16x16-tile kernels' sizes 224, 256, 320, 384, 448; above 448 the quarter-
+// split kernels' 512, 640, 768, 896, 1024 (at 512 those measured 18.5 ms
+// per 65536^2 half-step against 22.6 ms for the 16x16 kernel, which spills).
+int h3_kp(int d) {
+    if (d <= 256)
+        return (d + 31) / 32 * 32;
+    return d <= 448 ? (d + 63) / 64 * 64 : (d + 127) / 128 * 128;
+}
 
 size_t h3_maxabs_floats() { return 2 * kMaxabsBlocks + 2; }
 
@@ -514,7 +520,7 @@ size_t h3_center_scratch_bytes(int d) {
 
 hipError_t launch_center_maxabs(const float *x, int64_t n, const float *y, int64_t m, int d,
                                 void *center_scratch, float *scratch, hipStream_t s) {
-    if (d < 1 || d > 512)
+    if (d < 1 || d > 1024)
         return hipErrorInvalidValue;
     double *part = static_cast<double *>(center_scratch);
     float *center = reinterpret_cast<float *>(part + (size_t)2 * kCenterBlocks * d);
@@ -550,6 +556,8 @@ hipError_t launch_prep_h3(const float *pts, const float *pot, int64_t count, int
 }
 
 int plan_pass_h3_splits(int64_t rows, int64_t cols_pad, int kp) {
+    if (kp > 448)
+        return plan_pass_ksplit_splits(rows, cols_pad, kp);
     if (kp > 192)
         return plan_pass_wide_splits(rows, cols_pad, kp);
     return plan_h3(rows, cols_pad, kp).nsplit;
@@ -559,6 +567,9 @@ hipError_t launch_plan_pass_h3(int kp, bool cost, const void *row_rec, const flo
                                const float *row_nrm, const void *col_rec, const float *col_hat,
                                const float *col_nrm, int64_t rows, int64_t rows_pad,
                                int64_t cols_pad, double scale, double2 *part, hipStream_t s) {
+    if (kp > 448)
+        return launch_plan_pass_ksplit(kp, cost, row_rec, row_hat, row_nrm, col_rec, col_hat,
+                                       col_nrm, rows, rows_pad, cols_pad, scale, part, s);
     if (kp > 192)
         return launch_plan_pass_wide(kp, cost, row_rec, row_hat, row_nrm, col_rec, col_hat,
                                      col_nrm, rows, rows_pad, cols_pad, scale, part, s);
@@ -593,6 +604,8 @@ hipError_t launch_plan_pass_h3(int kp, bool cost, const void *row_rec, const flo
 }
 
 size_t half_step_partials_h3(int64_t rows, int64_t cols_pad, int kp) {
+    if (kp > 448)
+        return half_step_partials_ksplit(rows, cols_pad, kp);
     if (kp > 192)
         return half_step_partials_wide(rows, cols_pad, kp);
     const H3Plan p = plan_h3(rows, cols_pad, kp);
@@ -606,6 +619,8 @@ hipError_t launch_merge_h3(const HalfStep &h, int nsplit, hipStream_t s) {
 }
 
 hipError_t launch_half_step_h3(const HalfStep &h, int kp, hipStream_t s) {
+    if (kp > 448)
+        return launch_half_step_ksplit(h, kp, s);
     if (kp > 192)
         return launch_half_step_wide(h, kp, s);
     const H3Plan p = plan_h3(h.rows, h.cols_pad, kp);

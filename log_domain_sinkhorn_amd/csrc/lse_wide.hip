@@ -1,5 +1,5 @@
 // Log-domain Sinkhorn half-step and plan-statistics pass for wide feature
-// dimensions, 192 < d <= 512 (the pages measure up to d = 1024, "FlashSinkhorn:
+// dimensions, 192 < d <= 448 (the pages measure up to d = 1024, "FlashSinkhorn:
 // IO-Aware Entropic Optimal Transport on GPU", "Experimentelle Ergebnisse").
 //
 // The update is the one of the other half-step kernels ("Methodik" sections
@@ -10,7 +10,7 @@
 // 32x32 kernels hold a row's hi and lo operands in KP/2 registers per lane,
 // which spill above KP = 192. Here every wave owns 16 rows and runs
 // v_mfma_f32_16x16x32_f16, whose stationary operand takes KP/4 registers per
-// lane (128 at KP = 512): lane l holds row i = l % 16 and the 8-coordinate
+// lane (112 at KP = 448): lane l holds row i = l % 16 and the 8-coordinate
 // group g = l / 16 of every 32-coordinate k-step; the accumulator holds
 // D[j][i] for the 4 columns j = 4g + r of the lane's 16-column subtile, so
 // a row's running maximum and sum are shared by the 4 lane groups (lanes l,
@@ -358,9 +358,7 @@ hipError_t launch_wide_kp(const HalfStep &h, const WPlan &p, hipStream_t s) {
 
 }  // namespace
 
-bool wide_kp(int kp) {
-    return kp == 224 || kp == 256 || kp == 320 || kp == 384 || kp == 448 || kp == 512;
-}
+bool wide_kp(int kp) { return kp == 224 || kp == 256 || kp == 320 || kp == 384 || kp == 448; }
 
 size_t half_step_partials_wide(int64_t rows, int64_t cols_pad, int kp) {
     const WPlan p = plan_wide(rows, cols_pad, kp);
@@ -376,7 +374,6 @@ hipError_t launch_half_step_wide(const HalfStep &h, int kp, hipStream_t s) {
     case 320: e = launch_wide_kp<320>(h, p, s); break;
     case 384: e = launch_wide_kp<384>(h, p, s); break;
     case 448: e = launch_wide_kp<448>(h, p, s); break;
-    case 512: e = launch_wide_kp<512>(h, p, s); break;
     default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess || p.nsplit <= 1)
@@ -414,7 +411,6 @@ hipError_t launch_plan_pass_wide(int kp, bool cost, const void *row_rec, const f
         OTSK_PW(320)
         OTSK_PW(384)
         OTSK_PW(448)
-        OTSK_PW(512)
     default:
         return hipErrorInvalidValue;
     }

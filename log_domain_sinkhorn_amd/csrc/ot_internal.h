@@ -153,9 +153,9 @@ hipError_t launch_plan_stats_h3(int kp, const void *xrow, const void *xcol, cons
 hipError_t launch_half_step_h3(const HalfStep &h, int kp, hipStream_t s);
 // Merge of the column splits' (max, sum) partials of a split-f16 half-step.
 hipError_t launch_merge_h3(const HalfStep &h, int nsplit, hipStream_t s);
-// The same half-step and statistics pass for kp in {224, 256, 320, 384, 448,
-// 512} on 16x16 matrix-core tiles (lse_wide.hip); the h3 entry points above
-// dispatch to them for kp > 192.
+// The same half-step and statistics pass for kp in {224, 256, 320, 384, 448}
+// on 16x16 matrix-core tiles (lse_wide.hip); the h3 entry points above
+// dispatch to them for 192 < kp <= 448.
 bool wide_kp(int kp);
 size_t half_step_partials_wide(int64_t rows, int64_t cols_pad, int kp);
 hipError_t launch_half_step_wide(const HalfStep &h, int kp, hipStream_t s);
@@ -164,6 +164,18 @@ hipError_t launch_plan_pass_wide(int kp, bool cost, const void *row_rec, const f
                                  const float *row_nrm, const void *col_rec, const float *col_hat,
                                  const float *col_nrm, int64_t rows, int64_t rows_pad,
                                  int64_t cols_pad, double scale, double2 *part, hipStream_t s);
+// For kp in {512, 640, 768, 896, 1024} (448 < d <= 1024) the coordinates are
+// split in quarters over four waves per row group (lse_ksplit.hip); the h3
+// entry points dispatch to these for kp > 448.
+bool ksplit_kp(int kp);
+size_t half_step_partials_ksplit(int64_t rows, int64_t cols_pad, int kp);
+hipError_t launch_half_step_ksplit(const HalfStep &h, int kp, hipStream_t s);
+int plan_pass_ksplit_splits(int64_t rows, int64_t cols_pad, int kp);
+hipError_t launch_plan_pass_ksplit(int kp, bool cost, const void *row_rec, const float *row_hat,
+                                   const float *row_nrm, const void *col_rec,
+                                   const float *col_hat, const float *col_nrm, int64_t rows,
+                                   int64_t rows_pad, int64_t cols_pad, double scale,
+                                   double2 *part, hipStream_t s);
 
 // Cosine cost: normalised copies of the points, scaled potentials.
 hipError_t launch_normalize(const float *pts, int64_t count, int d, float *out, hipStream_t s);

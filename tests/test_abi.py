@@ -40,6 +40,7 @@ def test_every_declared_function_is_exported(lib):
 def test_header_max_dim_matches_binding():
     text = open(lds._HEADER).read()
     assert f"#define OT_MAX_DIM {lds.OT_MAX_DIM}" in text
+    assert f"#define OT_MAX_TRANSPORT_DIM {lds.OT_MAX_TRANSPORT_DIM}" in text
     assert f"#define OT_MAX_VALUE_DIM {lds.OT_MAX_VALUE_DIM}" in text
     assert "#define OT_NO_ALLOC_SCRATCH_BYTES (128ull << 20)" in text
     assert lds.OT_NO_ALLOC_SCRATCH_BYTES == 128 << 20
@@ -132,6 +133,7 @@ def test_transport_apply_rejects_invalid(lib):
                dict(out=X), dict(out=V + 8), dict(out=F - 16)]:
         assert call(**kw) == INVALID, kw
     assert call(d=lds.OT_MAX_DIM + 1) == UNSUPPORTED
+    assert call(d=lds.OT_MAX_TRANSPORT_DIM + 1) == UNSUPPORTED
     assert call(dv=lds.OT_MAX_VALUE_DIM + 1) == UNSUPPORTED
     assert call(dv=lds.OT_MAX_VALUE_DIM + 1, eps=-1.0) == INVALID
 
@@ -147,6 +149,9 @@ def test_map_and_gradient_reject_invalid(lib):
     assert gx(X, Y, F, G, 10, 12, 3, 0.1, Y + 4, None) == INVALID          # out overlaps y
     assert gx(X, Y, F, G, 10, 12, 3, -0.1, OUT, None) == INVALID
     assert gx(X, Y, F, G, 10, 12, lds.OT_MAX_DIM + 1, 0.1, OUT, None) == UNSUPPORTED
+    # the solve's range goes past the transport calls' range
+    assert bm(X, Y, A, F, G, 10, 12, lds.OT_MAX_TRANSPORT_DIM + 1, 0.1, OUT, None) == UNSUPPORTED
+    assert gx(X, Y, F, G, 10, 12, lds.OT_MAX_TRANSPORT_DIM + 1, 0.1, OUT, None) == UNSUPPORTED
 
 
 def test_birkhoff_rejects_invalid(lib):
