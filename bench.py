@@ -274,8 +274,16 @@ def run_cloud_workload(name, steps, warmup, torch, lds, with_stats=True):
 
 def h3_kp(d: int) -> int:
     """Coordinates per record of the split-f16 half-step: d padded to a
-    multiple of 32 up to 256, of 64 above."""
-    return (d + 31) // 32 * 32 if d <= 256 else (d + 63) // 64 * 64
+    multiple of 32 up to 256, of 64 up to 448, of 128 above."""
+    if d <= 256:
+        return (d + 31) // 32 * 32
+    return (d + 63) // 64 * 64 if d <= 448 else (d + 127) // 128 * 128
+
+
+def h3_kernel(kp: int) -> str:
+    """The half-step kernel the library runs for kp coordinates per record."""
+    return "lse_rows_h3_kernel" if kp <= 192 else (
+        "lse_rows_wide_kernel" if kp <= 448 else "lse_rows_ksplit_kernel")
 
 
 def roofline_for(r, workload, rates):
@@ -289,7 +297,7 @@ def roofline_for(r, workload, rates):
         # three split f16 products), so the peak is the f16 dense peak; the
         # method's work is 2d flops per pair-side.
         kp = h3_kp(d)
-        wide = kp > 192
+        kernel = h3_kernel(kp)
         work = 2.0 * d * n * m
         ach = work / launch_s / 1e12
         # Implementation model, beside it: the kernel issues 6*kp f16 MFMA
@@ -297,17 +305,17 @@ def roofline_for(r, workload, rates):
         # fp32 MFMA flops for the column bias and row offset per pair-side on
         # the one matrix pipe, one after the other: 4 on 32x32 tiles (d <=
         # 192; 448 cycles per 32x32 subtile-wave at d = 64), 8 on the 16x16
-        # tiles of wider d (the 16x16x4 instruction's four k-slots, two
-        # used). At the published peaks its ceiling on the method's rate is
-        # 2d / (6 kp + fp32 flops * 2500/157.3).
-        bias_flops = 8.0 if wide else 4.0
+        # tiles up to d = 448 (the 16x16x4 instruction's four k-slots, two
+        # used), none above (the quarter-split kernel adds the bias on the
+        # vector ALUs). At the published peaks its ceiling on the method's
+        # rate is 2d / (6 kp + fp32 flops * 2500/157.3).
+        bias_flops = {"lse_rows_h3_kernel": 4.0, "lse_rows_wide_kernel": 8.0}.get(kernel, 0.0)
         impl_flops = 6.0 * kp + bias_flops * PEAK_MFMA_FP16_TFLOPS / PEAK_MFMA_FP32_TFLOPS
         impl_ach = impl_flops * n * m / launch_s / 1e12
         return {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_FP16_TFLOPS,
                 "unit": "TFLOP/s", "frac": ach / PEAK_MFMA_FP16_TFLOPS,
-                "traffic": traffic_for("lse_rows_wide_kernel" if wide else "lse_rows_h3_kernel",
-                                       workload),
-                "kernel": f"lse_rows_{'wide' if wide else 'h3'}_kernel<{kp}>",
+                "traffic": traffic_for(kernel, workload),
+                "kernel": f"{kernel}<{kp}>",
                 "launch_ms": r["half_step_ms"],
                 "work_per_launch": f"{n}*{m} pair-sides x {2 * d} flops (the dot product, 2d)",
                 "peak_dtype": "f16 (dense matrix cores; the fp32 dot products are formed as "
@@ -581,7 +589,7 @@ def main():
         sec = {}
         wanted = None if args.secondary_only is None else set(args.secondary_only.split(","))
         for name in ("cube_gauss3d_64k", "cube_gauss3d_16k", "mixture_sphere3d_eps_scaling",
-                     "feature192_64k", "feature256_64k"):
+                     "feature192_64k", "feature256_64k", "feature1024_50k"):
             if name == args.workload or (wanted is not None and name not in wanted):
                 continue
             print(f"# secondary {name}", file=sys.stderr, flush=True)

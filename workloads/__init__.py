@@ -128,6 +128,17 @@ CLOUD_WORKLOADS: Dict[str, CloudWorkload] = {
             "n=m=65536, d=256, x,y~N(0,I/256), y shifted by 0.3 along a random unit vector, "
             "Dirichlet(1) weights, eps=0.5, 100 iterations",
         ),
+        # The feature distributions at the size and the largest feature dimension
+        # of the pages' dimension sweep (n = 50,000, d up to 1024; "FlashSinkhorn:
+        # IO-Aware Entropic Optimal Transport on GPU", "Experimentelle
+        # Ergebnisse"); the pages fix no iteration count there, 20 is this
+        # workload's.
+        CloudWorkload(
+            "feature1024_50k", 50000, 50000, 1024, (0.5,), 20,
+            "normal(0, I/1024)", "normal(0, I/1024) + 0.3*u", "dirichlet",
+            "n=m=50000, d=1024, x,y~N(0,I/1024), y shifted by 0.3 along a random unit vector, "
+            "Dirichlet(1) weights, eps=0.5, 20 iterations",
+        ),
         # Same distributions as cube_gauss3d_16k at n=m=65536: the d=3 point at the
         # 65536 x 65536 size.
         CloudWorkload(
@@ -203,7 +214,7 @@ def make_clouds(name: str, seed: int = 0, n: Optional[int] = None, m: Optional[i
     elif name in ("cube_gauss3d_16k", "cube_gauss3d_64k"):
         x = rng.uniform(0.0, 1.0, size=(n, d))
         y = rng.normal(0.5, 0.1, size=(m, d))
-    elif name in ("feature64_64k", "feature192_64k", "feature256_64k"):
+    elif name in ("feature64_64k", "feature192_64k", "feature256_64k", "feature1024_50k"):
         x = rng.normal(0.0, 1.0 / math.sqrt(d), size=(n, d))
         y = rng.normal(0.0, 1.0 / math.sqrt(d), size=(m, d))
         z = rng.normal(size=d)
