@@ -13,14 +13,12 @@
 // One matrix per lane, everything in registers, no cross-lane traffic (the
 // page's kernel puts two matrices in a 32-lane warp and exchanges values by
 // shuffles; with one matrix per lane on 64-wide wavefronts there is nothing to
-// exchange). Convergence test, in two stages: after iteration k row i of the
-// plan sums to 2^(f_i + m_i) * s_i, where (m_i, s_i) is the max / shifted sum
-// the next f update needs anyway, so a cheap estimate costs one exp2 per row.
-// Its fp32 rounding grows with the size of the potentials (up to ~1e-5 for
-// N(0, 10^2) logits), so only when the estimate is within that margin of tol
-// is the plan itself formed -- exactly as it will be written -- and its row
-// and column sums tested. The decision is thus taken on the fp32 output, and
-// a matrix that stops is written from the plan already formed.
+// exchange). The kernel carries the log-plan u_ij = f_i + g_j + l_ij instead
+// of the potentials (see birkhoff4_kernel). Convergence test: after iteration
+// k the row sums of the plan 2^u are the sums the next row step forms anyway;
+// only when they are all within tol of 1 are the column sums of the same
+// plan, exactly as it will be written, tested too. The decision is thus taken
+// on the fp32 output, and a matrix that stops is written from those entries.
 #include "ot_internal.h"
 
 #include <math.h>
@@ -36,7 +34,8 @@ __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf
 // s = sum 2^(v-m). The maximum's term is 2^0 = 1 and is not exponentiated:
 // with p = max(v0, v1, v2) the maximum is max(p, v3) and the other three
 // values are min(p, v3), med(v0, v1, v2) and min(v0, v1, v2), so one LSE of 4
-// takes 3 exp2 (24 per iteration instead of 32).
+// takes 3 exp2 (used for the first row step, whose logits may be large, and
+// when a row or column sum underflows).
 __device__ __forceinline__ float lse4_parts(float v0, float v1, float v2, float v3, float &s) {
     const float p = fmaxf(fmaxf(v0, v1), v2);
     const float m = fmaxf(p, v3);
@@ -45,20 +44,6 @@ __device__ __forceinline__ float lse4_parts(float v0, float v1, float v2, float 
     const float o3 = fminf(fminf(v0, v1), v2);
     s = 1.f + (hw_exp2(o1 - m) + (hw_exp2(o2 - m) + hw_exp2(o3 - m)));
     return m;
-}
-
-// Margin of the cheap row-sum estimate (2^-16): beyond the fp32 rounding of
-// f_i + m_i for potentials up to a few hundred log2 units.
-constexpr float kEstimateMargin = 1.52587890625e-05f;
-
-// out_ij = 2^(f_i + g_j + l_ij), the plan as it is written.
-__device__ __forceinline__ void form_plan(const float f[4], const float g[4], const float l[4][4],
-                                          float P[4][4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            P[i][j] = hw_exp2(f[i] + g[j] + l[i][j]);
 }
 
 // Largest deviation of a row sum or a column sum of P from 1.
@@ -73,6 +58,29 @@ __device__ __forceinline__ float plan_error(const float P[4][4]) {
     return e;
 }
 
+// Normaliser of one row or column of the log-plan u (four entries): d with
+// sum 2^(u - d) = 1. After a row or column step every entry is at most 0 and
+// the sums are at most 4, so d = log2 of the plain sum; only when that sum
+// falls below 2^-100 (entries near fp32's underflow, early iterations of
+// extreme logits) is the maximum subtracted first. `e` holds 2^u on entry.
+__device__ __forceinline__ float normaliser4(float u0, float u1, float u2, float u3,
+                                             float e0, float e1, float e2, float e3) {
+    const float s = (e0 + e1) + (e2 + e3);
+    if (s >= 0x1p-100f)
+        return hw_log2(s);
+    float sm;
+    const float m = lse4_parts(u0, u1, u2, u3, sm);
+    return m + hw_log2(sm);
+}
+
+// The iteration on the log-plan u_ij = f_i + g_j + l_ij itself: a row step
+// (the f update) subtracts from row i the base-2 LSE of the row, a column
+// step (the g update) the LSE of the column; the potentials are implicit.
+// This is the alternating update above, term for term: u_ij - LSE_j(u_ij) =
+// f_i' + g_j + l_ij with f_i' = -LSE_j(g_j + l_ij). Carrying u instead of
+// (f, g) saves forming f_i + l_ij for every entry at every step, and after
+// the first (max-subtracted) row step the entries stay <= 0, so the plain
+// sum of 2^u is safe without a maximum (see normaliser4).
 __global__ __launch_bounds__(256) void birkhoff4_kernel(const float *logits, int64_t batch,
                                                         float scale, int max_iters, float tol,
                                                         float *out, int32_t *iters_out) {
@@ -80,52 +88,68 @@ __global__ __launch_bounds__(256) void birkhoff4_kernel(const float *logits, int
     if (bi >= batch)
         return;
     const float4 *src = reinterpret_cast<const float4 *>(logits) + 4 * bi;
-    float l[4][4];
+    float u[4][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const float4 v = src[r];
-        l[r][0] = v.x * scale;
-        l[r][1] = v.y * scale;
-        l[r][2] = v.z * scale;
-        l[r][3] = v.w * scale;
+        u[r][0] = v.x * scale;
+        u[r][1] = v.y * scale;
+        u[r][2] = v.z * scale;
+        u[r][3] = v.w * scale;
     }
-    float f[4] = {0.f, 0.f, 0.f, 0.f};
-    float g[4] = {0.f, 0.f, 0.f, 0.f};
     float P[4][4];
     bool have_plan = false;
     int k = 0;
     if (max_iters > 0) {
         const bool check = tol >= 0.f;
-        float m[4], s[4];
-        // first f update (from g = 0)
+        // first row step (from g = 0), with the maximum subtracted: the
+        // logits may be large
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            m[i] = lse4_parts(l[i][0], l[i][1], l[i][2], l[i][3], s[i]);
-            f[i] = -(m[i] + hw_log2(s[i]));
+            float si;
+            const float mi = lse4_parts(u[i][0], u[i][1], u[i][2], u[i][3], si);
+            const float d = mi + hw_log2(si);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                u[i][j] -= d;
         }
+        float e[4][4];
         for (k = 1;; ++k) {
-            // g update from the current f: iterate k is complete afterwards
+            // column step: iterate k is complete afterwards
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    e[i][j] = hw_exp2(u[i][j]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float sj;
-                const float mj = lse4_parts(f[0] + l[0][j], f[1] + l[1][j], f[2] + l[2][j],
-                                            f[3] + l[3][j], sj);
-                g[j] = -(mj + hw_log2(sj));
+                const float d = normaliser4(u[0][j], u[1][j], u[2][j], u[3][j], e[0][j], e[1][j],
+                                            e[2][j], e[3][j]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    u[i][j] -= d;
             }
             if (k >= max_iters)
                 break;
-            // the next f update's row statistics
+            // the next row step's sums: the row sums of iterate k's plan
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                m[i] = lse4_parts(g[0] + l[i][0], g[1] + l[i][1], g[2] + l[i][2], g[3] + l[i][3],
-                                  s[i]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    e[i][j] = hw_exp2(u[i][j]);
             if (check) {
                 float est = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    est = fmaxf(est, fabsf(hw_exp2(f[i] + m[i]) * s[i] - 1.f));
-                if (est <= tol + kEstimateMargin) {
-                    form_plan(f, g, l, P);
+                    est = fmaxf(est,
+                                fabsf(((e[i][0] + e[i][1]) + (e[i][2] + e[i][3])) - 1.f));
+                if (est <= tol) {
+                    // rows within tol: test the columns of the same plan
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            P[i][j] = e[i][j];
                     if (plan_error(P) <= tol) {
                         have_plan = true;
                         break;
@@ -133,12 +157,22 @@ __global__ __launch_bounds__(256) void birkhoff4_kernel(const float *logits, int
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                f[i] = -(m[i] + hw_log2(s[i]));
+            for (int i = 0; i < 4; ++i) {
+                const float d = normaliser4(u[i][0], u[i][1], u[i][2], u[i][3], e[i][0], e[i][1],
+                                            e[i][2], e[i][3]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    u[i][j] -= d;
+            }
         }
     }
-    if (!have_plan)
-        form_plan(f, g, l, P);
+    if (!have_plan) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                P[i][j] = hw_exp2(u[i][j]);
+    }
     float4 *dst = reinterpret_cast<float4 *>(out) + 4 * bi;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
