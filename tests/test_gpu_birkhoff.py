@@ -97,3 +97,21 @@ def test_eps_other_than_one():
     P, it = gpu_birkhoff(L, 3.0, 30, -1.0)
     Po, _ = oracle.birkhoff4_replay(L, it, 3.0)
     assert np.abs(P - Po).max() <= TOL_P4
+
+
+@pytest.mark.parametrize("eps", [0.2, 0.1])
+def test_small_eps_extreme_logits(eps):
+    # l = L log2(e)/eps reaches hundreds of log2 units: the first row step
+    # subtracts the maximum, and column and row sums that underflow fp32 take
+    # the max-subtracted LSE instead of the plain sum of 2^u. (Below eps ~
+    # 0.05 the fp32 rounding of l itself, ~2^-24 |l|, brings plans of
+    # near-tied assignments to ~1e-5 of the fp64 oracle.)
+    L = make_logits(4096, (1.0, 10.0), seed=21)
+    for max_iters, tol in ((20, -1.0), (200, 1e-6)):
+        P, it = gpu_birkhoff(L, eps, max_iters, tol)
+        assert np.all(np.isfinite(P))
+        Po, _ = oracle.birkhoff4_replay(L, it, eps)
+        err = np.abs(P - Po).max()
+        print(f"eps {eps} max_iters {max_iters} tol {tol:g}: max|P-P*| {err:.2e}, "
+              f"mean iters {it.mean():.1f}", flush=True)
+        assert err <= TOL_P4

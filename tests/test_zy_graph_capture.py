@@ -50,7 +50,7 @@ def _replays_match(run, outputs, reset):
     print(f"{REPLAYS} replays identical to the eager call", flush=True)
 
 
-@pytest.mark.parametrize("d", [3, 64, 256])
+@pytest.mark.parametrize("d", [3, 64, 256, 1024])
 def test_solve_and_plan_stats_capture(d):
     c = random_clouds(1500, 1100, d, seed=d)
     x, y, a, b = dev(c["x"]), dev(c["y"]), dev(c["a"]), dev(c["b"])

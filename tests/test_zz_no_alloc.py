@@ -31,7 +31,7 @@ def _both(c, eps, iters, g0=None):
     return (f1, g1), (f2, g2)
 
 
-@pytest.mark.parametrize("d", [3, 64, 256])
+@pytest.mark.parametrize("d", [3, 64, 256, 1024])
 def test_no_alloc_matches_solve_two_calls(d):
     for call, (n, m) in enumerate([(3000, 2500), (700, 900)]):
         print(f"d={d} call {call}: {n}x{m}", flush=True)
