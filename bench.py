@@ -283,7 +283,7 @@ def h3_kp(d: int) -> int:
 def h3_kernel(kp: int) -> str:
     """The half-step kernel the library runs for kp coordinates per record."""
     return "lse_rows_h3_kernel" if kp <= 192 else (
-        "lse_rows_wide_kernel" if kp <= 448 else "lse_rows_ksplit_kernel")
+        "lse_rows_wide_kernel" if kp <= 448 else "lse_rows_gemm_kernel")
 
 
 def roofline_for(r, workload, rates):
@@ -306,8 +306,8 @@ def roofline_for(r, workload, rates):
         # the one matrix pipe, one after the other: 4 on 32x32 tiles (d <=
         # 192; 448 cycles per 32x32 subtile-wave at d = 64), 8 on the 16x16
         # tiles up to d = 448 (the 16x16x4 instruction's four k-slots, two
-        # used), none above (the quarter-split kernel adds the bias on the
-        # vector ALUs). At the published peaks its ceiling on the method's
+        # used), none above (the kernel tiled like a matrix product adds the
+        # bias on the vector ALUs). At the published peaks its ceiling on the method's
         # rate is 2d / (6 kp + fp32 flops * 2500/157.3).
         bias_flops = {"lse_rows_h3_kernel": 4.0, "lse_rows_wide_kernel": 8.0}.get(kernel, 0.0)
         impl_flops = 6.0 * kp + bias_flops * PEAK_MFMA_FP16_TFLOPS / PEAK_MFMA_FP32_TFLOPS

@@ -557,7 +557,7 @@ hipError_t launch_prep_h3(const float *pts, const float *pot, int64_t count, int
 
 int plan_pass_h3_splits(int64_t rows, int64_t cols_pad, int kp) {
     if (kp > 448)
-        return plan_pass_ksplit_splits(rows, cols_pad, kp);
+        return plan_pass_gemm_splits(rows, cols_pad);
     if (kp > 192)
         return plan_pass_wide_splits(rows, cols_pad, kp);
     return plan_h3(rows, cols_pad, kp).nsplit;
@@ -568,8 +568,8 @@ hipError_t launch_plan_pass_h3(int kp, bool cost, const void *row_rec, const flo
                                const float *col_nrm, int64_t rows, int64_t rows_pad,
                                int64_t cols_pad, double scale, double2 *part, hipStream_t s) {
     if (kp > 448)
-        return launch_plan_pass_ksplit(kp, cost, row_rec, row_hat, row_nrm, col_rec, col_hat,
-                                       col_nrm, rows, rows_pad, cols_pad, scale, part, s);
+        return launch_plan_pass_gemm(kp, cost, row_rec, row_hat, row_nrm, col_rec, col_hat,
+                                     col_nrm, rows, rows_pad, cols_pad, scale, part, s);
     if (kp > 192)
         return launch_plan_pass_wide(kp, cost, row_rec, row_hat, row_nrm, col_rec, col_hat,
                                      col_nrm, rows, rows_pad, cols_pad, scale, part, s);
@@ -605,7 +605,7 @@ hipError_t launch_plan_pass_h3(int kp, bool cost, const void *row_rec, const flo
 
 size_t half_step_partials_h3(int64_t rows, int64_t cols_pad, int kp) {
     if (kp > 448)
-        return half_step_partials_ksplit(rows, cols_pad, kp);
+        return half_step_partials_gemm(rows, cols_pad);
     if (kp > 192)
         return half_step_partials_wide(rows, cols_pad, kp);
     const H3Plan p = plan_h3(rows, cols_pad, kp);
@@ -620,7 +620,7 @@ hipError_t launch_merge_h3(const HalfStep &h, int nsplit, hipStream_t s) {
 
 hipError_t launch_half_step_h3(const HalfStep &h, int kp, hipStream_t s) {
     if (kp > 448)
-        return launch_half_step_ksplit(h, kp, s);
+        return launch_half_step_gemm(h, kp, s);
     if (kp > 192)
         return launch_half_step_wide(h, kp, s);
     const H3Plan p = plan_h3(h.rows, h.cols_pad, kp);

@@ -164,18 +164,17 @@ hipError_t launch_plan_pass_wide(int kp, bool cost, const void *row_rec, const f
                                  const float *row_nrm, const void *col_rec, const float *col_hat,
                                  const float *col_nrm, int64_t rows, int64_t rows_pad,
                                  int64_t cols_pad, double scale, double2 *part, hipStream_t s);
-// For kp in {512, 640, 768, 896, 1024} (448 < d <= 1024) the coordinates are
-// split in quarters over four waves per row group (lse_ksplit.hip); the h3
-// entry points dispatch to these for kp > 448.
-bool ksplit_kp(int kp);
-size_t half_step_partials_ksplit(int64_t rows, int64_t cols_pad, int kp);
-hipError_t launch_half_step_ksplit(const HalfStep &h, int kp, hipStream_t s);
-int plan_pass_ksplit_splits(int64_t rows, int64_t cols_pad, int kp);
-hipError_t launch_plan_pass_ksplit(int kp, bool cost, const void *row_rec, const float *row_hat,
-                                   const float *row_nrm, const void *col_rec,
-                                   const float *col_hat, const float *col_nrm, int64_t rows,
-                                   int64_t rows_pad, int64_t cols_pad, double scale,
-                                   double2 *part, hipStream_t s);
+// For kp in {512, 640, 768, 896, 1024} (448 < d <= 1024) the half-step and
+// the statistics pass are tiled like a matrix product, both sides streamed
+// through LDS in coordinate stages (lse_gemm.hip); the h3 entry points
+// dispatch to these for kp > 448.
+size_t half_step_partials_gemm(int64_t rows, int64_t cols_pad);
+hipError_t launch_half_step_gemm(const HalfStep &h, int kp, hipStream_t s);
+int plan_pass_gemm_splits(int64_t rows, int64_t cols_pad);
+hipError_t launch_plan_pass_gemm(int kp, bool cost, const void *row_rec, const float *row_hat,
+                                 const float *row_nrm, const void *col_rec, const float *col_hat,
+                                 const float *col_nrm, int64_t rows, int64_t rows_pad,
+                                 int64_t cols_pad, double scale, double2 *part, hipStream_t s);
 
 // Cosine cost: normalised copies of the points, scaled potentials.
 hipError_t launch_normalize(const float *pts, int64_t count, int d, float *out, hipStream_t s);

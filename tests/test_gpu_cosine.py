@@ -59,7 +59,7 @@ def test_cosine_solve_and_stats(name, n, m, eps, iters):
 def test_cosine_high_dimension(d):
     # Embedding-sized features: the normalised points go through the
     # 64-column-tile kernels above 128 coordinates, the 16x16-tile kernels
-    # above 192 and the quarter-split kernels above 448.
+    # above 192 and the kernels tiled like a matrix product above 448.
     c = random_clouds(600, 800, d, seed=d, spread=1.0)
     eps, iters = 0.02, 20
     f, g = gpu_solve_cos(c, eps, iters)
