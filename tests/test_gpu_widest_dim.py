@@ -121,6 +121,33 @@ def test_widest_plan_stats(n, m, d, offset):
     assert abs(st["marg_col"] - sk["marg_col"]) <= TOL_MARG
 
 
+def test_widest_grid_rounding():
+    # 2600 and 3000 rows are 11 and 12 blocks of 256: at least 8 but not a
+    # multiple of 8, so the grid rounds the row-block count up to 16 (the
+    # extra workgroups exit at once) and several column splits per row block
+    # run; one half-step each way and the statistics against the oracle.
+    c = random_clouds(2600, 3000, 768, seed=77, spread=1.0)
+    eps = 0.5 * 768 ** 0.5
+    print("2600x3000x768: one half-step each way, then statistics", flush=True)
+    fo, go = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, 3)
+    g32 = go.astype(np.float32)
+    f1, g1 = gpu_solve(c, eps, 1, g0=g32)
+    f_ref = oracle.half_update(c["x"], c["y"], c["a"], g32, eps)
+    g_ref = oracle.half_update(c["y"], c["x"], c["b"], f1, eps)
+    ef, eg = rel_inf(f1, f_ref), rel_inf(g1, g_ref)
+    print(f"  one half-step rel err f {ef:.2e} g {eg:.2e}", flush=True)
+    assert ef <= TOL_HALF and eg <= TOL_HALF
+    f, g = fo.astype(np.float32), go.astype(np.float32)
+    st = gpu_plan_stats(c, f, g, eps)
+    sk = oracle.plan_stats(c["x"], c["y"], c["a"], c["b"], f, g, eps)
+    ec = abs(st["cost"] - sk["cost"]) / abs(sk["cost"])
+    print(f"  cost rel {ec:.1e}; marg {st['marg_row']:.3e}/{st['marg_col']:.3e} vs "
+          f"{sk['marg_row']:.3e}/{sk['marg_col']:.3e}", flush=True)
+    assert ec <= TOL_COST
+    assert abs(st["marg_row"] - sk["marg_row"]) <= TOL_MARG
+    assert abs(st["marg_col"] - sk["marg_col"]) <= TOL_MARG
+
+
 def test_widest_bitwise_deterministic():
     c = random_clouds(2000, 1700, 1024, seed=5, spread=1.0 / 32.0)
     a = gpu_solve(c, 0.4, 5)
