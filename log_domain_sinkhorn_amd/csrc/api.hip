@@ -569,6 +569,10 @@ ot_status ot_marginal_error(const float *x, const float *y, const float *a, cons
     return ot_plan_stats(x, y, a, b, f, g, n, m, d, eps, nullptr, marg, stream);
 }
 
+// The transport kernels read records in the unstaged layout.
+static_assert(OT_MAX_TRANSPORT_DIM <= otsk::kStagedRecordKP,
+              "transport records must stay unstaged");
+
 ot_status ot_transport_apply(const float *x, const float *y, const float *f, const float *g,
                              int64_t n, int64_t m, int32_t d, float eps, const float *v,
                              int32_t dv, float *out, void *stream) {

@@ -84,7 +84,10 @@ __device__ __forceinline__ bool gemm_block(int nmap, int nrb, int nsplit, int &r
 // l of load g serves record 8g + l/8 and position l mod 8. Column records
 // carry the global layout's chunk swizzle (16-byte chunk q of point j at
 // q ^ (j & 15); column blocks start at multiples of 128, so j & 15 is the
-// record's index in the block, mod 16); row records are unswizzled. With
+// record's index in the block, mod 16); row records are unswizzled. Above
+// kStagedRecordKP both sides' records are staged (a stage's 8 chunks side by
+// side at 8s .. 8s + 7, unswizzled), so a record's stage is one 128-byte
+// line. With
 // the last stage of a block, waves 0 and 1 also load the block's 128 column
 // biases behind the stage's records, where the block's epilogue reads them,
 // and with NRM waves 2 and 3 the columns' squared norms after those.
@@ -105,7 +108,7 @@ __device__ __forceinline__ void issue_stage(const float4 *__restrict__ row4,
     for (int k = 0; k < kGRowLoads; ++k) {
         const int g = wave * kGRowLoads + k;
         const int t = lp ^ ((lr ^ g) & 7);
-        const int q = (t < 4 ? 0 : KP / 8) + 4 * s + (t & 3);
+        const int q = KP > kStagedRecordKP ? 8 * s + t : (t < 4 ? 0 : KP / 8) + 4 * s + (t & 3);
         __builtin_amdgcn_global_load_lds(row4 + (row0 + g * 8 + lr) * RC + q,
                                          (lds_void *)(buf + g * 64), 16, 0, 0);
     }
@@ -114,7 +117,8 @@ __device__ __forceinline__ void issue_stage(const float4 *__restrict__ row4,
         const int g = wave * kGColLoads + k;
         const int rl = g * 8 + lr;  // column within the block
         const int t = lp ^ ((lr ^ g) & 7);
-        const int q = (t < 4 ? 0 : KP / 8) + ((4 * s + (t & 3)) ^ (rl & 15));
+        const int q = KP > kStagedRecordKP ? 8 * s + t
+                                           : (t < 4 ? 0 : KP / 8) + ((4 * s + (t & 3)) ^ (rl & 15));
         __builtin_amdgcn_global_load_lds(col4 + (col0 + rl) * RC + q,
                                          (lds_void *)(buf + kGBM * 8 + g * 64), 16, 0, 0);
     }

@@ -312,8 +312,9 @@ __device__ __forceinline__ float4 pack8(const _Float16 (&v)[8]) {
 }
 
 // One side's records at one eps, of the centred points p = x - c: column
-// record (scaled, split, swizzled), row record (split), |p|^2 and the bias
-// (zero, hat of pot, or padding).
+// record (scaled, split, swizzled; staged above kStagedRecordKP), row record
+// (split; staged likewise), |p|^2 and the bias (zero, hat of pot, or
+// padding).
 __global__ __launch_bounds__(256) void prep_h3_kernel(
     const float *__restrict__ pts, const float *__restrict__ pot, const float *__restrict__ center,
     int64_t count, int64_t padded, int d, int kp, double scale, double hat_scale, int bias_mode,
@@ -340,10 +341,18 @@ __global__ __launch_bounds__(256) void prep_h3_kernel(
             ch[r] = split_hi((float)(v * cf), cl[r]);
             rh[r] = split_hi((float)(v * rf), rl[r]);
         }
-        colrec[i * rc + (q ^ sw)] = pack8(ch);
-        colrec[i * rc + ((hc + q) ^ sw)] = pack8(cl);
-        rowrec[i * rc + q] = pack8(rh);
-        rowrec[i * rc + hc + q] = pack8(rl);
+        if (kp > kStagedRecordKP) {
+            const int st = (q >> 2) * 8 + (q & 3);
+            colrec[i * rc + st] = pack8(ch);
+            colrec[i * rc + st + 4] = pack8(cl);
+            rowrec[i * rc + st] = pack8(rh);
+            rowrec[i * rc + st + 4] = pack8(rl);
+        } else {
+            colrec[i * rc + (q ^ sw)] = pack8(ch);
+            colrec[i * rc + ((hc + q) ^ sw)] = pack8(cl);
+            rowrec[i * rc + q] = pack8(rh);
+            rowrec[i * rc + hc + q] = pack8(rl);
+        }
     }
     nrm_out[i] = (float)nrm;
     float bv = kPadBias;

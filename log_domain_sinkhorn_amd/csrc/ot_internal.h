@@ -164,6 +164,12 @@ hipError_t launch_plan_pass_wide(int kp, bool cost, const void *row_rec, const f
                                  const float *row_nrm, const void *col_rec, const float *col_hat,
                                  const float *col_nrm, int64_t rows, int64_t rows_pad,
                                  int64_t cols_pad, double scale, double2 *part, hipStream_t s);
+// Above this many coordinates per record the split-f16 records are staged:
+// each 32-coordinate stage's 4 hi and 4 lo 16-byte chunks side by side (one
+// 128-byte line per record and stage, chunk q of stage s at 8s + q for hi and
+// 8s + 4 + q for lo), unswizzled, on both sides; only the kernels tiled like
+// a matrix product read them (the transport calls stop at 512).
+constexpr int kStagedRecordKP = 512;
 // For kp in {512, 640, 768, 896, 1024} (448 < d <= 1024) the half-step and
 // the statistics pass are tiled like a matrix product, both sides streamed
 // through LDS in coordinate stages (lse_gemm.hip); the h3 entry points
