@@ -50,7 +50,7 @@ constexpr int kGKS = 32;                     // coordinates per stage
 constexpr int kGRecs = kGBM + kGBN;          // records per stage
 constexpr int kGStage4 = kGRecs * 8;         // 16-byte chunks per stage (4 hi + 4 lo each)
 constexpr int kGLoads = kGStage4 / 64 / kGW; // direct loads per wave and stage
-constexpr int kGTail4 = 2 * kGBN / 4;       // behind the records: biases, norms
+constexpr int kGTail4 = 2 * kGBN / 4;        // behind the records: biases, norms
 constexpr int kGTargetBlocks = 2048;
 static_assert(kGStage4 % (64 * kGW) == 0, "whole loads per wave");
 
@@ -87,10 +87,10 @@ __device__ __forceinline__ bool gemm_block(int nmap, int nrb, int nsplit, int &r
 // record's index in the block, mod 16); row records are unswizzled. Above
 // kStagedRecordKP both sides' records are staged (a stage's 8 chunks side by
 // side at 8s .. 8s + 7, unswizzled), so a record's stage is one 128-byte
-// line. With
-// the last stage of a block, waves 0 and 1 also load the block's 128 column
-// biases behind the stage's records, where the block's epilogue reads them,
-// and with NRM waves 2 and 3 the columns' squared norms after those.
+// line. With the last stage of a block, waves 0 and 1 also load the block's
+// 128 column biases behind the stage's records, where the block's epilogue
+// reads them, and with NRM waves 2 and 3 the columns' squared norms after
+// those.
 constexpr int kGRowLoads = kGBM * 8 / 64 / kGW;  // per wave and stage
 constexpr int kGColLoads = kGBN * 8 / 64 / kGW;
 static_assert(kGRowLoads + kGColLoads == kGLoads, "every slot loaded once");
