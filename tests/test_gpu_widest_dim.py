@@ -148,6 +148,30 @@ def test_widest_grid_rounding():
     assert abs(st["marg_col"] - sk["marg_col"]) <= TOL_MARG
 
 
+def test_widest_single_column_split():
+    # 524288 rows are 2048 row blocks: the column split count drops to one,
+    # so the f half-step writes its potentials directly (no partials, no
+    # merge); the g half-step (200 rows) runs 2048 splits. One iteration from
+    # g = 0, checked on sampled rows of both sides.
+    n, m, d = 524288, 200, 513
+    c = random_clouds(n, m, d, seed=13, spread=1.0 / np.sqrt(d))
+    eps = 0.3
+    print(f"{n}x{m}x{d}: one iteration from g = 0", flush=True)
+    x, y, a, b = dev(c["x"]), dev(c["y"]), dev(c["a"]), dev(c["b"])
+    f = torch.zeros(n, device=DEV)
+    g = torch.zeros(m, device=DEV)
+    lds.ot_sinkhorn_solve(x, y, a, b, eps, 1, f, g)
+    torch.cuda.synchronize()
+    f_np, g_np = f.cpu().numpy(), g.cpu().numpy()
+    rows = np.arange(0, n, 5003)
+    f_ref = oracle.half_update(c["x"], c["y"], c["a"], np.zeros(m), eps, rows=rows)
+    g_rows = np.arange(0, m, 10)
+    g_ref = oracle.half_update(c["y"], c["x"], c["b"], f_np, eps, rows=g_rows)
+    ef, eg = rel_inf(f_np[rows], f_ref), rel_inf(g_np[g_rows], g_ref)
+    print(f"  sampled rows: rel err f {ef:.2e} g {eg:.2e}", flush=True)
+    assert ef <= TOL_HALF and eg <= TOL_HALF
+
+
 def test_widest_bitwise_deterministic():
     c = random_clouds(2000, 1700, 1024, seed=5, spread=1.0 / 32.0)
     a = gpu_solve(c, 0.4, 5)
