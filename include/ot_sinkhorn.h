@@ -72,9 +72,10 @@ typedef enum {
 } ot_status;
 
 /* Largest feature dimension d the point-cloud calls accept: up to 192 the
- * matrix-core kernels work on 32x32 tiles, from 193 to 512 on 16x16 tiles
- * (half the row-operand registers per lane), from 513 to 1024 on 16x16 tiles
- * with each row's coordinates split in quarters over four waves. */
+ * matrix-core kernels work on 32x32 tiles with a row's operands in registers,
+ * from 193 to 448 on 16x16 tiles (half the row-operand registers per lane),
+ * from 449 to 1024 tiled like a matrix product, both sides streamed through
+ * LDS in 32-coordinate stages. */
 #define OT_MAX_DIM 1024
 
 /* Largest d of the transport calls (ot_transport_apply, ot_barycentric_map,

@@ -512,9 +512,10 @@ constexpr int kCenterBlocks = 256;
 }  // namespace
 
 // Coordinates per record: 32k up to 192 (the 32x32 kernels); above, the
-// 16x16-tile kernels' sizes 224, 256, 320, 384, 448; above 448 the quarter-
-// split kernels' 512, 640, 768, 896, 1024 (at 512 those measured 18.5 ms
-// per 65536^2 half-step against 22.6 ms for the 16x16 kernel, which spills).
+// 16x16-tile kernels' sizes 224, 256, 320, 384, 448; above 448 the sizes of
+// the kernels tiled like a matrix product, 512, 640, 768, 896, 1024 (whole
+// 32-coordinate stages; at 512 the 16x16 kernel spills and measured 22.6 ms
+// per 65536^2 half-step, the tiled one 13.3 ms).
 int h3_kp(int d) {
     if (d <= 256)
         return (d + 31) / 32 * 32;

@@ -1,8 +1,9 @@
-"""GPU parity for the widest feature dimensions, 512 < d <= 1024 (the pages
+"""GPU parity for the widest feature dimensions, 448 < d <= 1024 (the pages
 measure up to d = 1024, "FlashSinkhorn: IO-Aware Entropic Optimal Transport
-on GPU", "Experimentelle Ergebnisse"). Records of 640, 768, 896 or 1024
-coordinates; each row's coordinates are split in quarters over four waves
-whose partial dot products are added in LDS. The update is the one of
+on GPU", "Experimentelle Ergebnisse"). Records of 512, 640, 768, 896 or 1024
+coordinates (staged above 512); the half-step and the statistics are tiled
+like a matrix product, both sides streamed through LDS in 32-coordinate
+stages, each stage's chains flushed into fp32 sums. The update is the one of
 "Methodik" section 1, checked against the fp64 oracle at the bounds of the
 other paths:
 
