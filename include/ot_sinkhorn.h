@@ -79,9 +79,10 @@ typedef enum {
 #define OT_MAX_DIM 1024
 
 /* Largest d of the transport calls (ot_transport_apply, ot_barycentric_map,
- * ot_cost_gradient_x); from OT_MAX_TRANSPORT_DIM + 1 to OT_MAX_DIM they return
- * NOT_SUPPORTED. */
-#define OT_MAX_TRANSPORT_DIM 512
+ * ot_cost_gradient_x): all of OT_MAX_DIM. Above 512 the plan's terms come
+ * from the kernels tiled like a matrix product and the values are applied
+ * 64 channels per pass over the columns. */
+#define OT_MAX_TRANSPORT_DIM 1024
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *ot_status_string(ot_status s);
@@ -203,8 +204,11 @@ ot_status ot_marginal_error(const float *x, const float *y, const float *a,
  *   dv   in [1, OT_MAX_VALUE_DIM]
  *   out  [n*dv]  row-major; must not overlap any input
  *
- * Other arguments as ot_plan_stats. Terms of P are formed in fp64 and
- * exponentiated in fp32; sums over j are fp64 in a fixed order.
+ * Other arguments as ot_plan_stats. d < 32: the exponent of each P_ij is
+ * formed in fp64 and exponentiated in fp32. d >= 32: log2 P_ij comes from the
+ * split-f16 products of the solve (fp32 accumulation) and P.v from products
+ * of three-part bf16 splits of P and v. Sums over j are fp32 within a column
+ * range and fp64 across ranges, in a fixed order.
  * Errors: INVALID_VALUE (null pointer, sizes < 1, bad eps, overlap),
  * NOT_SUPPORTED (d > OT_MAX_TRANSPORT_DIM, dv > OT_MAX_VALUE_DIM),
  * OUT_OF_MEMORY, LAUNCH_FAILURE.

@@ -57,7 +57,7 @@ OT_ERROR_NOT_SUPPORTED = 2
 OT_ERROR_OUT_OF_MEMORY = 3
 OT_ERROR_LAUNCH_FAILURE = 4
 OT_MAX_DIM = 1024
-OT_MAX_TRANSPORT_DIM = 512
+OT_MAX_TRANSPORT_DIM = 1024
 OT_MAX_VALUE_DIM = 1024
 OT_NO_ALLOC_SCRATCH_BYTES = 128 << 20
 

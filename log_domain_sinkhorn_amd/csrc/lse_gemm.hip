@@ -31,174 +31,23 @@
 // Workgroup order: the 1-D grid is dealt so that the column splits of one
 // row block run on one XCD (workgroup L goes to XCD L mod 8), so that
 // block's row records, re-read for every column block, stay in that XCD's L2.
-#include "mfma_common.h"
+//
+// The stage pipeline, the workgroup order and the grid plan are in
+// gemm_pipeline.h (shared with the transport application); these kernels run
+// it with two row subtiles per wave.
+#include "gemm_pipeline.h"
 
 #include <math.h>
-
-#include <type_traits>
 
 namespace otsk {
 
 namespace {
 
 using namespace mfma;
+using namespace gemm;
 
-constexpr int kGW = 8;                       // waves per workgroup
-constexpr int kGBM = 256;                    // rows per workgroup
-constexpr int kGBN = 128;                    // columns per column block
-constexpr int kGKS = 32;                     // coordinates per stage
-constexpr int kGRecs = kGBM + kGBN;          // records per stage
-constexpr int kGStage4 = kGRecs * 8;         // 16-byte chunks per stage (4 hi + 4 lo each)
-constexpr int kGLoads = kGStage4 / 64 / kGW; // direct loads per wave and stage
-constexpr int kGTail4 = 2 * kGBN / 4;        // behind the records: biases, norms
-constexpr int kGTargetBlocks = 2048;
-static_assert(kGStage4 % (64 * kGW) == 0, "whole loads per wave");
-
-// LDS slot of logical chunk t (0-3 hi, 4-7 lo) of stage record r. The XOR
-// keeps the 16-byte reads of 8 (and of 16) consecutive lanes, which take
-// consecutive records, on distinct banks.
-__device__ __forceinline__ int gslot(int r, int t) { return r * 8 + (t ^ ((r ^ (r >> 3)) & 7)); }
-
-// Workgroup L -> (row block, column split) over nmap row blocks: the splits
-// of row block rb run on XCD rb mod 8 when nmap is a multiple of 8 (the grid
-// then rounds the row-block count up to it), otherwise in split-minor order.
-// Returns false for the rounding's extra workgroups (rb >= nrb).
-__device__ __forceinline__ bool gemm_block(int nmap, int nrb, int nsplit, int &rb, int &split) {
-    const int L = (int)blockIdx.x;
-    if (nmap % 8 == 0) {
-        const int q = L / 8;
-        split = q % nsplit;
-        rb = (q / nsplit) * 8 + L % 8;
-    } else {
-        split = L % nsplit;
-        rb = L / nsplit;
-    }
-    return rb < nrb;
-}
-
-// Issue the direct loads of stage s of column block cb into `buf`. Stage
-// record r (rows 0-255, then columns) fills slots 8r .. 8r + 7; slot 8r + p
-// holds logical chunk t = p ^ ((r ^ (r >> 3)) & 7) (the read swizzle of
-// gslot). Each 64-lane load fills 64 consecutive slots, i.e. 8 records:
-// wave w issues row loads 4w .. 4w + 3 and column loads 2w, 2w + 1, so lane
-// l of load g serves record 8g + l/8 and position l mod 8. Column records
-// carry the global layout's chunk swizzle (16-byte chunk q of point j at
-// q ^ (j & 15); column blocks start at multiples of 128, so j & 15 is the
-// record's index in the block, mod 16); row records are unswizzled. Above
-// kStagedRecordKP both sides' records are staged (a stage's 8 chunks side by
-// side at 8s .. 8s + 7, unswizzled), so a record's stage is one 128-byte
-// line. With the last stage of a block, waves 0 and 1 also load the block's
-// 128 column biases behind the stage's records, where the block's epilogue
-// reads them, and with NRM waves 2 and 3 the columns' squared norms after
-// those.
-constexpr int kGRowLoads = kGBM * 8 / 64 / kGW;  // per wave and stage
-constexpr int kGColLoads = kGBN * 8 / 64 / kGW;
-static_assert(kGRowLoads + kGColLoads == kGLoads, "every slot loaded once");
-
-template <int KP, bool NRM>
-__device__ __forceinline__ void issue_stage(const float4 *__restrict__ row4,
-                                            const float4 *__restrict__ col4,
-                                            const float *__restrict__ colb,
-                                            const float *__restrict__ coln, int64_t row0,
-                                            int64_t col0, int s, bool last, float4 *buf,
-                                            int wave, int lane) {
-    constexpr int RC = KP / 4;
-    const int lr = lane >> 3, lp = lane & 7;
-#pragma unroll
-    for (int k = 0; k < kGRowLoads; ++k) {
-        const int g = wave * kGRowLoads + k;
-        const int t = lp ^ ((lr ^ g) & 7);
-        const int q = KP > kStagedRecordKP ? 8 * s + t : (t < 4 ? 0 : KP / 8) + 4 * s + (t & 3);
-        __builtin_amdgcn_global_load_lds(row4 + (row0 + g * 8 + lr) * RC + q,
-                                         (lds_void *)(buf + g * 64), 16, 0, 0);
-    }
-#pragma unroll
-    for (int k = 0; k < kGColLoads; ++k) {
-        const int g = wave * kGColLoads + k;
-        const int rl = g * 8 + lr;  // column within the block
-        const int t = lp ^ ((lr ^ g) & 7);
-        const int q = KP > kStagedRecordKP ? 8 * s + t
-                                           : (t < 4 ? 0 : KP / 8) + ((4 * s + (t & 3)) ^ (rl & 15));
-        __builtin_amdgcn_global_load_lds(col4 + (col0 + rl) * RC + q,
-                                         (lds_void *)(buf + kGBM * 8 + g * 64), 16, 0, 0);
-    }
-    if (last && wave < kGBN / 64)
-        __builtin_amdgcn_global_load_lds(
-            colb + col0 + wave * 64 + lane,
-            (lds_void *)(reinterpret_cast<float *>(buf + kGStage4) + wave * 64), 4, 0, 0);
-    if (NRM && last && wave >= kGBN / 64 && wave < kGBN / 32)
-        __builtin_amdgcn_global_load_lds(
-            coln + col0 + (wave - kGBN / 64) * 64 + lane,
-            (lds_void *)(reinterpret_cast<float *>(buf + kGStage4) + kGBN +
-                         (wave - kGBN / 64) * 64),
-            4, 0, 0);
-}
-
-// The wave's operands of one stage: hi and lo chunks of both 16-coordinate
-// k-steps for its two column subtiles (a) and two row subtiles (b).
-struct StageOps {
-    half8 ah[2][2], al[2][2], bh[2][2], bl[2][2];
-};
-
-__device__ __forceinline__ void stage_operands(const float4 *buf, int rw, int cw, int li, int hl,
-                                               StageOps &o) {
-    // In the order the chains consume them: the first layer's operands
-    // (lo of the columns, hi of the rows, k-step 0) first.
-    int rc[2], rr[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        rc[u] = kGBM + 64 * cw + 32 * u + li;
-        rr[u] = 64 * rw + 32 * u + li;
-    }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            o.al[u][c] = as_half8(buf[gslot(rc[u], 4 + 2 * c + hl)]);
-            o.bh[u][c] = as_half8(buf[gslot(rr[u], 2 * c + hl)]);
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            o.ah[u][c] = as_half8(buf[gslot(rc[u], 2 * c + hl)]);
-            o.bl[u][c] = as_half8(buf[gslot(rr[u], 4 + 2 * c + hl)]);
-        }
-    }
-}
-
-// One stage of the wave's 2 x 2 subtiles: chains from zero (corrections,
-// then hi x hi) added to the fp32 sums. The four chains advance together,
-// one product each in turn, on four accumulators; layers [l0, l1) of the
-// six (al0.bh0, ah0.bl0, al1.bh1, ah1.bl1, ah0.bh0, ah1.bh1).
-template <int L0, int L1>
-__device__ __forceinline__ void stage_layers(const StageOps &o, floatx16 (&acc)[2][2]) {
-#pragma unroll
-    for (int l = L0; l < L1; ++l) {
-        const int c = (l == 0 || l == 1 || l == 4) ? 0 : 1;
-#pragma unroll
-        for (int rs = 0; rs < 2; ++rs)
-#pragma unroll
-            for (int cs = 0; cs < 2; ++cs) {
-                const half8 a = (l == 0 || l == 2) ? o.al[cs][c] : o.ah[cs][c];
-                const half8 b = (l == 1 || l == 3) ? o.bl[rs][c] : o.bh[rs][c];
-                acc[rs][cs] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                    a, b,
-                    l == 0 ? floatx16{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
-                                      0.f, 0.f, 0.f, 0.f}
-                           : acc[rs][cs],
-                    0, 0, 0);
-            }
-    }
-}
-
-__device__ __forceinline__ void add_sums(const floatx16 (&acc)[2][2], floatx16 (&sum)[2][2]) {
-#pragma unroll
-    for (int rs = 0; rs < 2; ++rs)
-#pragma unroll
-        for (int cs = 0; cs < 2; ++cs)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                sum[rs][cs][v] += acc[rs][cs][v];
-}
+constexpr int kGBM = GTile<2>::BM;         // rows per workgroup
+constexpr int kGStage4 = GTile<2>::Stage4; // 16-byte chunks per stage
 
 // Fold the finished column block (sums plus column biases) into the rows'
 // running (M, S).
@@ -237,89 +86,6 @@ __device__ __forceinline__ void lse_combine2(float &M, float &S, float Mo, float
     M = Mn;
 }
 
-// The stage pipeline of one workgroup: column blocks bbeg .. bend - 1 of its
-// split against its 256 rows; after the last stage of each block,
-// epi(bias, nrm, sum) consumes the block (bias and norms in LDS) and the
-// sums restart from zero. st0 .. st2 are three separate __shared__ arrays:
-// each gets its own alias scope, so the compiler sees that reading stage t
-// does not wait for the direct loads into the other two buffers.
-template <int KP, bool NRM, class Epi>
-__device__ __forceinline__ void gemm_stream(float4 *st0, float4 *st1, float4 *st2,
-                                            const float4 *row4, const float4 *col4,
-                                            const float *colb, const float *coln, int64_t row0,
-                                            int bbeg, int bend, int wave, int lane, Epi &&epi) {
-    constexpr int NS = KP / kGKS;  // stages per column block
-    static_assert(KP % kGKS == 0 && NS >= 2, "whole stages, at least two per block");
-    float4 *const stg[3] = {st0, st1, st2};
-    const int rw = wave & 3;
-    const int cw = wave >> 2;
-    const int hl = lane >> 5;
-    const int li = lane & 31;
-    const int T = (bend - bbeg) * NS;  // stages of this workgroup (>= NS)
-
-    auto issue = [&](int t, auto bc) {
-        constexpr int b = decltype(bc)::value;
-        const int cb = bbeg + t / NS;
-        issue_stage<KP, NRM>(row4, col4, colb, coln, row0, (int64_t)cb * kGBN, t % NS,
-                             t % NS == NS - 1, stg[b], wave, lane);
-    };
-    issue(0, std::integral_constant<int, 0>{});
-    issue(1, std::integral_constant<int, 1>{});
-
-    floatx16 sum[2][2];
-#pragma unroll
-    for (int rs = 0; rs < 2; ++rs)
-#pragma unroll
-        for (int cs = 0; cs < 2; ++cs)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                sum[rs][cs][v] = 0.f;
-
-    // Stage t: wait for its loads (those of stage t + 1, issued later, may
-    // still be in flight), then the barrier makes every wave's loads
-    // visible and tells that every wave is done with stage t - 1, whose
-    // buffer then takes stage t + 2. A bare s_barrier: the direct loads are
-    // ordered by the explicit vmcnt wait, and __syncthreads()'s fence would
-    // wait for the loads of stage t + 1 as well. Every step issues one
-    // stage (past the end, a reload of the last one into the free buffer,
-    // never read), so the count of loads behind stage t is always the same
-    // and the compiler adds no wait of its own before the LDS reads.
-    auto step = [&](int t, auto bc) {
-        constexpr int b = decltype(bc)::value;
-        __builtin_amdgcn_s_waitcnt(0x0F70 | kGLoads);  // vmcnt(kGLoads)
-        __builtin_amdgcn_s_barrier();
-        StageOps o;
-        stage_operands(stg[b], rw, cw, li, hl, o);
-        issue(min(t + 2, T - 1), std::integral_constant<int, (b + 2) % 3>{});
-        floatx16 acc[2][2];
-        stage_layers<0, 6>(o, acc);
-        add_sums(acc, sum);
-        if (t % NS == NS - 1) {
-            const float *tail = reinterpret_cast<const float *>(stg[b] + kGStage4);
-            epi(tail, tail + kGBN, sum);
-#pragma unroll
-            for (int rs = 0; rs < 2; ++rs)
-#pragma unroll
-                for (int cs = 0; cs < 2; ++cs)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        sum[rs][cs][v] = 0.f;
-        }
-    };
-    for (int t = 0; t < T; t += 3) {
-        // Nested, so that no path reaches step t + 2 without step t + 1.
-        step(t, std::integral_constant<int, 0>{});
-        if (t + 1 < T) {
-            step(t + 1, std::integral_constant<int, 1>{});
-            if (t + 2 < T)
-                step(t + 2, std::integral_constant<int, 2>{});
-        }
-    }
-    // The last reloads land before the caller reuses stage buffer 0.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-}
-
 template <int KP>
 __global__ __launch_bounds__(64 * kGW) void lse_rows_gemm_kernel(HalfStep h, int blocks_per_split,
                                                                  int nblocks, int nmap,
@@ -343,7 +109,7 @@ __global__ __launch_bounds__(64 * kGW) void lse_rows_gemm_kernel(HalfStep h, int
     const int64_t row0 = (int64_t)rblk * kGBM;
 
     float M[2] = {0.f, 0.f}, S[2] = {0.f, 0.f};
-    gemm_stream<KP, false>(st0, st1, st2, static_cast<const float4 *>(h.row_rec),
+    gemm_stream<KP, false, 2>(st0, st1, st2, static_cast<const float4 *>(h.row_rec),
                            static_cast<const float4 *>(h.col_rec),
                            static_cast<const float *>(h.col_bias), nullptr, row0, bbeg, bend,
                            wave, lane, [&](const float *bias, const float *, floatx16(&sum)[2][2]) {
@@ -426,7 +192,7 @@ __global__ __launch_bounds__(64 * kGW) void plan_rows_gemm_kernel(
     const float m2 = -2.f * inv_scale;
 
     double rsum[2] = {0.0, 0.0}, csum[2] = {0.0, 0.0};
-    gemm_stream<KP, COST>(
+    gemm_stream<KP, COST, 2>(
         st0, st1, st2, row_rec, col4, colb, col_nrm, row0, bbeg, bend, wave, lane,
         [&](const float *bias, const float *nrm, floatx16(&sum)[2][2]) {
 #pragma unroll
@@ -480,31 +246,6 @@ __global__ __launch_bounds__(64 * kGW) void plan_rows_gemm_kernel(
     }
 }
 
-struct GPlan {
-    int nblocks;
-    int blocks_per_split;
-    int nsplit;
-    int64_t row_blocks;
-    int64_t row_map;  // row blocks of the grid's mapping (>= row_blocks)
-};
-
-// Column splits: enough workgroups for the chip (about kGTargetBlocks), a
-// multiple of 8 row blocks when possible so the XCD order applies.
-GPlan plan_gemm(int64_t rows, int64_t cols_pad) {
-    GPlan p;
-    p.nblocks = (int)(cols_pad / kGBN);
-    p.row_blocks = (rows + kGBM - 1) / kGBM;
-    int64_t want = (kGTargetBlocks + p.row_blocks - 1) / p.row_blocks;
-    if (want > p.nblocks)
-        want = p.nblocks;
-    if (want < 1)
-        want = 1;
-    p.blocks_per_split = (int)((p.nblocks + want - 1) / want);
-    p.nsplit = (p.nblocks + p.blocks_per_split - 1) / p.blocks_per_split;
-    p.row_map = p.row_blocks >= 8 ? (p.row_blocks + 7) / 8 * 8 : p.row_blocks;
-    return p;
-}
-
 template <int KP>
 hipError_t launch_gemm_kp(const HalfStep &h, const GPlan &p, hipStream_t s) {
     hipLaunchKernelGGL((lse_rows_gemm_kernel<KP>), dim3((unsigned)(p.row_map * p.nsplit)),
@@ -528,12 +269,12 @@ hipError_t launch_plan_gemm_kp(const GPlan &p, const float4 *rr, const float *ro
 }  // namespace
 
 size_t half_step_partials_gemm(int64_t rows, int64_t cols_pad) {
-    const GPlan p = plan_gemm(rows, cols_pad);
+    const GPlan p = plan_gemm(rows, cols_pad, kGBM);
     return p.nsplit > 1 ? (size_t)p.nsplit * (size_t)pad_points(rows) : 0;
 }
 
 hipError_t launch_half_step_gemm(const HalfStep &h, int kp, hipStream_t s) {
-    const GPlan p = plan_gemm(h.rows, h.cols_pad);
+    const GPlan p = plan_gemm(h.rows, h.cols_pad, kGBM);
     hipError_t e;
     switch (kp) {
     case 512: e = launch_gemm_kp<512>(h, p, s); break;
@@ -549,14 +290,14 @@ hipError_t launch_half_step_gemm(const HalfStep &h, int kp, hipStream_t s) {
 }
 
 int plan_pass_gemm_splits(int64_t rows, int64_t cols_pad) {
-    return plan_gemm(rows, cols_pad).nsplit;
+    return plan_gemm(rows, cols_pad, kGBM).nsplit;
 }
 
 hipError_t launch_plan_pass_gemm(int kp, bool cost, const void *row_rec, const float *row_hat,
                                  const float *row_nrm, const void *col_rec, const float *col_hat,
                                  const float *col_nrm, int64_t rows, int64_t rows_pad,
                                  int64_t cols_pad, double scale, double2 *part, hipStream_t s) {
-    const GPlan p = plan_gemm(rows, cols_pad);
+    const GPlan p = plan_gemm(rows, cols_pad, kGBM);
     const float4 *rr = static_cast<const float4 *>(row_rec);
     const float4 *cr = static_cast<const float4 *>(col_rec);
     const float inv = (float)(1.0 / scale);

@@ -104,7 +104,10 @@ hipError_t launch_transport_apply(const Layout &L, const void *xrec, const void 
 // Matrix-core variant on split-f16 records (launch_prep_h3 with the hat
 // biases of f and g): x's row records and y's column records; rowsum
 // (nullable) also receives r_i = sum_j P_ij, with rowsum = true in the
-// scratch size.
+// scratch size, where transport_row_sums(kp) (record sizes up to 192 and
+// 224, 320, 448; at the others the caller appends a column of ones to the
+// values).
+bool transport_row_sums(int kp);
 size_t transport_mfma_scratch_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum,
                                       int kp);
 hipError_t launch_transport_apply_mfma(int kp, const void *xrow, const float *xhat,
@@ -168,7 +171,8 @@ hipError_t launch_plan_pass_wide(int kp, bool cost, const void *row_rec, const f
 // each 32-coordinate stage's 4 hi and 4 lo 16-byte chunks side by side (one
 // 128-byte line per record and stage, chunk q of stage s at 8s + q for hi and
 // 8s + 4 + q for lo), unswizzled, on both sides; only the kernels tiled like
-// a matrix product read them (the transport calls stop at 512).
+// a matrix product read them (the widest half-step and statistics pass, and
+// the transport application).
 constexpr int kStagedRecordKP = 512;
 // For kp in {512, 640, 768, 896, 1024} (448 < d <= 1024) the half-step and
 // the statistics pass are tiled like a matrix product, both sides streamed

@@ -149,9 +149,8 @@ def test_map_and_gradient_reject_invalid(lib):
     assert gx(X, Y, F, G, 10, 12, 3, 0.1, Y + 4, None) == INVALID          # out overlaps y
     assert gx(X, Y, F, G, 10, 12, 3, -0.1, OUT, None) == INVALID
     assert gx(X, Y, F, G, 10, 12, lds.OT_MAX_DIM + 1, 0.1, OUT, None) == UNSUPPORTED
-    # the solve's range goes past the transport calls' range
-    assert bm(X, Y, A, F, G, 10, 12, lds.OT_MAX_TRANSPORT_DIM + 1, 0.1, OUT, None) == UNSUPPORTED
-    assert gx(X, Y, F, G, 10, 12, lds.OT_MAX_TRANSPORT_DIM + 1, 0.1, OUT, None) == UNSUPPORTED
+    # the transport calls cover the solve's whole range of d
+    assert lds.OT_MAX_TRANSPORT_DIM == lds.OT_MAX_DIM
 
 
 def test_birkhoff_rejects_invalid(lib):

@@ -191,7 +191,7 @@ def test_deterministic():
 # full sizes: synthetic potentials, sampled rows                                #
 # --------------------------------------------------------------------------- #
 
-@pytest.mark.parametrize("name", ["feature64_64k", "cube_gauss3d_64k"])
+@pytest.mark.parametrize("name", ["feature64_64k", "cube_gauss3d_64k", "feature1024_50k"])
 def test_full_size_sampled_rows(name):
     c = make_clouds(name)
     eps = c["eps"][0]

@@ -14,7 +14,10 @@ Transport on GPU", "Experimentelle Ergebnisse"); the update is the one of
 * at 65536 x 65536 x 256, one half-step from the GPU's own iterate on sampled
   rows (the size the benchmark measures at d = 256);
 * the transport application, barycentric map and x-gradient ("Methodik"
-  section 3) on the same tiles, P.V on 16x16x32 bf16 matrix cores.
+  section 3): at record sizes 224, 320 and 448 on the same tiles (P.V on
+  16x16x32 bf16 matrix cores, row sums beside the values), at 256, 384 and
+  512 on the widest dimensions' matrix-product tiling (the x-gradient through
+  [y | 1]).
 """
 import numpy as np
 import pytest
@@ -164,7 +167,8 @@ def _apply(c, f, g, eps, v):
 
 @pytest.mark.parametrize("n,m,d,dv", [(700, 900, 224, 224), (1000, 700, 256, 5),
                                       (300, 1300, 384, 40), (500, 600, 512, 512),
-                                      (1, 300, 256, 33), (257, 1, 320, 64)])
+                                      (1, 300, 256, 33), (257, 1, 320, 64),
+                                      (400, 500, 448, 70), (129, 640, 300, 300)])
 def test_wide_transport_apply(n, m, d, dv):
     # out_i = sum_j P_ij v_j on 16x16 tiles; oracle potentials, random values.
     from workloads import random_values
@@ -181,10 +185,13 @@ def test_wide_transport_apply(n, m, d, dv):
     assert err <= TOL_APPLY
 
 
-def test_wide_map_and_gradient_d256():
-    c = make_clouds("feature64_64k", n=900, m=1100, d=256)
+@pytest.mark.parametrize("d", [256, 448])
+def test_wide_map_and_gradient(d):
+    # d = 256: matrix-product tiling, gradient through [y | 1]; d = 448:
+    # 16x16 tiles with the row sums beside the values.
+    c = make_clouds("feature64_64k", n=900, m=1100, d=d)
     eps = c["eps"][0]
-    print("barycentric map and x-gradient at d=256", flush=True)
+    print(f"barycentric map and x-gradient at d={d}", flush=True)
     fo, go = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, 20)
     f, g = fo.astype(np.float32), go.astype(np.float32)
     x, y, a = dev(c["x"]), dev(c["y"]), dev(c["a"])

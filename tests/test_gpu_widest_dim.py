@@ -14,7 +14,10 @@ other paths:
   eps schedule, statistics of identical potentials, bitwise determinism;
 * at 65536 x 65536 x 1024, one half-step from the GPU's own iterate on
   sampled rows;
-* the transport calls stop at OT_MAX_TRANSPORT_DIM = 512 and refuse larger d.
+* the transport application, barycentric map and x-gradient ("Methodik"
+  section 3) on the same pipeline with P.V per 128-column block, 64 value
+  channels per pass: whole outputs against the oracle on odd shapes and value
+  widths, and the refusal above OT_MAX_DIM.
 """
 import numpy as np
 import pytest
@@ -202,18 +205,83 @@ def test_widest_full_size_sampled_half_steps():
     assert err <= TOL_HALF
 
 
-def test_transport_calls_refuse_beyond_their_limit():
-    d = lds.OT_MAX_TRANSPORT_DIM + 1
-    c = random_clouds(40, 50, d, seed=1)
+TOL_APPLY = 5e-5  # the transport tests' bound (see test_gpu_transport.py)
+
+
+@pytest.mark.parametrize("n,m,d,dv", [(700, 900, 640, 640), (1000, 700, 1024, 5),
+                                      (300, 1300, 768, 100), (1, 300, 896, 65),
+                                      (257, 1, 1024, 1024), (129, 257, 1000, 64),
+                                      (600, 500, 513, 130)])
+def test_widest_transport_apply(n, m, d, dv):
+    # out_i = sum_j P_ij v_j with P from the matrix-product tiling; oracle
+    # potentials, random values (several passes of 64 channels, ragged ends).
+    from workloads import random_values
+    c = random_clouds(n, m, d, seed=n + m + d, spread=1.0 / np.sqrt(d))
+    eps = 0.3
+    print(f"transport {n}x{m}x{d}, dv={dv}", flush=True)
+    fo, go = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, 6)
+    f, g = fo.astype(np.float32), go.astype(np.float32)
+    v = random_values(m, dv, seed=d)
+    x, y = dev(c["x"]), dev(c["y"])
+    out = torch.empty((n, dv), dtype=torch.float32, device=DEV)
+    lds.ot_transport_apply(x, y, dev(f), dev(g), eps, dev(v), out)
+    torch.cuda.synchronize()
+    err = rel_inf(out.cpu().numpy(), oracle.transport_apply(c["x"], c["y"], f, g, eps, v))
+    print(f"  rel err {err:.2e}", flush=True)
+    assert err <= TOL_APPLY
+
+
+@pytest.mark.parametrize("d", [640, 1024])
+def test_widest_map_and_gradient(d):
+    # The x-gradient applies the plan to [y | 1] at these sizes (the row sums
+    # come out as the last channel).
+    c = make_clouds("feature64_64k", n=600, m=700, d=d)
+    eps = c["eps"][0]
+    print(f"barycentric map and x-gradient at d={d}", flush=True)
+    fo, go = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, 10)
+    f, g = fo.astype(np.float32), go.astype(np.float32)
     x, y, a = dev(c["x"]), dev(c["y"]), dev(c["a"])
+    bary = torch.empty_like(x)
+    grad = torch.empty_like(x)
+    lds.ot_barycentric_map(x, y, a, dev(f), dev(g), eps, bary)
+    lds.ot_cost_gradient_x(x, y, dev(f), dev(g), eps, grad)
+    torch.cuda.synchronize()
+    eb = rel_inf(bary.cpu().numpy(), oracle.barycentric_map(c["x"], c["y"], c["a"], f, g, eps))
+    eg = rel_inf(grad.cpu().numpy(), oracle.grad_x(c["x"], c["y"], f, g, eps))
+    print(f"  map rel err {eb:.2e}, gradient rel err {eg:.2e}", flush=True)
+    assert eb <= TOL_APPLY and eg <= TOL_APPLY
+
+
+def test_widest_transport_deterministic():
+    from workloads import random_values
+    c = random_clouds(300, 700, 1024, seed=9, spread=1.0 / 32)
+    v = random_values(700, 70, seed=2)
+    x, y = dev(c["x"]), dev(c["y"])
+    f = dev(np.zeros(300, np.float32))
+    g = dev(np.zeros(700, np.float32))
+    outs = []
+    for _ in range(2):
+        out = torch.empty((300, 70), dtype=torch.float32, device=DEV)
+        lds.ot_transport_apply(x, y, f, g, 0.5, dev(v), out)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    assert np.isfinite(outs[0]).all()
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_calls_refuse_beyond_the_largest_dimension():
+    # The transport calls cover every d the solve covers; beyond it, every
+    # call returns NOT_SUPPORTED.
+    assert lds.OT_MAX_TRANSPORT_DIM == lds.OT_MAX_DIM
+    d = lds.OT_MAX_DIM + 1
+    c = random_clouds(40, 50, d, seed=1)
+    x, y, a, b = dev(c["x"]), dev(c["y"]), dev(c["a"]), dev(c["b"])
     f, g = torch.zeros(40, device=DEV), torch.zeros(50, device=DEV)
     out = torch.empty_like(x)
     for call in (lambda: lds.ot_transport_apply(x, y, f, g, 0.5, y, out),
                  lambda: lds.ot_barycentric_map(x, y, a, f, g, 0.5, out),
-                 lambda: lds.ot_cost_gradient_x(x, y, f, g, 0.5, out)):
+                 lambda: lds.ot_cost_gradient_x(x, y, f, g, 0.5, out),
+                 lambda: lds.ot_sinkhorn_solve(x, y, a, b, 0.5, 3, f, g)):
         with pytest.raises(lds.OTError) as ei:
             call()
         assert ei.value.status == lds.OT_ERROR_NOT_SUPPORTED
-    # the solve itself runs at that d
-    f2, g2 = gpu_solve(c, 0.5 * d ** 0.5, 3)
-    assert np.isfinite(f2).all() and np.isfinite(g2).all()
