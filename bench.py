@@ -520,10 +520,11 @@ def run_transport(name, torch, lds, rates, reps=10, warm=3):
         res[f"{label}_pairs_per_s"] = n * m / (ms / 1e3)
     if d >= 32:
         # Matrix-pipe time per 32x32 subtile and wave: the split-f16 score
-        # (3*kp/16 f16 MFMAs of 32 cycles + one fp32 MFMA of 64) and P.V
+        # once (3*kp/16 f16 MFMAs of 32 cycles + one fp32 MFMA of 64) and P.V
         # (12 bf16 MFMAs of 32 cycles per 32 value channels: 2 column chunks
         # x 6 split products), at 2.4 GHz on 1024 SIMDs; frac = that time /
-        # the measured call.
+        # the measured call, so the kernels' score recomputation per pass of
+        # value channels (32 or 64 channels a pass) counts against it.
         kp = h3_kp(d)
         cycles = 3 * kp // 16 * 32 + 64 + 12 * 32 * ((d + 31) // 32)
         model_ms = (n / 32) * (m / 32) * cycles / (1024 * 2.4e9) * 1e3
@@ -599,12 +600,13 @@ def main():
                          "stats_roofline": stats_roofline(s["n"], s["m"], s["d"], s["stats_ms"],
                                                           rates),
                          "roofline": roofline_for(s, name, rates)}
-        for name in ("feature64_64k", "cube_gauss3d_64k"):
+        for name, reps, warm in (("feature64_64k", 10, 3), ("cube_gauss3d_64k", 10, 3),
+                                 ("feature1024_50k", 3, 1)):
             key = f"transport:{name}"
             if wanted is not None and key not in wanted:
                 continue
             print(f"# secondary {key}", file=sys.stderr, flush=True)
-            sec[key] = run_transport(name, torch, lds, rates)
+            sec[key] = run_transport(name, torch, lds, rates, reps=reps, warm=warm)
         for name in ("birkhoff4x4_1m_fixed20", "birkhoff4x4_1m"):
             if wanted is not None and name not in wanted:
                 continue

@@ -1,6 +1,6 @@
-// The stage pipeline of the kernels tiled like a matrix product (feature
-// dimensions 448 < d <= 1024: the half-step and the plan statistics in
-// lse_gemm.hip, the transport application in transport_mfma.hip).
+// The stage pipeline of the kernels tiled like a matrix product: the
+// half-step and the plan statistics for 448 < d <= 1024 (lse_gemm.hip) and
+// the transport application above 192 coordinates (transport_mfma.hip).
 //
 // A workgroup of 8 waves owns 128 RS rows (RS = 1 or 2 row subtiles of 32
 // per wave) and walks its column split in blocks of 128 columns. For each
@@ -75,14 +75,14 @@ __device__ __forceinline__ bool gemm_block(int nmap, int nrb, int nsplit, int &r
 // wave w issues row loads RowLoads w .. RowLoads (w + 1) - 1 and column
 // loads 2w, 2w + 1, so lane l of load g serves record 8g + l/8 and position
 // l mod 8. Column records carry the global layout's chunk swizzle (16-byte
-// chunk q of point j at q ^ (j & 15); column blocks start at multiples of
-// 128, so j & 15 is the record's index in the block, mod 16); row records
-// are unswizzled. Above kStagedRecordKP both sides' records are staged (a
-// stage's 8 chunks side by side at 8s .. 8s + 7, unswizzled), so a record's
-// stage is one 128-byte line. With the last stage of a block, waves 0 and 1
-// also load the block's 128 column biases behind the stage's records, where
-// the block's epilogue reads them, and with NRM waves 2 and 3 the columns'
-// squared norms after those.
+// chunk q of point j at q ^ (j & SW), SW = swizzle_mask(KP / 4); column
+// blocks start at multiples of 128, so j & SW is the record's index in the
+// block, masked); row records are unswizzled. Above kStagedRecordKP both
+// sides' records are staged (a stage's 8 chunks side by side at 8s .. 8s + 7,
+// unswizzled), so a record's stage is one 128-byte line. With the last stage
+// of a block, waves 0 and 1 also load the block's 128 column biases behind
+// the stage's records, where the block's epilogue reads them, and with NRM
+// waves 2 and 3 the columns' squared norms after those.
 template <int KP, bool NRM, int RS>
 __device__ __forceinline__ void issue_stage(const float4 *__restrict__ row4,
                                             const float4 *__restrict__ col4,
@@ -106,8 +106,9 @@ __device__ __forceinline__ void issue_stage(const float4 *__restrict__ row4,
         const int g = wave * kGColLoads + k;
         const int rl = g * 8 + lr;  // column within the block
         const int t = lp ^ ((lr ^ g) & 7);
-        const int q = KP > kStagedRecordKP ? 8 * s + t
-                                           : (t < 4 ? 0 : KP / 8) + ((4 * s + (t & 3)) ^ (rl & 15));
+        const int q = KP > kStagedRecordKP
+                          ? 8 * s + t
+                          : ((t < 4 ? 0 : KP / 8) + 4 * s + (t & 3)) ^ (rl & swizzle_mask(RC));
         __builtin_amdgcn_global_load_lds(col4 + (col0 + rl) * RC + q,
                                          (lds_void *)(buf + G::BM * 8 + g * 64), 16, 0, 0);
     }

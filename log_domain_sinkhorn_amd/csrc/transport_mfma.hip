@@ -31,9 +31,8 @@
 // Accumulation is fp32 within a workgroup's column range; the column ranges'
 // partials are added in fp64, in split order. No atomics.
 //
-// Three kernels by record size: transport_mfma_kernel (32x32 tiles, a row's
-// operands in registers, kp <= 192), transport_wide_kernel (16x16 tiles,
-// kp = 224, 320, 448) and transport_gemm_kernel (kp = 256, 384 and 512 ..
+// Two kernels by record size: transport_mfma_kernel (32x32 tiles, a row's
+// operands in registers, kp <= 192) and transport_gemm_kernel (kp = 224 ..
 // 1024: the score on the stage pipeline of the widest half-step, P.V per
 // 128-column block).
 #include "gemm_pipeline.h"
@@ -390,317 +389,7 @@ int padded_channels(int dv, int kp) {
 }
 
 // ---------------------------------------------------------------------------
-// Wide feature dimensions (kp > 192): the score on 16x16 tiles as in the wide
-// half-step (each wave owns 16 rows; lane l holds row i = l % 16 and the
-// columns j = 4g + r, g = l / 16, of each 16-column subtile), P.V on
-// v_mfma_f32_16x16x32_bf16 with the same three-part bf16 split of P and V.
-// Two subtiles make one 32-column k-step: lane group g supplies k-slots
-// 8g..8g+7, slot s < 4 holding column 4g + s of the first subtile and slot
-// s >= 4 column 16 + 4g + s - 4 of the second; the values are staged with
-// the columns of every 32-column pair in that order (wkmap). 32 value
-// channels per pass (two 16-channel blocks).
-// ---------------------------------------------------------------------------
-constexpr int kWRowsPerBlock = 16 * kWaves;
-constexpr int kWVC = 32;
-
-__host__ __device__ constexpr int wtile_cols(int kp) { return kp <= 256 ? 64 : 32; }
-__host__ __device__ constexpr int wvrow(int kp) { return wtile_cols(kp) + 8; }
-__host__ __device__ constexpr int wkmap(int k) {
-    return (k % 8 < 4) ? 4 * (k / 8) + k % 8 : 16 + 4 * (k / 8) + (k % 8 - 4);
-}
-
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-// Wide-tile score (mirrors the wide half-step): dot products of the lane's
-// 16-column subtile, then + bias_j - Mu_i through one 16x16x4 fp32 MFMA.
-template <int KP>
-__device__ __forceinline__ floatx4 wscore(const float4 *rec, const float *bias, int sub, int lane,
-                                          int g, const half8 (&bh)[KP / 32],
-                                          const half8 (&bl)[KP / 32], float Mu) {
-    constexpr int RC = KP / 4;
-    constexpr int SW = swizzle_mask(RC);
-    const int j = sub * 16 + (lane & 15);
-    const float4 *ap = rec + j * RC;
-    const int sw = j & SW;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < KP / 32; ++c) {
-        const half8 ql = as_half8(ap[(KP / 8 + 4 * c + g) ^ sw]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql, bh[c], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(ap[(4 * c + g) ^ sw]), bl[c], acc,
-                                                     0, 0, 0);
-    }
-#pragma unroll
-    for (int c = 0; c < KP / 32; ++c)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(ap[(4 * c + g) ^ sw]), bh[c], acc,
-                                                     0, 0, 0);
-    const float a0 = lane < 16 ? bias[sub * 16 + lane] : (lane < 32 ? 1.f : 0.f);
-    const float b0 = lane < 16 ? 1.f : (lane < 32 ? -Mu : 0.f);
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b0, acc, 0, 0, 0);
-}
-
-template <int KP, bool RSUM>
-__global__ __launch_bounds__(kThreads) void transport_wide_kernel(
-    const float4 *__restrict__ row_rec, const float *__restrict__ row_bias,
-    const float4 *__restrict__ col4, const float *__restrict__ colb,
-    const float4 *__restrict__ vt, int dv_pad, int k0, int64_t rows, int64_t rows_pad,
-    int tiles_per_split, int ntiles, double *__restrict__ part, double *__restrict__ rpart) {
-    constexpr int RC = KP / 4;
-    constexpr int TC = wtile_cols(KP);
-    constexpr int TILE4 = TC * RC;
-    constexpr int VROW = wvrow(KP);
-    constexpr int PARTW = kWVC * VROW / 8;  // 16-byte chunks of one bf16 part
-    static_assert(TILE4 % (64 * kWaves) == 0, "whole chunk rounds per wave");
-    __shared__ float4 lrec[2][TILE4];
-    __shared__ float lbias[2][TC];
-    __shared__ float4 lvt[2][3 * PARTW];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int g = lane >> 4;
-    const int split = blockIdx.y;
-    const int tbeg = split * tiles_per_split;
-    const int tend = min(tbeg + tiles_per_split, ntiles);
-
-    auto issue_cols = [&](int t, float4 *rec, float *bias) {
-        const float4 *src = col4 + (int64_t)t * TILE4;
-#pragma unroll
-        for (int c = 0; c < TILE4 / 64; c += kWaves)
-            __builtin_amdgcn_global_load_lds(src + (c + wave) * 64 + lane,
-                                             (lds_void *)(rec + (c + wave) * 64), 16, 0, 0);
-        if (wave == kWaves - 1 && lane < TC)
-            __builtin_amdgcn_global_load_lds(colb + (int64_t)t * TC + lane, (lds_void *)bias, 4,
-                                             0, 0);
-    };
-    // Staged values: tile t, part p, channel c at vt[((t*3 + p)*dv_pad + c)*VROW / 8].
-    auto issue_values = [&](int t, float4 *dst) {
-#pragma unroll
-        for (int p = 0; p < 3; ++p)
-            issue_copy<kWaves>(vt + ((int64_t)(t * 3 + p) * dv_pad + k0) * (VROW / 8),
-                               dst + p * PARTW, PARTW, wave, lane);
-    };
-    issue_cols(tbeg, lrec[0], lbias[0]);
-    issue_values(tbeg, lvt[0]);
-
-    const int64_t i = (int64_t)blockIdx.x * kWRowsPerBlock + wave * 16 + (lane & 15);
-    const int64_t ic = i < rows ? i : rows - 1;
-    half8 bh[KP / 32], bl[KP / 32];
-    {
-        const float4 *rr = row_rec + ic * RC;
-#pragma unroll
-        for (int c = 0; c < KP / 32; ++c) {
-            bh[c] = as_half8(rr[4 * c + g]);
-            bl[c] = as_half8(rr[KP / 8 + 4 * c + g]);
-        }
-    }
-    // The bias MFMA adds ghat_j x 1 + 1 x (-Mu): Mu = -fhat_i puts fhat_i in.
-    const float Mu = -row_bias[ic];
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    floatx4 O[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            O[nb][r] = 0.f;
-    float rsum = 0.f;
-
-    for (int t = tbeg; t < tend; ++t) {
-        const int b = (t - tbeg) & 1;
-        if (t + 1 < tend) {
-            issue_cols(t + 1, lrec[b ^ 1], lbias[b ^ 1]);
-            issue_values(t + 1, lvt[b ^ 1]);
-        }
-#pragma unroll
-        for (int u = 0; u < TC / 32; ++u) {
-            floatx4 p0 = wscore<KP>(lrec[b], lbias[b], 2 * u, lane, g, bh, bl, Mu);
-            floatx4 p1 = wscore<KP>(lrec[b], lbias[b], 2 * u + 1, lane, g, bh, bl, Mu);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                p0[r] = hw_exp2(p0[r]);
-                p1[r] = hw_exp2(p1[r]);
-            }
-            if (RSUM)
-                rsum += (p0[0] + p0[1]) + (p0[2] + p0[3]) + ((p1[0] + p1[1]) + (p1[2] + p1[3]));
-            // B operand: slots 0-3 from the first subtile, 4-7 from the second.
-            bf16x8 ph, pm, plo;
-#pragma unroll
-            for (int r = 0; r < 4; r += 2) {
-                bf16x2v h, mm, l;
-                split3_bf16x2(float2v{p0[r], p0[r + 1]}, h, mm, l);
-                ph[r] = h[0]; ph[r + 1] = h[1];
-                pm[r] = mm[0]; pm[r + 1] = mm[1];
-                plo[r] = l[0]; plo[r + 1] = l[1];
-                split3_bf16x2(float2v{p1[r], p1[r + 1]}, h, mm, l);
-                ph[4 + r] = h[0]; ph[5 + r] = h[1];
-                pm[4 + r] = mm[0]; pm[5 + r] = mm[1];
-                plo[4 + r] = l[0]; plo[5 + r] = l[1];
-            }
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const int at = ((nb * 16 + (lane & 15)) * VROW + 32 * u + 8 * g) / 8;
-                const bf16x8 vh = as_bf16x8(lvt[b][at]);
-                const bf16x8 vm = as_bf16x8(lvt[b][PARTW + at]);
-                const bf16x8 vl = as_bf16x8(lvt[b][2 * PARTW + at]);
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vm, pm, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vl, ph, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh, plo, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vm, ph, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh, pm, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vh, ph, acc, 0, 0, 0);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    O[nb][r] += acc[r];
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    }
-
-    // The four lane groups of a row summed different columns.
-    if (RSUM) {
-        float rs = rsum + __shfl_xor(rsum, 16);
-        rs += __shfl_xor(rs, 32);
-        if (g == 0 && i < rows)
-            rpart[(int64_t)split * rows_pad + i] = (double)rs;
-    }
-    // Lane l holds D[c][i] for row i = l % 16 and channels c = 4g + r of each
-    // 16-channel block.
-    if (i < rows) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                part[((int64_t)split * rows_pad + i) * kWVC + nb * 16 + 4 * g + r] =
-                    (double)O[nb][r];
-    }
-}
-
-// Stage the values for the wide kernel: for every column tile t (TC
-// columns), part p (h, m, l) and channel c < dv_pad, the row of VROW bf16
-// vt[((t*3 + p)*dv_pad + c)*VROW + q] = part p of
-// v[t*TC + 32*(q/32) + wkmap(q % 32)][c] for q < TC (zero for missing
-// columns or channels and for the padding q >= TC).
-template <int TC>
-__global__ __launch_bounds__(256) void values_wide_kernel(const float *__restrict__ v, int64_t m,
-                                                          int dv, int dv_pad, int ntiles,
-                                                          __bf16 *__restrict__ vt) {
-    constexpr int VROW = TC + 8;
-    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = (int64_t)ntiles * dv_pad * VROW;
-    if (e >= total)
-        return;
-    const int q = (int)(e % VROW);
-    const int c = (int)((e / VROW) % dv_pad);
-    const int64_t t = e / ((int64_t)VROW * dv_pad);
-    float x = 0.f;
-    if (q < TC) {
-        const int64_t j = t * TC + 32 * (q / 32) + wkmap(q % 32);
-        if (j < m && c < dv)
-            x = v[j * dv + c];
-    }
-    __bf16 h, mm, l;
-    split3_bf16(x, h, mm, l);
-    const int64_t base = (t * 3 * dv_pad + c) * VROW + q;
-    vt[base] = h;
-    vt[base + (int64_t)dv_pad * VROW] = mm;
-    vt[base + 2 * (int64_t)dv_pad * VROW] = l;
-}
-
-MPlan plan_tw(int64_t rows, int64_t cols_pad, int kp) {
-    MPlan p;
-    p.ntiles = (int)(cols_pad / wtile_cols(kp));
-    p.row_blocks = (rows + kWRowsPerBlock - 1) / kWRowsPerBlock;
-    int64_t want = (kTargetBlocks + p.row_blocks - 1) / p.row_blocks;
-    if (want > p.ntiles)
-        want = p.ntiles;
-    if (want > 65535)
-        want = 65535;
-    if (want < 1)
-        want = 1;
-    p.tiles_per_split = (int)((p.ntiles + want - 1) / want);
-    p.nsplit = (p.ntiles + p.tiles_per_split - 1) / p.tiles_per_split;
-    return p;
-}
-
-size_t wide_partial_doubles(int64_t n, int64_t m_pad, bool rowsum, int kp) {
-    const MPlan p = plan_tw(n, m_pad, kp);
-    const size_t d = (size_t)p.nsplit * (size_t)pad_points(n) * (size_t)(kWVC + (rowsum ? 1 : 0));
-    return (d + 31) / 32 * 32;
-}
-
-int wide_padded_channels(int dv) { return (dv + kWVC - 1) / kWVC * kWVC; }
-
-template <int KP>
-hipError_t launch_tw(const float4 *xrec, const float *xbias, const float4 *col4, const float *colb,
-                     const float4 *vt, int dv_pad, int k0, int64_t n, int64_t n_pad,
-                     const MPlan &p, double *part, double *rpart, hipStream_t s) {
-    dim3 grid((unsigned)p.row_blocks, (unsigned)p.nsplit);
-    if (rpart)
-        hipLaunchKernelGGL((transport_wide_kernel<KP, true>), grid, dim3(kThreads), 0, s, xrec,
-                           xbias, col4, colb, vt, dv_pad, k0, n, n_pad, p.tiles_per_split,
-                           p.ntiles, part, rpart);
-    else
-        hipLaunchKernelGGL((transport_wide_kernel<KP, false>), grid, dim3(kThreads), 0, s, xrec,
-                           xbias, col4, colb, vt, dv_pad, k0, n, n_pad, p.tiles_per_split,
-                           p.ntiles, part, rpart);
-    return hipGetLastError();
-}
-
-hipError_t launch_transport_wide(int kp, const float4 *xr, const float *xhat, const float4 *col4,
-                                 const float *yhat, const float *v, int64_t n, int64_t n_pad,
-                                 int64_t m, int64_t m_pad, int dv, double *part, float *out,
-                                 float *rowsum, hipStream_t s) {
-    const MPlan p = plan_tw(n, m_pad, kp);
-    const int dv_pad = wide_padded_channels(dv);
-    const int tc = wtile_cols(kp);
-    double *rpart = rowsum ? part + (size_t)p.nsplit * (size_t)n_pad * (size_t)kWVC : nullptr;
-    __bf16 *vt = reinterpret_cast<__bf16 *>(part + wide_partial_doubles(n, m_pad, rowsum, kp));
-    {
-        const int64_t total = (int64_t)p.ntiles * dv_pad * (tc + 8);
-        const dim3 grid((unsigned)((total + 255) / 256));
-        if (tc == 64)
-            hipLaunchKernelGGL(values_wide_kernel<64>, grid, dim3(256), 0, s, v, m, dv, dv_pad,
-                               p.ntiles, vt);
-        else
-            hipLaunchKernelGGL(values_wide_kernel<32>, grid, dim3(256), 0, s, v, m, dv, dv_pad,
-                               p.ntiles, vt);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-    }
-    const float4 *vt4 = reinterpret_cast<const float4 *>(vt);
-    for (int k0 = 0; k0 < dv; k0 += kWVC) {
-        double *rp = k0 == 0 ? rpart : nullptr;
-        hipError_t e;
-        switch (kp) {
-        case 224: e = launch_tw<224>(xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, p, part, rp, s); break;
-        case 320: e = launch_tw<320>(xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, p, part, rp, s); break;
-        case 448: e = launch_tw<448>(xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, p, part, rp, s); break;
-        default: return hipErrorInvalidValue;
-        }
-        if (e != hipSuccess)
-            return e;
-        const unsigned blocks = (unsigned)((n * kWVC + 255) / 256);
-        hipLaunchKernelGGL(transport_mfma_reduce_kernel<kWVC>, dim3(blocks), dim3(256), 0, s, part,
-                           p.nsplit, n, n_pad, dv, k0, out);
-        if ((e = hipGetLastError()) != hipSuccess)
-            return e;
-        if (rp) {
-            hipLaunchKernelGGL(transport_mfma_reduce_kernel<1>, dim3((unsigned)((n + 255) / 256)),
-                               dim3(256), 0, s, rp, p.nsplit, n, n_pad, 1, 0, rowsum);
-            if ((e = hipGetLastError()) != hipSuccess)
-                return e;
-        }
-    }
-    return hipSuccess;
-}
-
-// ---------------------------------------------------------------------------
-// Record sizes 256, 384 and 512 .. 1024: the score on the stage pipeline of
+// Record sizes above 192 (kp = 224 .. 1024): the score on the stage pipeline of
 // the widest half-step (gemm_pipeline.h) with one row subtile per wave. A
 // workgroup owns 128 rows; wave (rw, cw) forms rows 32 rw .. 32 rw + 31 and
 // columns 64 cw .. 64 cw + 63 of each 128-column block as two 32x32
@@ -719,12 +408,6 @@ hipError_t launch_transport_wide(int kp, const float4 *xr, const float *xhat, co
 // the end, cw = 0 first; fp64 partials per column split as above. No row
 // sums: the x-gradient applies the plan to [y | 1] at these sizes.
 // ---------------------------------------------------------------------------
-// Record sizes taken by transport_gemm_kernel: the multiples of 128 from 256
-// (below kStagedRecordKP its column loads need each half of a record to be
-// whole 16-chunk swizzle groups). At 65536^2 with v = y it applies the plan
-// 1.3x (256), 1.4x (384) and 1.85x (512, where transport_wide_kernel's
-// registers spill) faster than transport_wide_kernel.
-__host__ __device__ constexpr bool gemm_transport(int kp) { return kp >= 256 && kp % 128 == 0; }
 constexpr int kGVC = 64;                    // value channels per pass
 constexpr int kGPart16 = kGVC * kVRow / 8;  // 16-byte chunks of one (tile, part) slab
 constexpr int kGV16 = 2 * 3 * kGPart16;     // of a column block's values
@@ -926,8 +609,11 @@ hipError_t launch_transport_gemm(int kp, const float4 *xr, const float *xhat, co
     for (int k0 = 0; k0 < dv; k0 += kGVC) {
         hipError_t e;
         switch (kp) {
+        case 224: e = launch_tg<224>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, s); break;
         case 256: e = launch_tg<256>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, s); break;
+        case 320: e = launch_tg<320>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, s); break;
         case 384: e = launch_tg<384>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, s); break;
+        case 448: e = launch_tg<448>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, s); break;
         case 512: e = launch_tg<512>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, s); break;
         case 640: e = launch_tg<640>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, s); break;
         case 768: e = launch_tg<768>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, s); break;
@@ -948,18 +634,13 @@ hipError_t launch_transport_gemm(int kp, const float4 *xr, const float *xhat, co
 
 }  // namespace
 
-bool transport_row_sums(int kp) { return !gemm_transport(kp); }
+bool transport_row_sums(int kp) { return kp <= 192; }
 
 size_t transport_mfma_scratch_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum, int kp) {
-    if (gemm_transport(kp)) {
+    if (kp > 192) {
         const size_t vt_bytes = (size_t)(m_pad / kTileCols) * 3 *
                                 (size_t)gemm_padded_channels(dv) * kVRow * sizeof(__bf16);
         return gemm_partial_doubles(n, m_pad) + (vt_bytes + 7) / 8;
-    }
-    if (kp > 192) {
-        const size_t vt_bytes = (size_t)(m_pad / wtile_cols(kp)) * 3 *
-                                (size_t)wide_padded_channels(dv) * wvrow(kp) * sizeof(__bf16);
-        return wide_partial_doubles(n, m_pad, rowsum, kp) + (vt_bytes + 7) / 8;
     }
     const size_t vt_bytes = (size_t)(m_pad / kTileCols) * 3 * (size_t)padded_channels(dv, kp) *
                             kVRow * sizeof(__bf16);
@@ -970,15 +651,11 @@ hipError_t launch_transport_apply_mfma(int kp, const void *xrow, const float *xh
                                        const void *ycol, const float *yhat, const float *v,
                                        int64_t n, int64_t n_pad, int64_t m, int64_t m_pad, int dv,
                                        double *part, float *out, float *rowsum, hipStream_t s) {
-    if (gemm_transport(kp))
+    if (kp > 192)
         return rowsum ? hipErrorInvalidValue
                       : launch_transport_gemm(kp, static_cast<const float4 *>(xrow), xhat,
                                               static_cast<const float4 *>(ycol), yhat, v, n,
                                               n_pad, m, m_pad, dv, part, out, s);
-    if (kp > 192)
-        return launch_transport_wide(kp, static_cast<const float4 *>(xrow), xhat,
-                                     static_cast<const float4 *>(ycol), yhat, v, n, n_pad, m,
-                                     m_pad, dv, part, out, rowsum, s);
     const MPlan p = plan_tm(n, m_pad);
     const int nvb = value_blocks(dv, kp);
     const int vc = 32 * nvb;

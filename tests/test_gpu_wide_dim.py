@@ -14,10 +14,8 @@ Transport on GPU", "Experimentelle Ergebnisse"); the update is the one of
 * at 65536 x 65536 x 256, one half-step from the GPU's own iterate on sampled
   rows (the size the benchmark measures at d = 256);
 * the transport application, barycentric map and x-gradient ("Methodik"
-  section 3): at record sizes 224, 320 and 448 on the same tiles (P.V on
-  16x16x32 bf16 matrix cores, row sums beside the values), at 256, 384 and
-  512 on the widest dimensions' matrix-product tiling (the x-gradient through
-  [y | 1]).
+  section 3), on the widest dimensions' matrix-product tiling at every record
+  size here (the x-gradient through [y | 1]).
 """
 import numpy as np
 import pytest
@@ -187,8 +185,7 @@ def test_wide_transport_apply(n, m, d, dv):
 
 @pytest.mark.parametrize("d", [256, 448])
 def test_wide_map_and_gradient(d):
-    # d = 256: matrix-product tiling, gradient through [y | 1]; d = 448:
-    # 16x16 tiles with the row sums beside the values.
+    # The gradient through [y | 1]: the row sums are the last channel.
     c = make_clouds("feature64_64k", n=900, m=1100, d=d)
     eps = c["eps"][0]
     print(f"barycentric map and x-gradient at d={d}", flush=True)
