@@ -71,7 +71,7 @@ def test_solve_and_plan_stats_capture(d):
     _replays_match(run, [f, g, cost, marg], reset)
 
 
-@pytest.mark.parametrize("d", [3, 64, 256])
+@pytest.mark.parametrize("d", [3, 64, 256, 1024])
 def test_transport_capture(d):
     c = random_clouds(700, 900, d, seed=10 + d, spread=1.0 / np.sqrt(d))
     x, y = dev(c["x"]), dev(c["y"])
