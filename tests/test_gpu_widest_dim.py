@@ -252,6 +252,30 @@ def test_widest_map_and_gradient(d):
     assert eb <= TOL_APPLY and eg <= TOL_APPLY
 
 
+def test_transport_random_shapes():
+    # Seeded random shapes over every record size of the matrix-product
+    # transport (d from 193 to 1024), ragged row and column counts and value
+    # widths; whole outputs against the oracle.
+    from workloads import random_values
+    rng = np.random.default_rng(1234)
+    for case in range(8):
+        d = int(rng.integers(193, 1025))
+        n, m = (int(v) for v in rng.integers(1, 900, size=2))
+        dv = int(rng.integers(1, 200))
+        c = random_clouds(n, m, d, seed=case, spread=1.0 / np.sqrt(d))
+        eps = float(rng.uniform(0.1, 1.0))
+        print(f"case {case}: {n}x{m}x{d}, dv={dv}, eps={eps:.3f}", flush=True)
+        fo, go = oracle.sinkhorn(c["x"], c["y"], c["a"], c["b"], eps, 3)
+        f, g = fo.astype(np.float32), go.astype(np.float32)
+        v = random_values(m, dv, seed=case)
+        out = torch.empty((n, dv), dtype=torch.float32, device=DEV)
+        lds.ot_transport_apply(dev(c["x"]), dev(c["y"]), dev(f), dev(g), eps, dev(v), out)
+        torch.cuda.synchronize()
+        err = rel_inf(out.cpu().numpy(), oracle.transport_apply(c["x"], c["y"], f, g, eps, v))
+        print(f"  rel err {err:.2e}", flush=True)
+        assert err <= TOL_APPLY
+
+
 def test_widest_transport_deterministic():
     from workloads import random_values
     c = random_clouds(300, 700, 1024, seed=9, spread=1.0 / 32)
