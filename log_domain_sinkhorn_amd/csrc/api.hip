@@ -636,9 +636,9 @@ ot_status map_or_grad(const float *x, const float *y, const float *a, const floa
     hipStream_t s = (hipStream_t)stream;
     if (stream_capturing(s))
         return OT_ERROR_NOT_SUPPORTED;
-    const bool beside = choose_layout(d).mfma && transport_row_sums(h3_kp(d));
-    const bool ones = mode == 1 && !beside;  // values [y | 1]
-    const bool rows = mode == 1 && beside;   // row sums beside the values
+    const bool mfma = choose_layout(d).mfma;
+    const bool ones = mode == 1 && !mfma;  // values [y | 1]
+    const bool rows = mode == 1 && mfma;   // row sums beside the values
     const int dv = ones ? d + 1 : d;
     auto carve = [&](Carve &c, float *&v1, float *&w, float *&r) {
         v1 = ones ? c.take<float>((size_t)m * dv * sizeof(float)) : nullptr;

@@ -104,9 +104,7 @@ hipError_t launch_transport_apply(const Layout &L, const void *xrec, const void 
 // Matrix-core variant on split-f16 records (launch_prep_h3 with the hat
 // biases of f and g): x's row records and y's column records; rowsum
 // (nullable) also receives r_i = sum_j P_ij, with rowsum = true in the
-// scratch size, where transport_row_sums(kp) (record sizes up to 192; above,
-// the caller appends a column of ones to the values).
-bool transport_row_sums(int kp);
+// scratch size.
 size_t transport_mfma_scratch_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum,
                                       int kp);
 hipError_t launch_transport_apply_mfma(int kp, const void *xrow, const float *xhat,

@@ -405,8 +405,8 @@ int padded_channels(int dv, int kp) {
 // running fp32 sums). The pipeline restarts for every block: the next
 // block's value copy may only start once every wave is done with these
 // values. The two column waves of a row combine their sums through LDS at
-// the end, cw = 0 first; fp64 partials per column split as above. No row
-// sums: the x-gradient applies the plan to [y | 1] at these sizes.
+// the end, cw = 0 first; fp64 partials per column split as above. With
+// RSUM the row sums come out beside the values on the first pass.
 // ---------------------------------------------------------------------------
 constexpr int kGVC = 64;                    // value channels per pass
 constexpr int kGPart16 = kGVC * kVRow / 8;  // 16-byte chunks of one (tile, part) slab
@@ -415,13 +415,13 @@ constexpr int kGVGroups = kGV16 / 64;       // 64-lane direct loads
 static_assert(kGV16 % 64 == 0, "whole loads");
 static_assert(gemm::kGBN == 2 * kTileCols, "a column block is two value tiles");
 
-template <int KP>
+template <int KP, bool RSUM>
 __global__ __launch_bounds__(64 * gemm::kGW) void transport_gemm_kernel(
     const float4 *__restrict__ row_rec, const float *__restrict__ row_bias,
     const float4 *__restrict__ col4, const float *__restrict__ colb,
     const float4 *__restrict__ vt, int dv_pad, int k0, int64_t rows, int64_t rows_pad,
     int blocks_per_split, int nblocks, int nmap, int nrb, int nsplit,
-    double *__restrict__ part) {
+    double *__restrict__ part, double *__restrict__ rpart) {
     using G = gemm::GTile<1>;
     __shared__ float4 st0[G::Stage4 + gemm::kGTail4];
     __shared__ float4 st1[G::Stage4 + gemm::kGTail4];
@@ -455,10 +455,11 @@ __global__ __launch_bounds__(64 * gemm::kGW) void transport_gemm_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r)
             O[nb][r] = 0.f;
+    float rsum = 0.f;
 
     for (int cb = bbeg; cb < bend; ++cb) {
         // Slab (tile tt, part p) = tt * 3 + p of this block's values holds
-        // kGPart16 chunks at vt[((2 cb + tt) * 3 + p) * dv_pad + k0) * kVRow / 8].
+        // kGPart16 chunks from vt[(((2 cb + tt) * 3 + p) * dv_pad + k0) * kVRow / 8].
         // Issued before the block's stages: the pipeline's first wait
         // (vmcnt of one stage's loads) leaves only younger loads in flight.
 #pragma unroll
@@ -496,6 +497,15 @@ __global__ __launch_bounds__(64 * gemm::kGW) void transport_gemm_kernel(
                         for (int e = 0; e < 4; ++e)
                             P[cs][4 * q + e] = hw_exp2((sum[0][cs][4 * q + e] + bj[e]) + fh);
                     }
+                if (RSUM) {
+                    float c0 = 0.f, c1 = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        c0 += P[0][r];
+                        c1 += P[1][r];
+                    }
+                    rsum += c0 + c1;
+                }
 #pragma unroll
                 for (int cs = 0; cs < 2; ++cs) {
                     const floatx16 &pr = P[cs];
@@ -547,10 +557,18 @@ __global__ __launch_bounds__(64 * gemm::kGW) void transport_gemm_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 red[(rw * 64 + lane) * 32 + nb * 16 + r] = O[nb][r];
+        if (RSUM)
+            reinterpret_cast<float *>(st1)[rw * 64 + lane] = rsum;
     }
     __syncthreads();
     if (cw == 0) {
         const int64_t i = row0 + 32 * rw + li;
+        if (RSUM) {
+            float rs = rsum + reinterpret_cast<const float *>(st1)[rw * 64 + lane];
+            rs += __shfl_xor(rs, 32);
+            if (hl == 0 && i < rows)
+                rpart[(int64_t)split * rows_pad + i] = (double)rs;
+        }
         if (i < rows) {
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
@@ -568,9 +586,12 @@ gemm::GPlan plan_tg(int64_t rows, int64_t cols_pad) {
     return gemm::plan_gemm(rows, cols_pad, gemm::GTile<1>::BM);
 }
 
-size_t gemm_partial_doubles(int64_t n, int64_t m_pad) {
+// Doubles of scratch ahead of the staged values: the value partials, then
+// (rowsum) the row-sum partials, rounded to a 256-byte boundary.
+size_t gemm_partial_doubles(int64_t n, int64_t m_pad, bool rowsum) {
     const gemm::GPlan p = plan_tg(n, m_pad);
-    const size_t d = (size_t)p.nsplit * (size_t)pad_points(n) * (size_t)kGVC;
+    const size_t d =
+        (size_t)p.nsplit * (size_t)pad_points(n) * (size_t)(kGVC + (rowsum ? 1 : 0));
     return (d + 31) / 32 * 32;
 }
 
@@ -579,24 +600,29 @@ int gemm_padded_channels(int dv) { return (dv + kGVC - 1) / kGVC * kGVC; }
 template <int KP>
 hipError_t launch_tg(const gemm::GPlan &p, const float4 *xrec, const float *xbias,
                      const float4 *col4, const float *colb, const float4 *vt, int dv_pad, int k0,
-                     int64_t n, int64_t n_pad, double *part, hipStream_t s) {
-    hipLaunchKernelGGL((transport_gemm_kernel<KP>), dim3((unsigned)(p.row_map * p.nsplit)),
-                       dim3(64 * gemm::kGW), 0, s, xrec, xbias, col4, colb, vt, dv_pad, k0, n,
-                       n_pad, p.blocks_per_split, p.nblocks, (int)p.row_map, (int)p.row_blocks,
-                       p.nsplit, part);
+                     int64_t n, int64_t n_pad, double *part, double *rpart, hipStream_t s) {
+    const dim3 grid((unsigned)(p.row_map * p.nsplit));
+    if (rpart)
+        hipLaunchKernelGGL((transport_gemm_kernel<KP, true>), grid, dim3(64 * gemm::kGW), 0, s,
+                           xrec, xbias, col4, colb, vt, dv_pad, k0, n, n_pad, p.blocks_per_split,
+                           p.nblocks, (int)p.row_map, (int)p.row_blocks, p.nsplit, part, rpart);
+    else
+        hipLaunchKernelGGL((transport_gemm_kernel<KP, false>), grid, dim3(64 * gemm::kGW), 0, s,
+                           xrec, xbias, col4, colb, vt, dv_pad, k0, n, n_pad, p.blocks_per_split,
+                           p.nblocks, (int)p.row_map, (int)p.row_blocks, p.nsplit, part, rpart);
     return hipGetLastError();
 }
 
-// No row sums beside the values here: the x-gradient applies the plan to
-// [y | 1] instead.
 hipError_t launch_transport_gemm(int kp, const float4 *xr, const float *xhat, const float4 *col4,
                                  const float *yhat, const float *v, int64_t n, int64_t n_pad,
                                  int64_t m, int64_t m_pad, int dv, double *part, float *out,
-                                 hipStream_t s) {
+                                 float *rowsum, hipStream_t s) {
     const gemm::GPlan p = plan_tg(n, m_pad);
     const int dv_pad = gemm_padded_channels(dv);
     const int ntiles = (int)(m_pad / kTileCols);
-    __bf16 *vt = reinterpret_cast<__bf16 *>(part + gemm_partial_doubles(n, m_pad));
+    double *rpart = rowsum ? part + (size_t)p.nsplit * (size_t)n_pad * (size_t)kGVC : nullptr;
+    __bf16 *vt =
+        reinterpret_cast<__bf16 *>(part + gemm_partial_doubles(n, m_pad, rowsum != nullptr));
     {
         const int64_t total = (int64_t)ntiles * dv_pad * kVRow;
         hipLaunchKernelGGL(values_bf16x3_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
@@ -607,18 +633,19 @@ hipError_t launch_transport_gemm(int kp, const float4 *xr, const float *xhat, co
     }
     const float4 *vt4 = reinterpret_cast<const float4 *>(vt);
     for (int k0 = 0; k0 < dv; k0 += kGVC) {
+        double *rp = k0 == 0 ? rpart : nullptr;
         hipError_t e;
         switch (kp) {
-        case 224: e = launch_tg<224>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, s); break;
-        case 256: e = launch_tg<256>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, s); break;
-        case 320: e = launch_tg<320>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, s); break;
-        case 384: e = launch_tg<384>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, s); break;
-        case 448: e = launch_tg<448>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, s); break;
-        case 512: e = launch_tg<512>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, s); break;
-        case 640: e = launch_tg<640>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, s); break;
-        case 768: e = launch_tg<768>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, s); break;
-        case 896: e = launch_tg<896>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, s); break;
-        case 1024: e = launch_tg<1024>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, s); break;
+        case 224: e = launch_tg<224>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
+        case 256: e = launch_tg<256>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
+        case 320: e = launch_tg<320>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
+        case 384: e = launch_tg<384>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
+        case 448: e = launch_tg<448>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
+        case 512: e = launch_tg<512>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
+        case 640: e = launch_tg<640>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
+        case 768: e = launch_tg<768>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
+        case 896: e = launch_tg<896>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
+        case 1024: e = launch_tg<1024>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
         default: return hipErrorInvalidValue;
         }
         if (e != hipSuccess)
@@ -628,19 +655,23 @@ hipError_t launch_transport_gemm(int kp, const float4 *xr, const float *xhat, co
                            p.nsplit, n, n_pad, dv, k0, out);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
+        if (rp) {
+            hipLaunchKernelGGL(transport_mfma_reduce_kernel<1>, dim3((unsigned)((n + 255) / 256)),
+                               dim3(256), 0, s, rp, p.nsplit, n, n_pad, 1, 0, rowsum);
+            if ((e = hipGetLastError()) != hipSuccess)
+                return e;
+        }
     }
     return hipSuccess;
 }
 
 }  // namespace
 
-bool transport_row_sums(int kp) { return kp <= 192; }
-
 size_t transport_mfma_scratch_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum, int kp) {
     if (kp > 192) {
         const size_t vt_bytes = (size_t)(m_pad / kTileCols) * 3 *
                                 (size_t)gemm_padded_channels(dv) * kVRow * sizeof(__bf16);
-        return gemm_partial_doubles(n, m_pad) + (vt_bytes + 7) / 8;
+        return gemm_partial_doubles(n, m_pad, rowsum) + (vt_bytes + 7) / 8;
     }
     const size_t vt_bytes = (size_t)(m_pad / kTileCols) * 3 * (size_t)padded_channels(dv, kp) *
                             kVRow * sizeof(__bf16);
@@ -652,10 +683,9 @@ hipError_t launch_transport_apply_mfma(int kp, const void *xrow, const float *xh
                                        int64_t n, int64_t n_pad, int64_t m, int64_t m_pad, int dv,
                                        double *part, float *out, float *rowsum, hipStream_t s) {
     if (kp > 192)
-        return rowsum ? hipErrorInvalidValue
-                      : launch_transport_gemm(kp, static_cast<const float4 *>(xrow), xhat,
-                                              static_cast<const float4 *>(ycol), yhat, v, n,
-                                              n_pad, m, m_pad, dv, part, out, s);
+        return launch_transport_gemm(kp, static_cast<const float4 *>(xrow), xhat,
+                                     static_cast<const float4 *>(ycol), yhat, v, n, n_pad, m,
+                                     m_pad, dv, part, out, rowsum, s);
     const MPlan p = plan_tm(n, m_pad);
     const int nvb = value_blocks(dv, kp);
     const int vc = 32 * nvb;
