@@ -1,6 +1,5 @@
 // The stage pipeline of the kernels tiled like a matrix product: the
-// half-step and the plan statistics for 448 < d <= 1024 (lse_gemm.hip) and
-// the transport application above 192 coordinates (transport_mfma.hip).
+// half-step and the plan statistics for 448 < d <= 1024 (lse_gemm.hip).
 //
 // A workgroup of 8 waves owns 128 RS rows (RS = 1 or 2 row subtiles of 32
 // per wave) and walks its column split in blocks of 128 columns. For each

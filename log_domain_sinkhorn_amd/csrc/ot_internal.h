@@ -105,6 +105,13 @@ hipError_t launch_transport_apply(const Layout &L, const void *xrec, const void 
 // biases of f and g): x's row records and y's column records; rowsum
 // (nullable) also receives r_i = sum_j P_ij, with rowsum = true in the
 // scratch size.
+// Above kp = 192 (dv <= 1024), in transport_rows.hip, with the same records
+// and arguments.
+size_t transport_rows_scratch_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum);
+hipError_t launch_transport_rows(int kp, const void *xrow, const float *xhat, const void *ycol,
+                                 const float *yhat, const float *v, int64_t n, int64_t n_pad,
+                                 int64_t m, int64_t m_pad, int dv, double *part, float *out,
+                                 float *rowsum, hipStream_t s);
 size_t transport_mfma_scratch_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum,
                                       int kp);
 hipError_t launch_transport_apply_mfma(int kp, const void *xrow, const float *xhat,
@@ -169,7 +176,7 @@ hipError_t launch_plan_pass_wide(int kp, bool cost, const void *row_rec, const f
 // 128-byte line per record and stage, chunk q of stage s at 8s + q for hi and
 // 8s + 4 + q for lo), unswizzled, on both sides; only the kernels tiled like
 // a matrix product read them (the widest half-step and statistics pass, and
-// the transport application).
+// the transport application above 192 coordinates).
 constexpr int kStagedRecordKP = 512;
 // For kp in {512, 640, 768, 896, 1024} (448 < d <= 1024) the half-step and
 // the statistics pass are tiled like a matrix product, both sides streamed

@@ -31,11 +31,8 @@
 // Accumulation is fp32 within a workgroup's column range; the column ranges'
 // partials are added in fp64, in split order. No atomics.
 //
-// Two kernels by record size: transport_mfma_kernel (32x32 tiles, a row's
-// operands in registers, kp <= 192) and transport_gemm_kernel (kp = 224 ..
-// 1024: the score on the stage pipeline of the widest half-step, P.V per
-// 128-column block).
-#include "gemm_pipeline.h"
+// Up to kp = 192; larger records go to transport_rows_kernel
+// (transport_rows.hip), every value channel in one pass.
 #include "mfma_common.h"
 
 #include <type_traits>
@@ -388,291 +385,11 @@ int padded_channels(int dv, int kp) {
     return (dv + vc - 1) / vc * vc;
 }
 
-// ---------------------------------------------------------------------------
-// Record sizes above 192 (kp = 224 .. 1024): the score on the stage pipeline of
-// the widest half-step (gemm_pipeline.h) with one row subtile per wave. A
-// workgroup owns 128 rows; wave (rw, cw) forms rows 32 rw .. 32 rw + 31 and
-// columns 64 cw .. 64 cw + 63 of each 128-column block as two 32x32
-// subtiles laid out as above (lane l: row l mod 32; register v: column
-// 8 (v / 4) + 4 (l / 32) + v mod 4). After a block's last stage the epilogue
-// turns the sums into P_ij = 2^((dot + ghat_j) + fhat_i) in registers. The
-// block's staged values (64 channels; its two 64-column tiles in the layout
-// of values_bf16x3_kernel) are copied into their own LDS buffer by direct
-// loads issued just before the block's stages, so they have landed when the
-// pipeline's first wait returns; P.V then runs with the same three-part bf16
-// split as transport_mfma_kernel (6 products per 16 columns and 32
-// channels, each subtile's products from a zero accumulator, added to the
-// running fp32 sums). The pipeline restarts for every block: the next
-// block's value copy may only start once every wave is done with these
-// values. The two column waves of a row combine their sums through LDS at
-// the end, cw = 0 first; fp64 partials per column split as above. With
-// RSUM the row sums come out beside the values on the first pass.
-// ---------------------------------------------------------------------------
-constexpr int kGVC = 64;                    // value channels per pass
-constexpr int kGPart16 = kGVC * kVRow / 8;  // 16-byte chunks of one (tile, part) slab
-constexpr int kGV16 = 2 * 3 * kGPart16;     // of a column block's values
-constexpr int kGVGroups = kGV16 / 64;       // 64-lane direct loads
-static_assert(kGV16 % 64 == 0, "whole loads");
-static_assert(gemm::kGBN == 2 * kTileCols, "a column block is two value tiles");
-
-template <int KP, bool RSUM>
-__global__ __launch_bounds__(64 * gemm::kGW) void transport_gemm_kernel(
-    const float4 *__restrict__ row_rec, const float *__restrict__ row_bias,
-    const float4 *__restrict__ col4, const float *__restrict__ colb,
-    const float4 *__restrict__ vt, int dv_pad, int k0, int64_t rows, int64_t rows_pad,
-    int blocks_per_split, int nblocks, int nmap, int nrb, int nsplit,
-    double *__restrict__ part, double *__restrict__ rpart) {
-    using G = gemm::GTile<1>;
-    __shared__ float4 st0[G::Stage4 + gemm::kGTail4];
-    __shared__ float4 st1[G::Stage4 + gemm::kGTail4];
-    __shared__ float4 st2[G::Stage4 + gemm::kGTail4];
-    __shared__ float4 lv[kGV16];
-    __shared__ float rowv[G::BM];
-    static_assert(sizeof(float) * 4 * 64 * 32 <= sizeof(st0), "combine fits st0");
-
-    int rblk, split;
-    if (!gemm::gemm_block(nmap, nrb, nsplit, rblk, split))
-        return;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int rw = wave & 3;
-    const int cw = wave >> 2;
-    const int hl = lane >> 5;
-    const int li = lane & 31;
-    const int bbeg = split * blocks_per_split;
-    const int bend = min(bbeg + blocks_per_split, nblocks);
-    const int64_t row0 = (int64_t)rblk * G::BM;
-    if (tid < G::BM) {
-        const int64_t i = row0 + tid;
-        rowv[tid] = row_bias[i < rows ? i : rows - 1];
-    }
-    __syncthreads();
-
-    floatx16 O[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            O[nb][r] = 0.f;
-    float rsum = 0.f;
-
-    for (int cb = bbeg; cb < bend; ++cb) {
-        // Slab (tile tt, part p) = tt * 3 + p of this block's values holds
-        // kGPart16 chunks from vt[(((2 cb + tt) * 3 + p) * dv_pad + k0) * kVRow / 8].
-        // Issued before the block's stages: the pipeline's first wait
-        // (vmcnt of one stage's loads) leaves only younger loads in flight.
-#pragma unroll
-        for (int q = 0; q < (kGVGroups + gemm::kGW - 1) / gemm::kGW; ++q) {
-            const int grp = q * gemm::kGW + wave;
-            if (grp < kGVGroups) {
-                const int c = grp * 64 + lane;
-                const int slab = c / kGPart16;
-                const int within = c - slab * kGPart16;
-                const int64_t src =
-                    ((int64_t)(6 * cb + slab) * dv_pad + k0) * (kVRow / 8) + within;
-                __builtin_amdgcn_global_load_lds(vt + src, (lds_void *)(lv + grp * 64), 16, 0, 0);
-            }
-        }
-        // The block epilogue: P in registers, then P.V against tile cw of
-        // the block's values. gemm_stream returns with the workgroup
-        // synchronised, after which the next block's copy may overwrite lv.
-        gemm::gemm_stream<KP, false, 1>(
-            st0, st1, st2, row_rec, col4, colb, nullptr, row0, cb, cb + 1, wave, lane,
-            [&](const float *bias, const float *, floatx16(&sum)[1][2]) {
-                // Both subtiles' P first: the column biases are read before
-                // any of the split's asm statements (after one, the compiler
-                // would wait for every load in flight before reading them).
-                const float fh = rowv[32 * rw + li];
-                const float4 *vs = lv + cw * 3 * kGPart16;
-                floatx16 P[2];
-#pragma unroll
-                for (int cs = 0; cs < 2; ++cs)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float4 b4 = *reinterpret_cast<const float4 *>(
-                            bias + 64 * cw + 32 * cs + 8 * q + 4 * hl);
-                        const float bj[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            P[cs][4 * q + e] = hw_exp2((sum[0][cs][4 * q + e] + bj[e]) + fh);
-                    }
-                if (RSUM) {
-                    float c0 = 0.f, c1 = 0.f;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        c0 += P[0][r];
-                        c1 += P[1][r];
-                    }
-                    rsum += c0 + c1;
-                }
-#pragma unroll
-                for (int cs = 0; cs < 2; ++cs) {
-                    const floatx16 &pr = P[cs];
-                    bf16x8 ph[2], pm[2], plo[2];
-#pragma unroll
-                    for (int r = 0; r < 16; r += 2) {
-                        bf16x2v h, mm, l;
-                        float2v pv = {pr[r], pr[r + 1]};
-                        split3_bf16x2(pv, h, mm, l);
-                        ph[r / 8][r % 8] = h[0];
-                        ph[r / 8][r % 8 + 1] = h[1];
-                        pm[r / 8][r % 8] = mm[0];
-                        pm[r / 8][r % 8 + 1] = mm[1];
-                        plo[r / 8][r % 8] = l[0];
-                        plo[r / 8][r % 8 + 1] = l[1];
-                    }
-#pragma unroll
-                    for (int nb = 0; nb < 2; ++nb) {
-                        floatx16 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
-                                        0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                        const int row = nb * 32 + li;
-#pragma unroll
-                        for (int u = 0; u < 2; ++u) {
-                            const int at = (row * kVRow + cs * 32 + 16 * u + 8 * hl) / 8;
-                            const bf16x8 vh = as_bf16x8(vs[at]);
-                            const bf16x8 vm = as_bf16x8(vs[kGPart16 + at]);
-                            const bf16x8 vl = as_bf16x8(vs[2 * kGPart16 + at]);
-                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vm, pm[u], acc, 0, 0, 0);
-                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, ph[u], acc, 0, 0, 0);
-                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, plo[u], acc, 0, 0, 0);
-                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vm, ph[u], acc, 0, 0, 0);
-                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, pm[u], acc, 0, 0, 0);
-                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, ph[u], acc, 0, 0, 0);
-                        }
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            O[nb][r] += acc[r];
-                    }
-                }
-            });
-    }
-
-    // Lane l of wave (rw, cw) holds row 32 rw + l mod 32 and the channels
-    // k = 32 nb + 8 (r / 4) + 4 (l / 32) + r mod 4 of its registers (nb, r).
-    float *red = reinterpret_cast<float *>(st0);
-    if (cw == 1) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                red[(rw * 64 + lane) * 32 + nb * 16 + r] = O[nb][r];
-        if (RSUM)
-            reinterpret_cast<float *>(st1)[rw * 64 + lane] = rsum;
-    }
-    __syncthreads();
-    if (cw == 0) {
-        const int64_t i = row0 + 32 * rw + li;
-        if (RSUM) {
-            float rs = rsum + reinterpret_cast<const float *>(st1)[rw * 64 + lane];
-            rs += __shfl_xor(rs, 32);
-            if (hl == 0 && i < rows)
-                rpart[(int64_t)split * rows_pad + i] = (double)rs;
-        }
-        if (i < rows) {
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int k = nb * 32 + 8 * (r / 4) + 4 * hl + (r % 4);
-                    part[((int64_t)split * rows_pad + i) * kGVC + k] =
-                        (double)(O[nb][r] + red[(rw * 64 + lane) * 32 + nb * 16 + r]);
-                }
-        }
-    }
-}
-
-gemm::GPlan plan_tg(int64_t rows, int64_t cols_pad) {
-    return gemm::plan_gemm(rows, cols_pad, gemm::GTile<1>::BM);
-}
-
-// Doubles of scratch ahead of the staged values: the value partials, then
-// (rowsum) the row-sum partials, rounded to a 256-byte boundary.
-size_t gemm_partial_doubles(int64_t n, int64_t m_pad, bool rowsum) {
-    const gemm::GPlan p = plan_tg(n, m_pad);
-    const size_t d =
-        (size_t)p.nsplit * (size_t)pad_points(n) * (size_t)(kGVC + (rowsum ? 1 : 0));
-    return (d + 31) / 32 * 32;
-}
-
-int gemm_padded_channels(int dv) { return (dv + kGVC - 1) / kGVC * kGVC; }
-
-template <int KP>
-hipError_t launch_tg(const gemm::GPlan &p, const float4 *xrec, const float *xbias,
-                     const float4 *col4, const float *colb, const float4 *vt, int dv_pad, int k0,
-                     int64_t n, int64_t n_pad, double *part, double *rpart, hipStream_t s) {
-    const dim3 grid((unsigned)(p.row_map * p.nsplit));
-    if (rpart)
-        hipLaunchKernelGGL((transport_gemm_kernel<KP, true>), grid, dim3(64 * gemm::kGW), 0, s,
-                           xrec, xbias, col4, colb, vt, dv_pad, k0, n, n_pad, p.blocks_per_split,
-                           p.nblocks, (int)p.row_map, (int)p.row_blocks, p.nsplit, part, rpart);
-    else
-        hipLaunchKernelGGL((transport_gemm_kernel<KP, false>), grid, dim3(64 * gemm::kGW), 0, s,
-                           xrec, xbias, col4, colb, vt, dv_pad, k0, n, n_pad, p.blocks_per_split,
-                           p.nblocks, (int)p.row_map, (int)p.row_blocks, p.nsplit, part, rpart);
-    return hipGetLastError();
-}
-
-hipError_t launch_transport_gemm(int kp, const float4 *xr, const float *xhat, const float4 *col4,
-                                 const float *yhat, const float *v, int64_t n, int64_t n_pad,
-                                 int64_t m, int64_t m_pad, int dv, double *part, float *out,
-                                 float *rowsum, hipStream_t s) {
-    const gemm::GPlan p = plan_tg(n, m_pad);
-    const int dv_pad = gemm_padded_channels(dv);
-    const int ntiles = (int)(m_pad / kTileCols);
-    double *rpart = rowsum ? part + (size_t)p.nsplit * (size_t)n_pad * (size_t)kGVC : nullptr;
-    __bf16 *vt =
-        reinterpret_cast<__bf16 *>(part + gemm_partial_doubles(n, m_pad, rowsum != nullptr));
-    {
-        const int64_t total = (int64_t)ntiles * dv_pad * kVRow;
-        hipLaunchKernelGGL(values_bf16x3_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
-                           0, s, v, m, dv, dv_pad, ntiles, vt);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-    }
-    const float4 *vt4 = reinterpret_cast<const float4 *>(vt);
-    for (int k0 = 0; k0 < dv; k0 += kGVC) {
-        double *rp = k0 == 0 ? rpart : nullptr;
-        hipError_t e;
-        switch (kp) {
-        case 224: e = launch_tg<224>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
-        case 256: e = launch_tg<256>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
-        case 320: e = launch_tg<320>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
-        case 384: e = launch_tg<384>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
-        case 448: e = launch_tg<448>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
-        case 512: e = launch_tg<512>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
-        case 640: e = launch_tg<640>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
-        case 768: e = launch_tg<768>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
-        case 896: e = launch_tg<896>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
-        case 1024: e = launch_tg<1024>(p, xr, xhat, col4, yhat, vt4, dv_pad, k0, n, n_pad, part, rp, s); break;
-        default: return hipErrorInvalidValue;
-        }
-        if (e != hipSuccess)
-            return e;
-        hipLaunchKernelGGL(transport_mfma_reduce_kernel<kGVC>,
-                           dim3((unsigned)((n * kGVC + 255) / 256)), dim3(256), 0, s, part,
-                           p.nsplit, n, n_pad, dv, k0, out);
-        if ((e = hipGetLastError()) != hipSuccess)
-            return e;
-        if (rp) {
-            hipLaunchKernelGGL(transport_mfma_reduce_kernel<1>, dim3((unsigned)((n + 255) / 256)),
-                               dim3(256), 0, s, rp, p.nsplit, n, n_pad, 1, 0, rowsum);
-            if ((e = hipGetLastError()) != hipSuccess)
-                return e;
-        }
-    }
-    return hipSuccess;
-}
-
 }  // namespace
 
 size_t transport_mfma_scratch_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum, int kp) {
-    if (kp > 192) {
-        const size_t vt_bytes = (size_t)(m_pad / kTileCols) * 3 *
-                                (size_t)gemm_padded_channels(dv) * kVRow * sizeof(__bf16);
-        return gemm_partial_doubles(n, m_pad, rowsum) + (vt_bytes + 7) / 8;
-    }
+    if (kp > 192)
+        return transport_rows_scratch_doubles(n, m_pad, dv, rowsum);
     const size_t vt_bytes = (size_t)(m_pad / kTileCols) * 3 * (size_t)padded_channels(dv, kp) *
                             kVRow * sizeof(__bf16);
     return partial_doubles(n, m_pad, dv, rowsum, kp) + (vt_bytes + 7) / 8;
@@ -683,9 +400,8 @@ hipError_t launch_transport_apply_mfma(int kp, const void *xrow, const float *xh
                                        int64_t n, int64_t n_pad, int64_t m, int64_t m_pad, int dv,
                                        double *part, float *out, float *rowsum, hipStream_t s) {
     if (kp > 192)
-        return launch_transport_gemm(kp, static_cast<const float4 *>(xrow), xhat,
-                                     static_cast<const float4 *>(ycol), yhat, v, n, n_pad, m,
-                                     m_pad, dv, part, out, rowsum, s);
+        return launch_transport_rows(kp, xrow, xhat, ycol, yhat, v, n, n_pad, m, m_pad, dv, part,
+                                     out, rowsum, s);
     const MPlan p = plan_tm(n, m_pad);
     const int nvb = value_blocks(dv, kp);
     const int vc = 32 * nvb;
