@@ -523,8 +523,9 @@ def run_transport(name, torch, lds, rates, reps=10, warm=3):
         # once (3*kp/16 f16 MFMAs of 32 cycles + one fp32 MFMA of 64) and P.V
         # (12 bf16 MFMAs of 32 cycles per 32 value channels: 2 column chunks
         # x 6 split products), at 2.4 GHz on 1024 SIMDs; frac = that time /
-        # the measured call, so the kernels' score recomputation per pass of
-        # value channels (32 or 64 channels a pass) counts against it.
+        # the measured call, so the 32x32 kernel's score recomputation per
+        # pass of 32 value channels (d <= 192) counts against it; above 192
+        # the score is formed once for every channel.
         kp = h3_kp(d)
         cycles = 3 * kp // 16 * 32 + 64 + 12 * 32 * ((d + 31) // 32)
         model_ms = (n / 32) * (m / 32) * cycles / (1024 * 2.4e9) * 1e3

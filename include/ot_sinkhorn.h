@@ -79,9 +79,9 @@ typedef enum {
 #define OT_MAX_DIM 1024
 
 /* Largest d of the transport calls (ot_transport_apply, ot_barycentric_map,
- * ot_cost_gradient_x): all of OT_MAX_DIM. Above 512 the plan's terms come
- * from the kernels tiled like a matrix product and the values are applied
- * 64 channels per pass over the columns. */
+ * ot_cost_gradient_x): all of OT_MAX_DIM. Above 192 one pass over the
+ * columns forms each score once and applies it to every value channel
+ * (up to 1024 channels). */
 #define OT_MAX_TRANSPORT_DIM 1024
 
 /* Human-readable name of a status code (static string, never NULL). */

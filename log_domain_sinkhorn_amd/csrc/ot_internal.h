@@ -174,9 +174,9 @@ hipError_t launch_plan_pass_wide(int kp, bool cost, const void *row_rec, const f
 // Above this many coordinates per record the split-f16 records are staged:
 // each 32-coordinate stage's 4 hi and 4 lo 16-byte chunks side by side (one
 // 128-byte line per record and stage, chunk q of stage s at 8s + q for hi and
-// 8s + 4 + q for lo), unswizzled, on both sides; only the kernels tiled like
-// a matrix product read them (the widest half-step and statistics pass, and
-// the transport application above 192 coordinates).
+// 8s + 4 + q for lo), unswizzled, on both sides; only the kernels that stream
+// both sides through LDS in coordinate stages read them (the widest half-step
+// and statistics pass, and the transport application above 192 coordinates).
 constexpr int kStagedRecordKP = 512;
 // For kp in {512, 640, 768, 896, 1024} (448 < d <= 1024) the half-step and
 // the statistics pass are tiled like a matrix product, both sides streamed

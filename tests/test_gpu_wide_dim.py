@@ -14,8 +14,8 @@ Transport on GPU", "Experimentelle Ergebnisse"); the update is the one of
 * at 65536 x 65536 x 256, one half-step from the GPU's own iterate on sampled
   rows (the size the benchmark measures at d = 256);
 * the transport application, barycentric map and x-gradient ("Methodik"
-  section 3), on the widest dimensions' matrix-product tiling at every record
-  size here (the x-gradient through [y | 1]).
+  section 3), on the one-pass transport kernel at every record size here
+  (the x-gradient with the row sums beside the values).
 """
 import numpy as np
 import pytest
@@ -185,7 +185,7 @@ def test_wide_transport_apply(n, m, d, dv):
 
 @pytest.mark.parametrize("d", [256, 448])
 def test_wide_map_and_gradient(d):
-    # The gradient through [y | 1]: the row sums are the last channel.
+    # The x-gradient takes the row sums beside the values in the same pass.
     c = make_clouds("feature64_64k", n=900, m=1100, d=d)
     eps = c["eps"][0]
     print(f"barycentric map and x-gradient at d={d}", flush=True)

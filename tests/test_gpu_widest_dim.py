@@ -213,8 +213,8 @@ TOL_APPLY = 5e-5  # the transport tests' bound (see test_gpu_transport.py)
                                       (257, 1, 1024, 1024), (129, 257, 1000, 64),
                                       (600, 500, 513, 130)])
 def test_widest_transport_apply(n, m, d, dv):
-    # out_i = sum_j P_ij v_j with P from the matrix-product tiling; oracle
-    # potentials, random values (several passes of 64 channels, ragged ends).
+    # out_i = sum_j P_ij v_j from the one-pass transport kernel; oracle
+    # potentials, random values (256 to 1024 padded channels, ragged ends).
     from workloads import random_values
     c = random_clouds(n, m, d, seed=n + m + d, spread=1.0 / np.sqrt(d))
     eps = 0.3
@@ -233,8 +233,7 @@ def test_widest_transport_apply(n, m, d, dv):
 
 @pytest.mark.parametrize("d", [640, 1024])
 def test_widest_map_and_gradient(d):
-    # The x-gradient applies the plan to [y | 1] at these sizes (the row sums
-    # come out as the last channel).
+    # The x-gradient takes the row sums beside the values in the same pass.
     c = make_clouds("feature64_64k", n=600, m=700, d=d)
     eps = c["eps"][0]
     print(f"barycentric map and x-gradient at d={d}", flush=True)
