@@ -15,16 +15,18 @@
 // reloads of the pipeline in gemm_pipeline.h); wave w forms the 32x32 subtile
 // of columns 32w .. 32w + 31
 // (chains from zero per stage, flushed into fp32 sums, as in the other
-// kernels). After the block's last stage each wave writes its P_ij =
-// 2^((dot + ghat_j) + fhat_i) to an LDS tile of 32 rows x 256 columns; then
+// kernels). After the block's last stage each wave splits its P_ij =
+// 2^((dot + ghat_j) + fhat_i) into three bf16 parts (h + m + l, each rounded
+// once) and writes them to three LDS planes of 32 rows x 256 columns; then
 // every wave multiplies the whole tile by its channels of the block's values:
 // B operand 8 consecutive columns of P (one row), A operand 8 consecutive
-// columns of one channel of v, both split into three bf16 parts (h.h + h.m +
-// m.h + h.l + l.h + m.m, each 16-column product from a zero accumulator, added
-// to the running fp32 sums). The values are read from L2, fp32, in blocks of
-// 16 columns x dv_pad channels (a wave's 32 channels x 16 columns are 2 KiB in
-// a row). With RSUM the row sums come out too. Partials per column split in
-// fp64, added in split order.
+// columns of one channel of v, both in three parts (h.h + h.m + m.h + h.l +
+// l.h + m.m, each 16-column product from a zero accumulator, added to the
+// running fp32 sums). The values are split the same way once per call
+// (values_split_kernel) and read from L2 in blocks of 16 columns x dv_pad
+// channels x 3 parts (a wave's 32 channels x 16 columns of one part are 1 KiB
+// in a row), kTVD six-product steps ahead of their use. With RSUM the row sums come
+// out too. Partials per column split in fp64, added in split order.
 //
 // It replaced a kernel on the same stage pipeline with 128-row workgroups,
 // which had to form the score again for every 64 value channels.
@@ -42,39 +44,39 @@ constexpr int kTW = 8;                // waves per workgroup
 constexpr int kTR = 32;               // rows per workgroup
 constexpr int kTN = 256;              // columns per block (32 per wave)
 constexpr int kTStage4 = (kTR + kTN) * 8;  // 16-byte chunks per stage
-constexpr int kTTail4 = kTN / 4;      // column biases behind the records
+constexpr int kTPP = kTN / 8 + 1;     // 16-byte chunks per row of a P plane (padded)
 constexpr int kTLoads = 5;            // direct loads per wave and stage
-constexpr int kTPRow = kTN + 4;       // floats per row of P in LDS
+constexpr int kTVD = 4;               // value loads in flight, in 6-product steps
 constexpr int kTKS = 32;              // coordinates per stage
 constexpr int kTTargetBlocks = 2048;
 
 typedef __bf16 bf16x8t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2t __attribute__((ext_vector_type(2)));
 typedef float float2t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int tslot(int r, int t) { return r * 8 + (t ^ ((r ^ (r >> 3)) & 7)); }
 
-// Split 8 fp32 values into three bf16 parts (h + m + l), each rounded once.
-__device__ __forceinline__ void split8(float4 a, float4 b, bf16x8t &h, bf16x8t &m, bf16x8t &l) {
-    const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int k = 0; k < 8; k += 2) {
-        float2t x = {v[k], v[k + 1]};
-        asm volatile("" : "+v"(x));
-        const bf16x2t xh = __builtin_convertvector(x, bf16x2t);
-        float2t r = x - __builtin_convertvector(xh, float2t);
-        asm volatile("" : "+v"(r));
-        const bf16x2t xm = __builtin_convertvector(r, bf16x2t);
-        float2t r2 = r - __builtin_convertvector(xm, float2t);
-        asm volatile("" : "+v"(r2));
-        const bf16x2t xl = __builtin_convertvector(r2, bf16x2t);
-        h[k] = xh[0];
-        h[k + 1] = xh[1];
-        m[k] = xm[0];
-        m[k + 1] = xm[1];
-        l[k] = xl[0];
-        l[k + 1] = xl[1];
-    }
+// Split two fp32 values into three bf16 parts (h + m + l, each rounded once:
+// h = bf16(x), m = bf16(x - h), l = bf16(x - h - m)).
+__device__ __forceinline__ void split2(float2t x, bf16x2t &h, bf16x2t &m, bf16x2t &l) {
+    asm volatile("" : "+v"(x));
+    h = __builtin_convertvector(x, bf16x2t);
+    float2t r = x - __builtin_convertvector(h, float2t);
+    asm volatile("" : "+v"(r));
+    m = __builtin_convertvector(r, bf16x2t);
+    float2t r2 = r - __builtin_convertvector(m, float2t);
+    asm volatile("" : "+v"(r2));
+    l = __builtin_convertvector(r2, bf16x2t);
+}
+
+__device__ __forceinline__ void split4(float4 a, bf16x4t &h, bf16x4t &m, bf16x4t &l) {
+    bf16x2t h0, m0, l0, h1, m1, l1;
+    split2(float2t{a.x, a.y}, h0, m0, l0);
+    split2(float2t{a.z, a.w}, h1, m1, l1);
+    h = bf16x4t{h0[0], h0[1], h1[0], h1[1]};
+    m = bf16x4t{m0[0], m0[1], m1[0], m1[1]};
+    l = bf16x4t{l0[0], l0[1], l1[0], l1[1]};
 }
 
 // Direct loads of stage s of the block at col0 into buf: row record r
@@ -84,13 +86,13 @@ __device__ __forceinline__ void split8(float4 a, float4 b, bf16x8t &h, bf16x8t &
 // above kStagedRecordKP hold each stage's 8 chunks at 8s .. 8s + 7; below it
 // the stage's hi chunks are 4s .. 4s + 3 and its lo chunks KP/8 + 4s ..,
 // column chunk q of point j stored at q ^ (j & SW). With the last stage,
-// waves 0-3 also load the block's 256 column biases behind the records.
+// waves 0-3 also load the block's 256 column biases into bias.
 template <int KP>
 __device__ __forceinline__ void t_issue(const float4 *__restrict__ row4,
                                         const float4 *__restrict__ col4,
                                         const float *__restrict__ colb, int64_t row0,
-                                        int64_t col0, int s, bool last, float4 *buf, int wave,
-                                        int lane) {
+                                        int64_t col0, int s, bool last, float4 *buf,
+                                        float *bias, int wave, int lane) {
     constexpr int RC = KP / 4;
     constexpr bool STAGED = KP > kStagedRecordKP;
     if (lane < 32) {
@@ -116,23 +118,26 @@ __device__ __forceinline__ void t_issue(const float4 *__restrict__ row4,
     if (last && wave < kTN / 64)
         __builtin_amdgcn_global_load_lds(
             colb + col0 + 64 * wave + lane,
-            (lds_void *)(reinterpret_cast<float *>(buf + kTStage4) + 64 * wave), 4, 0, 0);
+            (lds_void *)(bias + 64 * wave), 4, 0, 0);
 }
 
 template <int KP, int NB, bool RSUM>
 __global__ __launch_bounds__(64 * kTW) void transport_rows_kernel(
     const float4 *__restrict__ row_rec, const float *__restrict__ row_bias,
     const float4 *__restrict__ col4, const float *__restrict__ colb,
-    const float4 *__restrict__ vb, int dv_pad, int64_t rows, int64_t rows_pad, int nrb,
+    const bf16x8t *__restrict__ vb, int dv_pad, int64_t rows, int64_t rows_pad, int nrb,
     int blocks_per_split, int nblocks, double *__restrict__ part, double *__restrict__ rpart) {
     constexpr int NS = KP / kTKS;
     static_assert(KP % kTKS == 0 && NS >= 2, "whole stages");
-    __shared__ float4 st0[kTStage4 + kTTail4];
-    __shared__ float4 st1[kTStage4 + kTTail4];
-    __shared__ float4 st2[kTStage4 + kTTail4];
-    __shared__ float4 pl4[kTR * kTPRow / 4];
+    __shared__ float4 st0[kTStage4];
+    __shared__ float4 st1[kTStage4];
+    __shared__ float4 st2[kTStage4];
+    // The column biases of the block in flight: loaded with its last stage,
+    // at least two stages after the previous block's epilogue read them.
+    __shared__ float4 bias4[kTN / 4];
+    float *const biasb = reinterpret_cast<float *>(bias4);
+    __shared__ bf16x8t pp[3 * kTR * kTPP];  // P in 3 planes of 32 rows x kTPP chunks
     __shared__ float rowv[kTR];
-    float *pl = reinterpret_cast<float *>(pl4);
     float4 *const stg[3] = {st0, st1, st2};
 
     const int L = (int)blockIdx.x;
@@ -146,7 +151,9 @@ __global__ __launch_bounds__(64 * kTW) void transport_rows_kernel(
     const int bbeg = split * blocks_per_split;
     const int bend = min(bbeg + blocks_per_split, nblocks);
     const int64_t row0 = (int64_t)rb * kTR;
-    const int c0 = 32 * NB * wave;  // this wave's first value channel
+    // This wave's first value channel (wave-uniform, so that the value
+    // addresses are a scalar base plus one per-lane offset).
+    const int c0 = 32 * NB * __builtin_amdgcn_readfirstlane(wave);
     if (tid < kTR) {
         const int64_t i = row0 + tid;
         rowv[tid] = row_bias[i < rows ? i : rows - 1];
@@ -166,7 +173,7 @@ __global__ __launch_bounds__(64 * kTW) void transport_rows_kernel(
         constexpr int b = decltype(bc)::value;
         const int cb = bbeg + t / NS;
         t_issue<KP>(row_rec, col4, colb, row0, (int64_t)cb * kTN, t % NS, t % NS == NS - 1,
-                    stg[b], wave, lane);
+                    stg[b], biasb, wave, lane);
     };
     issue(0, std::integral_constant<int, 0>{});
     issue(1, std::integral_constant<int, 1>{});
@@ -179,6 +186,7 @@ __global__ __launch_bounds__(64 * kTW) void transport_rows_kernel(
     // The block's P tile times this wave's channels of the block's values.
     auto epilogue = [&](const float *bias, int cb) __attribute__((always_inline)) {
         const float fh = rowv[li];
+        bf16x4t *pw = reinterpret_cast<bf16x4t *>(pp);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int col = 32 * wave + 8 * q + 4 * hl;
@@ -190,53 +198,61 @@ __global__ __launch_bounds__(64 * kTW) void transport_rows_kernel(
             p4.w = hw_exp2((sum[4 * q + 3] + b4.w) + fh);
             if (RSUM)
                 rsum += (p4.x + p4.y) + (p4.z + p4.w);
-            *reinterpret_cast<float4 *>(pl + li * kTPRow + col) = p4;
+            bf16x4t h4, m4, l4;
+            split4(p4, h4, m4, l4);
+            const int slot = (li * kTPP + 4 * wave + q) * 2 + hl;
+            pw[slot] = h4;
+            pw[kTR * kTPP * 2 + slot] = m4;
+            pw[2 * kTR * kTPP * 2 + slot] = l4;
         }
         __syncthreads();  // the whole P tile is in LDS
-        const float4 *vblk = vb + ((int64_t)cb * (kTN / 16) * dv_pad) * 4;
-        // Values of 16-column block kc, channel c0 + 32 nb + li, columns
-        // 8 hl .. 8 hl + 7; loaded one block ahead of their products.
-        auto load_v = [&](int kc, float4 (&dst)[NB][2]) __attribute__((always_inline)) {
-            const float4 *vk = vblk + (int64_t)kc * dv_pad * 4;
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const float4 *va = vk + (int64_t)(c0 + 32 * nb + li) * 4 + 2 * hl;
-                dst[nb][0] = va[0];
-                dst[nb][1] = va[1];
-            }
+        // 96 bytes per (16-column block, channel): 3 parts x 2 halves.
+        const char *vblk =
+            reinterpret_cast<const char *>(vb) + ((int64_t)cb * (kTN / 16) * dv_pad + c0) * 96;
+        const unsigned voff = (unsigned)(li * 96 + hl * 16);
+        // Step st = kc * NB + nb: the three parts of channel c0 + 32 nb + li,
+        // columns 16 kc + 8 hl .. + 7; loaded kTVD steps ahead of their use.
+        auto load_v = [&](int st, bf16x8t (&dst)[3]) __attribute__((always_inline)) {
+            const int kc = st / NB, nb = st % NB;
+            const char *u = vblk + ((int64_t)kc * dv_pad + 32 * nb) * 96;
+            dst[0] = *reinterpret_cast<const bf16x8t *>(u + voff);
+            dst[1] = *reinterpret_cast<const bf16x8t *>(u + voff + 32);
+            dst[2] = *reinterpret_cast<const bf16x8t *>(u + voff + 64);
         };
-        float4 vcur[NB][2], vnxt[NB][2];
-        load_v(0, vcur);
+        constexpr int NST = (kTN / 16) * NB;
+        bf16x8t ring[kTVD + 1][3];
 #pragma unroll
-        for (int kc = 0; kc < kTN / 16; ++kc) {
-            if (kc + 1 < kTN / 16)
-                load_v(kc + 1, vnxt);
-            const float4 *pr = reinterpret_cast<const float4 *>(pl + li * kTPRow + 16 * kc + 8 * hl);
-            bf16x8t ph, pm, plo;
-            split8(pr[0], pr[1], ph, pm, plo);
+        for (int st = 0; st < kTVD; ++st)
+            load_v(st, ring[st]);
+        bf16x8t ph, pm, plo;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                bf16x8t vh, vm, vl;
-                split8(vcur[nb][0], vcur[nb][1], vh, vm, vl);
-                floatx16 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
-                                0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vm, pm, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, ph, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, plo, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vm, ph, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, pm, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, ph, acc, 0, 0, 0);
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    O[nb][r] += acc[r];
+        for (int st = 0; st < NST; ++st) {
+            // Keep each step's loads and products where they are written:
+            // hoisted loads would hold every step's values at once.
+            __builtin_amdgcn_sched_barrier(0);
+            if (st + kTVD < NST)
+                load_v(st + kTVD, ring[(st + kTVD) % (kTVD + 1)]);
+            const int kc = st / NB, nb = st % NB;
+            if (nb == 0) {
+                const int slot = li * kTPP + 2 * kc + hl;
+                ph = pp[slot];
+                pm = pp[kTR * kTPP + slot];
+                plo = pp[2 * kTR * kTPP + slot];
             }
-            if (kc + 1 < kTN / 16) {
+            const bf16x8t vh = ring[st % (kTVD + 1)][0];
+            const bf16x8t vm = ring[st % (kTVD + 1)][1];
+            const bf16x8t vl = ring[st % (kTVD + 1)][2];
+            floatx16 acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
+                            0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vm, pm, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, ph, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, plo, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vm, ph, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, pm, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vh, ph, acc, 0, 0, 0);
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    vcur[nb][0] = vnxt[nb][0];
-                    vcur[nb][1] = vnxt[nb][1];
-                }
-            }
+            for (int r = 0; r < 16; ++r)
+                O[nb][r] += acc[r];
         }
     };
 
@@ -267,7 +283,7 @@ __global__ __launch_bounds__(64 * kTW) void transport_rows_kernel(
         for (int v = 0; v < 16; ++v)
             sum[v] += acc[v];
         if (t % NS == NS - 1) {
-            epilogue(reinterpret_cast<const float *>(buf + kTStage4), bbeg + t / NS);
+            epilogue(biasb, bbeg + t / NS);
 #pragma unroll
             for (int v = 0; v < 16; ++v)
                 sum[v] = 0.f;
@@ -315,19 +331,40 @@ __global__ __launch_bounds__(64 * kTW) void transport_rows_kernel(
     }
 }
 
-// vb[((j / 16) * dv_pad + c) * 16 + j % 16] = v[j][c] (0 beyond m or dv).
-__global__ __launch_bounds__(256) void values_blocked_kernel(const float *__restrict__ v,
-                                                             int64_t m, int dv, int dv_pad,
-                                                             int64_t m_pad,
-                                                             float *__restrict__ vb) {
+// The values in three bf16 parts, in blocks of 16 columns: part p of
+// v[16 jb + 8 h + k][c] (k < 8; 0 beyond m or dv) is element k of
+// vb[((jb * dv_pad + c) * 3 + p) * 2 + h]. One thread per (jb, c, h).
+__global__ __launch_bounds__(256) void values_split_kernel(const float *__restrict__ v,
+                                                           int64_t m, int dv, int dv_pad,
+                                                           int64_t m_pad,
+                                                           bf16x8t *__restrict__ vb) {
     const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= m_pad * dv_pad)
+    if (e >= m_pad / 8 * dv_pad)
         return;
-    const int q = (int)(e % 16);
-    const int c = (int)((e / 16) % dv_pad);
-    const int64_t jb = e / (16 * (int64_t)dv_pad);
-    const int64_t j = jb * 16 + q;
-    vb[e] = (j < m && c < dv) ? v[j * dv + c] : 0.f;
+    const int h = (int)(e & 1);
+    const int c = (int)((e >> 1) % dv_pad);
+    const int64_t jb = (e >> 1) / dv_pad;
+    const int64_t j0 = jb * 16 + 8 * h;
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        x[k] = (j0 + k < m && c < dv) ? v[(j0 + k) * dv + c] : 0.f;
+    bf16x8t ph, pm, pl;
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+        bf16x2t xh, xm, xl;
+        split2(float2t{x[k], x[k + 1]}, xh, xm, xl);
+        ph[k] = xh[0];
+        ph[k + 1] = xh[1];
+        pm[k] = xm[0];
+        pm[k + 1] = xm[1];
+        pl[k] = xl[0];
+        pl[k + 1] = xl[1];
+    }
+    bf16x8t *o = vb + ((jb * dv_pad + c) * 3) * 2 + h;
+    o[0] = ph;
+    o[2] = pm;
+    o[4] = pl;
 }
 
 // out[i * dv + k] = sum over splits of part[s][i][k] (k < dv), in split order.
@@ -375,7 +412,7 @@ size_t rows_partial_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum) {
 
 template <int KP, int NB>
 hipError_t launch_tr(const RPlan &p, const float4 *xr, const float *xhat, const float4 *col4,
-                     const float *yhat, const float4 *vb, int dv_pad, int64_t n, int64_t n_pad,
+                     const float *yhat, const bf16x8t *vb, int dv_pad, int64_t n, int64_t n_pad,
                      double *part, double *rpart, hipStream_t s) {
     const dim3 grid((unsigned)((int64_t)p.nrb * p.nsplit));
     if (rpart)
@@ -391,7 +428,7 @@ hipError_t launch_tr(const RPlan &p, const float4 *xr, const float *xhat, const 
 
 template <int KP>
 hipError_t launch_tr_nb(int nb, const RPlan &p, const float4 *xr, const float *xhat,
-                        const float4 *col4, const float *yhat, const float4 *vb, int dv_pad,
+                        const float4 *col4, const float *yhat, const bf16x8t *vb, int dv_pad,
                         int64_t n, int64_t n_pad, double *part, double *rpart, hipStream_t s) {
     switch (nb) {
     case 1: return launch_tr<KP, 1>(p, xr, xhat, col4, yhat, vb, dv_pad, n, n_pad, part, rpart, s);
@@ -405,8 +442,8 @@ hipError_t launch_tr_nb(int nb, const RPlan &p, const float4 *xr, const float *x
 }  // namespace
 
 size_t transport_rows_scratch_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum) {
-    const size_t vb = (size_t)m_pad * (size_t)rows_channels(dv);  // floats
-    return rows_partial_doubles(n, m_pad, dv, rowsum) + (vb + 1) / 2;
+    const size_t vb = (size_t)m_pad * (size_t)rows_channels(dv) * 6;  // bytes, 3 bf16 parts
+    return rows_partial_doubles(n, m_pad, dv, rowsum) + (vb + 7) / 8;
 }
 
 hipError_t launch_transport_rows(int kp, const void *xrow, const float *xhat, const void *ycol,
@@ -419,18 +456,17 @@ hipError_t launch_transport_rows(int kp, const void *xrow, const float *xhat, co
         return hipErrorInvalidValue;
     const RPlan p = plan_rows(n, m_pad);
     double *rpart = rowsum ? part + (size_t)p.nsplit * (size_t)n_pad * (size_t)dv_pad : nullptr;
-    float *vbf = reinterpret_cast<float *>(part + rows_partial_doubles(n, m_pad, dv, rowsum));
+    bf16x8t *vb = reinterpret_cast<bf16x8t *>(part + rows_partial_doubles(n, m_pad, dv, rowsum));
     {
-        const int64_t total = m_pad * dv_pad;
-        hipLaunchKernelGGL(values_blocked_kernel, dim3((unsigned)((total + 255) / 256)),
-                           dim3(256), 0, s, v, m, dv, dv_pad, m_pad, vbf);
+        const int64_t total = m_pad / 8 * dv_pad;
+        hipLaunchKernelGGL(values_split_kernel, dim3((unsigned)((total + 255) / 256)),
+                           dim3(256), 0, s, v, m, dv, dv_pad, m_pad, vb);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
     const float4 *xr = static_cast<const float4 *>(xrow);
     const float4 *col4 = static_cast<const float4 *>(ycol);
-    const float4 *vb = reinterpret_cast<const float4 *>(vbf);
     hipError_t e;
     switch (kp) {
     case 224: e = launch_tr_nb<224>(nb, p, xr, xhat, col4, yhat, vb, dv_pad, n, n_pad, part, rpart, s); break;
