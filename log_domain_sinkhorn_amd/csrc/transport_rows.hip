@@ -48,7 +48,7 @@ constexpr int kTPP = kTN / 8 + 1;     // 16-byte chunks per row of a P plane (pa
 constexpr int kTLoads = 5;            // direct loads per wave and stage
 constexpr int kTVD = 4;               // value loads in flight, in 6-product steps
 constexpr int kTKS = 32;              // coordinates per stage
-constexpr int kTTargetBlocks = 2048;
+constexpr int kTTargetBlocks = 4096;
 
 typedef __bf16 bf16x8t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4t __attribute__((ext_vector_type(4)));
@@ -387,17 +387,39 @@ struct RPlan {
     int nrb, nblocks, blocks_per_split, nsplit;
 };
 
+// One workgroup fits a CU (its LDS), so the launch runs in rounds of kTCUs
+// workgroups. The split count is at least ceil(kTTargetBlocks / row blocks)
+// (measured at 65536 rows and d = 512: one split 53.9 ms, two 48.2); from
+// there up to twice that (at least 8) it takes the count with the fewest
+// rounds x blocks per workgroup, the smaller on a tie (50000 rows x 196
+// blocks: 7 splits, 43 rounds x 28 blocks; 2 splits took 63.0 ms, 7 55.4).
+constexpr int64_t kTCUs = 256;
+
 RPlan plan_rows(int64_t rows, int64_t cols_pad) {
     RPlan p;
     p.nrb = (int)((rows + kTR - 1) / kTR);
     p.nblocks = (int)(cols_pad / kTN);
-    int64_t want = (kTTargetBlocks + p.nrb - 1) / p.nrb;
-    if (want > p.nblocks)
-        want = p.nblocks;
-    if (want < 1)
-        want = 1;
-    p.blocks_per_split = (int)((p.nblocks + want - 1) / want);
-    p.nsplit = (p.nblocks + p.blocks_per_split - 1) / p.blocks_per_split;
+    int64_t lo = (kTTargetBlocks + p.nrb - 1) / p.nrb;
+    if (lo > p.nblocks)
+        lo = p.nblocks;
+    if (lo < 1)
+        lo = 1;
+    int64_t hi = 2 * lo < 8 ? 8 : 2 * lo;
+    if (hi > p.nblocks)
+        hi = p.nblocks;
+    int64_t best = -1;
+    p.blocks_per_split = p.nblocks;
+    p.nsplit = 1;
+    for (int64_t ns = lo; ns <= hi; ++ns) {
+        const int64_t bps = (p.nblocks + ns - 1) / ns;
+        const int64_t nsp = (p.nblocks + bps - 1) / bps;
+        const int64_t cost = (p.nrb * nsp + kTCUs - 1) / kTCUs * bps;
+        if (best < 0 || cost < best) {
+            best = cost;
+            p.blocks_per_split = (int)bps;
+            p.nsplit = (int)nsp;
+        }
+    }
     return p;
 }
 
