@@ -79,9 +79,9 @@ typedef enum {
 #define OT_MAX_DIM 1024
 
 /* Largest d of the transport calls (ot_transport_apply, ot_barycentric_map,
- * ot_cost_gradient_x): all of OT_MAX_DIM. Above 192 one pass over the
- * columns forms each score once and applies it to every value channel
- * (up to 1024 channels). */
+ * ot_cost_gradient_x): all of OT_MAX_DIM. Above d = 192, and from d = 129
+ * with more than 128 value channels, one pass over the columns forms each
+ * score once and applies it to every value channel (up to 1024). */
 #define OT_MAX_TRANSPORT_DIM 1024
 
 /* Human-readable name of a status code (static string, never NULL). */

@@ -105,8 +105,8 @@ hipError_t launch_transport_apply(const Layout &L, const void *xrec, const void 
 // biases of f and g): x's row records and y's column records; rowsum
 // (nullable) also receives r_i = sum_j P_ij, with rowsum = true in the
 // scratch size.
-// Above kp = 192 (dv <= 1024), in transport_rows.hip, with the same records
-// and arguments.
+// Above kp = 192, and at kp = 160 and 192 for wide enough dv (dv <= 1024),
+// in transport_rows.hip, with the same records and arguments.
 size_t transport_rows_scratch_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum);
 hipError_t launch_transport_rows(int kp, const void *xrow, const float *xhat, const void *ycol,
                                  const float *yhat, const float *v, int64_t n, int64_t n_pad,

@@ -326,6 +326,24 @@ MPlan plan_tm(int64_t rows, int64_t cols_pad) {
 // operands do not fit beside the row operands.
 int value_blocks(int dv, int kp) { return dv <= 32 || kp > 128 ? 1 : 2; }
 
+// Whether the one-pass kernel of transport_rows.hip takes the call: always
+// above kp = 192; at kp = 160 and 192 when this kernel's passes (each forming
+// the score again, 3 kp / 16 f16 and 12 bf16 matrix instructions per 32
+// channels per 32x32 subtile) cost more than one pass over dv rounded up to
+// 256 channels, at the measured efficiencies (about 0.5 of the matrix-pipe
+// time here, 0.33 there; d = 192, dv = 192: 31.6 ms here).
+bool one_pass(int dv, int kp) {
+    if (kp > 192)
+        return true;
+    if (kp < 160)
+        return false;
+    const int64_t vc = 32 * value_blocks(dv, kp);
+    const int64_t passes = (dv + vc - 1) / vc;
+    const int64_t here = passes * (3 * kp / 16 + 12 * vc / 32);
+    const int64_t there = 3 * kp / 16 + 12 * ((dv + 255) / 256 * 256) / 32;
+    return 2 * here > 3 * there;
+}
+
 template <int KP, int NVB>
 hipError_t launch_tm(const float4 *xrec, const float *xbias, const float4 *col4, const float *colb,
                      const float4 *vt, int dv_pad, int k0, int64_t n, int64_t n_pad,
@@ -388,7 +406,7 @@ int padded_channels(int dv, int kp) {
 }  // namespace
 
 size_t transport_mfma_scratch_doubles(int64_t n, int64_t m_pad, int dv, bool rowsum, int kp) {
-    if (kp > 192)
+    if (one_pass(dv, kp))
         return transport_rows_scratch_doubles(n, m_pad, dv, rowsum);
     const size_t vt_bytes = (size_t)(m_pad / kTileCols) * 3 * (size_t)padded_channels(dv, kp) *
                             kVRow * sizeof(__bf16);
@@ -399,7 +417,7 @@ hipError_t launch_transport_apply_mfma(int kp, const void *xrow, const float *xh
                                        const void *ycol, const float *yhat, const float *v,
                                        int64_t n, int64_t n_pad, int64_t m, int64_t m_pad, int dv,
                                        double *part, float *out, float *rowsum, hipStream_t s) {
-    if (kp > 192)
+    if (one_pass(dv, kp))
         return launch_transport_rows(kp, xrow, xhat, ycol, yhat, v, n, n_pad, m, m_pad, dv, part,
                                      out, rowsum, s);
     const MPlan p = plan_tm(n, m_pad);

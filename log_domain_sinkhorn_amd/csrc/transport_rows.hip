@@ -491,6 +491,8 @@ hipError_t launch_transport_rows(int kp, const void *xrow, const float *xhat, co
     const float4 *col4 = static_cast<const float4 *>(ycol);
     hipError_t e;
     switch (kp) {
+    case 160: e = launch_tr_nb<160>(nb, p, xr, xhat, col4, yhat, vb, dv_pad, n, n_pad, part, rpart, s); break;
+    case 192: e = launch_tr_nb<192>(nb, p, xr, xhat, col4, yhat, vb, dv_pad, n, n_pad, part, rpart, s); break;
     case 224: e = launch_tr_nb<224>(nb, p, xr, xhat, col4, yhat, vb, dv_pad, n, n_pad, part, rpart, s); break;
     case 256: e = launch_tr_nb<256>(nb, p, xr, xhat, col4, yhat, vb, dv_pad, n, n_pad, part, rpart, s); break;
     case 320: e = launch_tr_nb<320>(nb, p, xr, xhat, col4, yhat, vb, dv_pad, n, n_pad, part, rpart, s); break;

@@ -110,7 +110,8 @@ def test_reduced_workload_apply_map_grad(name, n, m, iters):
     (300, 600, 32), (257, 513, 33), (400, 350, 48), (1, 900, 64), (900, 1, 64),
     (513, 1025, 64), (300, 700, 100), (260, 300, 128),
     # above 128 coordinates: 64-column tiles, hi operands read twice, one
-    # 32-channel value block per pass
+    # 32-channel value block per pass; the map and the x-gradient (dv = d >
+    # 128) take the one-pass kernel
     (300, 400, 160), (257, 300, 192), (1, 500, 192),
 ])
 def test_shapes(n, m, d):
