@@ -158,6 +158,20 @@ def test_wide_values(d, dv):
     assert e <= TOL_APPLY
 
 
+@pytest.mark.parametrize("d,dv", [(160, 128), (160, 129), (192, 128), (192, 129), (192, 256),
+                                  (192, 257), (160, 1024)])
+def test_one_pass_boundary(d, dv):
+    # At 160 and 192 coordinates up to 128 value channels go through the
+    # 32x32 kernel's passes, from 129 on through the one-pass kernel; both
+    # sides of the switch and the channel padding to 256 against the oracle.
+    c = random_clouds(257, 600, d, seed=d * 7 + dv, spread=1.0 / np.sqrt(d))
+    f, g = _oracle_potentials(c, 0.3, 5)
+    v = random_values(600, dv, seed=dv + 2)
+    e = rel_inf(gpu_apply(c, f, g, 0.3, v), oracle.transport_apply(c["x"], c["y"], f, g, 0.3, v))
+    print(f"d={d} dv={dv}: rel err {e:.2e}", flush=True)
+    assert e <= TOL_APPLY
+
+
 def test_single_source_point_closed_form():
     # n = 1 after one f half-step from any g: P_1j = exp((g_j - C_1j)/eps) /
     # sum_k exp((g_k - C_1k)/eps) * a_1, so the map is the softmax-weighted
